@@ -1,0 +1,211 @@
+// C ABI of the DFlash2 draft-block head: host-side validation, then the
+// launchers.  Every error the host can detect is returned before anything is
+// enqueued; nothing here allocates or synchronises (except
+// dflash2_read_device_status).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/dflash2.h"
+#include "launch.hpp"
+
+using namespace dflash2;
+
+namespace {
+
+size_t elem_size(int dtype) { return dtype == DFLASH2_F32 ? 4 : 2; }
+bool dtype_ok(int dtype) { return dtype == DFLASH2_F32 || dtype == DFLASH2_BF16; }
+
+// true when [a, a + na) and [b, b + nb) share a byte
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+dflash2_status launched(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : DFLASH2_ERR_LAUNCH; }
+
+// Hidden sizes the contraction kernels tile without a remainder.
+bool hidden_supported(int32_t hidden) { return hidden % 64 == 0; }
+
+dflash2_status check_conv(int dtype, int64_t n_tokens, int32_t block_size, int32_t hidden,
+                          int32_t taps, int32_t group_size) {
+    if (!dtype_ok(dtype)) return DFLASH2_ERR_DTYPE;
+    if (n_tokens < 1 || block_size < 1 || hidden < 1 || taps < 1 || group_size < 1) return DFLASH2_ERR_SHAPE;
+    if (n_tokens % block_size != 0) return DFLASH2_ERR_SHAPE;  // draft length must be whole blocks
+    if (taps > block_size) return DFLASH2_ERR_SHAPE;
+    if (hidden % group_size != 0) return DFLASH2_ERR_SHAPE;
+    if (taps > DFLASH2_MAX_TAPS || !hidden_supported(hidden)) return DFLASH2_ERR_UNSUPPORTED;
+    if (n_tokens > INT_MAX) return DFLASH2_ERR_UNSUPPORTED;
+    return DFLASH2_OK;
+}
+
+dflash2_status check_selector(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,
+                              int32_t rank, int32_t top_k) {
+    if (!dtype_ok(dtype)) return DFLASH2_ERR_DTYPE;
+    if (n_rows < 1 || hidden < 1 || vocab < 1 || rank < 1) return DFLASH2_ERR_SHAPE;
+    if (top_k < 1 || top_k > vocab) return DFLASH2_ERR_SHAPE;
+    if (top_k > DFLASH2_MAX_TOP_K || rank % 8 != 0 || !hidden_supported(hidden)) return DFLASH2_ERR_UNSUPPORTED;
+    if (n_rows > INT_MAX) return DFLASH2_ERR_UNSUPPORTED;
+    return DFLASH2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dflash2_version(void) { return "dflash2-gfx950 0.1.0"; }
+
+const char *dflash2_status_str(int s) {
+    switch (s) {
+        case DFLASH2_OK: return "ok";
+        case DFLASH2_ERR_NULL: return "a required pointer is null";
+        case DFLASH2_ERR_SHAPE: return "sizes break a rule of the method";
+        case DFLASH2_ERR_DTYPE: return "unknown dtype";
+        case DFLASH2_ERR_UNSUPPORTED: return "sizes beyond what the kernels support";
+        case DFLASH2_ERR_ALIAS: return "an output overlaps an input";
+        case DFLASH2_ERR_WORKSPACE: return "workspace too small";
+        case DFLASH2_ERR_LAUNCH: return "kernel launch failed";
+        case DFLASH2_ERR_DEVICE_ID_RANGE: return "a token id was outside [0, vocab)";
+        default: return "unknown status";
+    }
+}
+
+size_t dflash2_workspace_bytes(int op, int64_t n_rows, int32_t hidden, int32_t vocab, int32_t rank,
+                               int32_t top_k) {
+    if (n_rows < 1 || n_rows > INT_MAX) return 0;
+    switch (op) {
+        case DFLASH2_OP_UNARY_TOPK: {
+            if (hidden < 1 || vocab < 1 || top_k < 1 || top_k > DFLASH2_MAX_TOP_K) return 0;
+            // the plan depends on the element size only through the streaming
+            // fragment buffer; take the larger of the two dtypes' needs
+            const LmheadPlan a = plan_lmhead(DFLASH2_F32, n_rows, hidden, vocab, top_k);
+            const LmheadPlan b = plan_lmhead(DFLASH2_BF16, n_rows, hidden, vocab, top_k);
+            const size_t p = a.partial_bytes > b.partial_bytes ? a.partial_bytes : b.partial_bytes;
+            return kStatusBytes + p;
+        }
+        case DFLASH2_OP_SELECTOR_WALK:
+        case DFLASH2_OP_SELECTOR_TF:
+            if (rank < 1) return 0;
+            return kStatusBytes + (size_t)n_rows * (size_t)rank * 4;
+        default: return 0;
+    }
+}
+
+dflash2_status dflash2_conv_prepare(int dtype, int64_t n_tokens, int32_t block_size, int32_t hidden,
+                                    int32_t taps, int32_t group_size, const void *x,
+                                    const void *w_proj, const void *base, void *x_out,
+                                    float *k_post, void *stream) {
+    dflash2_status s = check_conv(dtype, n_tokens, block_size, hidden, taps, group_size);
+    if (s != DFLASH2_OK) return s;
+    if (!x || !w_proj || !base || !x_out || !k_post) return DFLASH2_ERR_NULL;
+    const size_t es = elem_size(dtype);
+    const size_t act = (size_t)n_tokens * hidden * es;
+    const size_t kp = (size_t)n_tokens * taps * (hidden / group_size) * 4;
+    if (overlaps(x_out, act, x, act) || overlaps(k_post, kp, x, act) || overlaps(k_post, kp, x_out, act))
+        return DFLASH2_ERR_ALIAS;
+    return launched(launch_conv_prepare(dtype, n_tokens, block_size, hidden, taps, group_size, x,
+                                        w_proj, base, x_out, k_post, (hipStream_t)stream));
+}
+
+dflash2_status dflash2_conv_finish(int dtype, int64_t n_tokens, int32_t block_size, int32_t hidden,
+                                   int32_t taps, int32_t group_size, const void *y,
+                                   const float *k_post, const void *base, void *y_out,
+                                   void *stream) {
+    dflash2_status s = check_conv(dtype, n_tokens, block_size, hidden, taps, group_size);
+    if (s != DFLASH2_OK) return s;
+    if (!y || !k_post || !base || !y_out) return DFLASH2_ERR_NULL;
+    const size_t es = elem_size(dtype);
+    const size_t act = (size_t)n_tokens * hidden * es;
+    const size_t kp = (size_t)n_tokens * taps * (hidden / group_size) * 4;
+    if (overlaps(y_out, act, y, act) || overlaps(y_out, act, k_post, kp)) return DFLASH2_ERR_ALIAS;
+    return launched(launch_conv_finish(dtype, n_tokens, block_size, hidden, taps, group_size, y,
+                                       k_post, base, y_out, (hipStream_t)stream));
+}
+
+dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,
+                                  int32_t top_k, const void *h, const void *w_lm,
+                                  const int32_t *gold_ids, int32_t *out_ids, float *out_vals,
+                                  float *out_gold_logit, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    if (!dtype_ok(dtype)) return DFLASH2_ERR_DTYPE;
+    if (n_rows < 1 || hidden < 1 || vocab < 1) return DFLASH2_ERR_SHAPE;
+    if (top_k < 1 || top_k > vocab) return DFLASH2_ERR_SHAPE;
+    if (top_k > DFLASH2_MAX_TOP_K || !hidden_supported(hidden) || n_rows > INT_MAX)
+        return DFLASH2_ERR_UNSUPPORTED;
+    if (!h || !w_lm || !out_ids || !out_vals || !workspace) return DFLASH2_ERR_NULL;
+    if (gold_ids && !out_gold_logit) return DFLASH2_ERR_NULL;
+    if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_UNARY_TOPK, n_rows, hidden, vocab, 0, top_k))
+        return DFLASH2_ERR_WORKSPACE;
+    const size_t nk = (size_t)n_rows * top_k;
+    if (overlaps(out_ids, nk * 4, out_vals, nk * 4) || overlaps(out_ids, nk * 4, workspace, workspace_bytes) ||
+        overlaps(out_vals, nk * 4, workspace, workspace_bytes))
+        return DFLASH2_ERR_ALIAS;
+    return launched(launch_unary_topk(dtype, n_rows, hidden, vocab, top_k, h, w_lm, gold_ids, out_ids,
+                                      out_vals, out_gold_logit, workspace, (hipStream_t)stream));
+}
+
+dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,
+                                     int32_t vocab, int32_t rank, int32_t top_k, const void *h,
+                                     const void *w_h, const void *cb_pred, const void *cb_succ,
+                                     const int32_t *cand_ids, const float *cand_vals,
+                                     const int32_t *anchor_ids, int32_t *out_path,
+                                     float *out_path_score, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (n_blocks < 1 || block_size < 1) return dtype_ok(dtype) ? DFLASH2_ERR_SHAPE : DFLASH2_ERR_DTYPE;
+    const int64_t N = (int64_t)n_blocks * block_size;
+    dflash2_status s = check_selector(dtype, N, hidden, vocab, rank, top_k);
+    if (s != DFLASH2_OK) return s;
+    if (block_size > DFLASH2_MAX_BLOCK_SIZE) return DFLASH2_ERR_UNSUPPORTED;
+    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path || !workspace)
+        return DFLASH2_ERR_NULL;
+    if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))
+        return DFLASH2_ERR_WORKSPACE;
+    const size_t np = (size_t)N * 4;
+    if (overlaps(out_path, np, workspace, workspace_bytes) ||
+        (out_path_score && (overlaps(out_path_score, np, workspace, workspace_bytes) ||
+                            overlaps(out_path_score, np, out_path, np))))
+        return DFLASH2_ERR_ALIAS;
+    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
+                                         cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
+                                         out_path_score, workspace, (hipStream_t)stream));
+}
+
+dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,
+                                         int32_t rank, int32_t top_k, const void *h, const void *w_h,
+                                         const void *cb_pred, const void *cb_succ,
+                                         const int32_t *cand_ids, const float *cand_vals,
+                                         const int32_t *pred_ids, const int32_t *gold_ids,
+                                         const uint8_t *force, const float *gold_logit,
+                                         float *out_scores, int32_t *out_best_ids, float *out_ce,
+                                         uint8_t *out_valid, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    dflash2_status s = check_selector(dtype, n_rows, hidden, vocab, rank, top_k);
+    if (s != DFLASH2_OK) return s;
+    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !pred_ids || !out_scores ||
+        !out_best_ids || !workspace)
+        return DFLASH2_ERR_NULL;
+    if (force && !gold_ids) return DFLASH2_ERR_NULL;
+    if (force && !gold_logit) return DFLASH2_ERR_NULL;
+    if (gold_ids && (!out_ce || !out_valid)) return DFLASH2_ERR_NULL;
+    if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_TF, n_rows, hidden, vocab, rank, top_k))
+        return DFLASH2_ERR_WORKSPACE;
+    const size_t nk = (size_t)n_rows * top_k * 4;
+    if (overlaps(out_scores, nk, workspace, workspace_bytes) || overlaps(out_best_ids, (size_t)n_rows * 4, workspace, workspace_bytes) ||
+        overlaps(out_scores, nk, out_best_ids, (size_t)n_rows * 4))
+        return DFLASH2_ERR_ALIAS;
+    return launched(launch_selector_tf(dtype, n_rows, hidden, vocab, rank, top_k, h, w_h, cb_pred,
+                                       cb_succ, cand_ids, cand_vals, pred_ids, gold_ids, force,
+                                       gold_logit, out_scores, out_best_ids, out_ce, out_valid,
+                                       workspace, (hipStream_t)stream));
+}
+
+dflash2_status dflash2_read_device_status(const void *workspace, void *stream) {
+    if (!workspace) return DFLASH2_ERR_NULL;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DFLASH2_ERR_LAUNCH;
+    uint32_t word = 0;
+    if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return DFLASH2_ERR_LAUNCH;
+    return (word & kStatusIdRange) ? DFLASH2_ERR_DEVICE_ID_RANGE : DFLASH2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Host-side launchers behind the C ABI (one per operation).  Arguments are
+// already validated by api.cpp; each launcher only enqueues kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dflash2.h"
+
+namespace dflash2 {
+
+// Workspaces start with a 256-byte header holding the device status word.
+constexpr size_t kStatusBytes = 256;
+// Bit of the status word set when a token id is outside [0, vocab).
+constexpr uint32_t kStatusIdRange = 1u;
+
+struct LmheadPlan {
+    bool streaming;
+    int nw, tiles_per_wave, n_tiles;
+    int grid_x, grid_y, n_lists;
+    size_t lds, partial_bytes;
+};
+LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
+
+hipError_t launch_conv_prepare(int dtype, int64_t N, int bs, int H, int taps, int gs, const void *x,
+                               const void *w_proj, const void *base, void *x_out, float *k_post,
+                               hipStream_t stream);
+hipError_t launch_conv_finish(int dtype, int64_t N, int bs, int H, int taps, int gs, const void *y,
+                              const float *k_post, const void *base, void *y_out, hipStream_t stream);
+hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const void *h, const void *w,
+                             const int32_t *gold, int32_t *out_ids, float *out_vals,
+                             float *gold_logit, void *workspace, hipStream_t stream);
+hipError_t launch_context_proj(int dtype, int64_t N, int H, int r, const void *h, const void *w_h,
+                               float *g, uint32_t *status, hipStream_t stream);
+hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, int r, int K,
+                                const void *h, const void *w_h, const void *A, const void *B,
+                                const int32_t *cand_ids, const float *cand_vals,
+                                const int32_t *anchors, int32_t *path, float *path_score,
+                                void *workspace, hipStream_t stream);
+hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
+                              const void *w_h, const void *A, const void *B, const int32_t *cand_ids,
+                              const float *cand_vals, const int32_t *pred_ids,
+                              const int32_t *gold_ids, const uint8_t *force,
+                              const float *gold_logit, float *out_scores, int32_t *out_best,
+                              float *out_ce, uint8_t *out_valid, void *workspace,
+                              hipStream_t stream);
+
+}  // namespace dflash2

@@ -1,0 +1,247 @@
+// Candidate selector: S_t(a, b) = U_t(b) + <A(a) * H(h_t), B(b)>.
+//
+// Both modes score with one routine, pair_tile: a 16 x 16 tile of transition
+// terms sum_r B[cand, r] * (A[pred, r] * g[n, r]) on the float32 MFMA units,
+// candidates on the rows and predecessors on the columns, the rank index
+// visited in the same order.  The greedy walk scores every adjacent pair of a
+// block at once and reduces each predecessor's row to its best successor;
+// only the final pointer chase is sequential.  Teacher forcing places its one
+// predecessor in column 0 of the same routine, so replaying a walk's own
+// predecessors reproduces the walk's scores bit for bit.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dflash2 {
+
+// P[m][c] = sum_r B[cid_m, r] * (A[pid_c, r] * grow[r]) where lane l holds
+// candidate cid (row l % 16) and predecessor pid (column l % 16); a negative
+// id is a zero row/column.  r is a multiple of 8.  acc[i] of lane l is
+// P[4 * (l / 16) + i][l % 16].
+template <typename T>
+__device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__restrict__ B,
+                                           const float *__restrict__ grow, int pid, int cid, int r) {
+    const int q = lane_id() >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rho0 = 0; rho0 < r; rho0 += 32) {
+        const int rho = rho0 + q * 8;
+        float a[8], b[8], gg[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = b[e] = gg[e] = 0.f;
+        if (rho < r) {
+            if (pid >= 0) load8<T>(A + (size_t)pid * r + rho, a);
+            if (cid >= 0) load8<T>(B + (size_t)cid * r + rho, b);
+            load8<float>(grow + rho, gg);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mma16_f32x1(acc, b[e], a[e] * gg[e]);
+    }
+    return acc;
+}
+
+// ------------------------------------------------------------------ walk
+// One workgroup per anchor block.  Work item (t, it): position t and the
+// predecessor tile it (16 slots of C_{t-1}; at t = 1 the single anchor).
+// For each predecessor the item keeps the best successor as a key
+// (score, lowest slot on ties) in LDS; thread 0 then chases the pointers.
+template <typename T>
+__global__ __launch_bounds__(1024) void selector_walk_kernel(
+    const float *__restrict__ g, const T *__restrict__ A, const T *__restrict__ B,
+    const int32_t *__restrict__ cand_ids, const float *__restrict__ cand_vals,
+    const int32_t *__restrict__ anchors, int bs, int V, int r, int K, int32_t *__restrict__ path,
+    float *__restrict__ path_score, uint32_t *__restrict__ status) {
+    __shared__ uint64_t best[DFLASH2_MAX_BLOCK_SIZE * DFLASH2_MAX_TOP_K];
+    const int blk = blockIdx.x;
+    const int lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int q = lane >> 4, c = lane & 15;
+    const int n_it = (K + 15) / 16, n_jt = n_it;
+    const int n_items = bs >= 2 ? 1 + (bs - 2) * n_it : 0;
+    const int anchor = anchors[blk];
+    const bool anchor_ok = anchor >= 0 && anchor < V;
+    if (!anchor_ok && threadIdx.x == 0) flag_status(status, kStatusIdRange);
+
+    for (int item = wave; item < n_items; item += nwaves) {
+        const int t = item == 0 ? 1 : 2 + (item - 1) / n_it;
+        const int it = item == 0 ? 0 : (item - 1) % n_it;
+        const size_t n = (size_t)blk * bs + t;
+        int pid = -1;
+        bool col_used;
+        if (t == 1) {
+            col_used = c == 0;
+            pid = (col_used && anchor_ok) ? anchor : -1;
+        } else {
+            const int i = it * 16 + c;
+            col_used = i < K;
+            if (col_used) {
+                pid = cand_ids[(n - 1) * K + i];
+                if (pid < 0 || pid >= V) pid = -1;  // flagged when its own row is scored
+            }
+        }
+        uint64_t bestkey = 0;
+        for (int jt = 0; jt < n_jt; ++jt) {
+            const int j = jt * 16 + c;
+            int cid = j < K ? cand_ids[n * K + j] : -1;
+            bool cok = j < K && cid >= 0 && cid < V;
+            if (j < K && !cok) flag_status(status, kStatusIdRange);
+            if (!cok) cid = -1;
+            const f32x4 P = pair_tile<T>(A, B, g + n * r, pid, cid, r);
+            uint64_t local = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int jj = jt * 16 + 4 * q + i;
+                const bool ok = __shfl((int)cok, 4 * q + i) != 0;
+                const float s = jj < K ? cand_vals[n * K + jj] + P[i] : 0.f;
+                const uint64_t key = (ok && pid >= 0) ? make_key(s, (uint32_t)jj) : 0ull;
+                local = key > local ? key : local;
+            }
+            uint64_t o = shfl_xor_u64(local, 16);
+            local = o > local ? o : local;
+            o = shfl_xor_u64(local, 32);
+            local = o > local ? o : local;
+            bestkey = local > bestkey ? local : bestkey;
+        }
+        if (q == 0 && col_used) best[t * DFLASH2_MAX_TOP_K + (t == 1 ? 0 : it * 16 + c)] = bestkey;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const size_t p0 = (size_t)blk * bs;
+        path[p0] = anchor_ok ? anchor : -1;
+        if (path_score) path_score[p0] = 0.f;
+        bool alive = anchor_ok;
+        int slot = 0;
+        for (int t = 1; t < bs; ++t) {
+            const uint64_t key = alive ? best[t * DFLASH2_MAX_TOP_K + slot] : 0ull;
+            if (key == 0) {
+                alive = false;
+                path[p0 + t] = -1;
+                if (path_score) path_score[p0 + t] = __builtin_nanf("");
+                continue;
+            }
+            slot = (int)key_id(key);
+            path[p0 + t] = cand_ids[(p0 + t) * K + slot];
+            if (path_score) path_score[p0 + t] = key_val(key);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ teacher forcing
+// One wave per row: the given predecessor sits in column 0 of pair_tile.
+template <typename T>
+__global__ __launch_bounds__(256) void selector_tf_kernel(
+    const float *__restrict__ g, const T *__restrict__ A, const T *__restrict__ B,
+    const int32_t *__restrict__ cand_ids, const float *__restrict__ cand_vals,
+    const int32_t *__restrict__ pred_ids, const int32_t *__restrict__ gold_ids,
+    const uint8_t *__restrict__ force, const float *__restrict__ gold_logit, long long N, int V, int r,
+    int K, float *__restrict__ out_scores, int32_t *__restrict__ out_best, float *__restrict__ out_ce,
+    uint8_t *__restrict__ out_valid, uint32_t *__restrict__ status) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const long long n = (long long)blockIdx.x * 4 + wave;
+    if (n >= N) return;
+    const int c = lane & 15;
+    const int p = pred_ids[n];
+    const bool p_ok = p >= 0 && p < V;
+    const int pid = (c == 0 && p_ok) ? p : -1;
+    const int n_jt = (K + 15) / 16;
+    const float *grow = g + (size_t)n * r;
+    // lane k (< K) ends up with the score of slot k
+    float s = -__builtin_inff();
+    bool mine_ok = false;
+    const int qk = c >> 2, ik = lane & 3;
+    for (int jt = 0; jt < n_jt; ++jt) {
+        const int j = jt * 16 + c;
+        int cid = j < K ? cand_ids[(size_t)n * K + j] : -1;
+        const bool cok = j < K && cid >= 0 && cid < V;
+        if (!cok) cid = -1;
+        const f32x4 P = pair_tile<T>(A, B, grow, pid, cid, r);
+        const float v0 = __shfl(P[0], 16 * qk), v1 = __shfl(P[1], 16 * qk);
+        const float v2 = __shfl(P[2], 16 * qk), v3 = __shfl(P[3], 16 * qk);
+        const float pk = ik == 0 ? v0 : ik == 1 ? v1 : ik == 2 ? v2 : v3;
+        if ((lane >> 4) == jt && lane < K) {
+            mine_ok = cok && p_ok;
+            s = mine_ok ? cand_vals[(size_t)n * K + lane] + pk : __builtin_nanf("");
+        }
+    }
+    if (lane < K) out_scores[(size_t)n * K + lane] = s;
+    const uint64_t bestkey = wave_max_u64((lane < K && mine_ok) ? make_key(s, (uint32_t)lane) : 0ull);
+    const bool all_ok = __all(lane >= K || mine_ok) != 0;
+    if (!all_ok && lane == 0) flag_status(status, kStatusIdRange);
+    if (lane == 0) out_best[n] = bestkey ? cand_ids[(size_t)n * K + key_id(bestkey)] : -1;
+    if (!gold_ids) return;
+    const int gid = gold_ids[n];
+    const bool g_ok = gid >= 0 && gid < V;
+    if (!g_ok && lane == 0) flag_status(status, kStatusIdRange);
+    const int my_id = lane < K ? cand_ids[(size_t)n * K + lane] : -1;
+    const unsigned long long hit = __ballot(lane < K && g_ok && my_id == gid);
+    int kg = hit ? __ffsll(hit) - 1 : -1;
+    if (kg < 0 && g_ok && force && force[n]) {
+        const f32x4 P = pair_tile<T>(A, B, grow, pid, c == 0 ? gid : -1, r);
+        const float sg = gold_logit[n] + __shfl(P[0], 0);
+        kg = K - 1;
+        if (lane == kg) s = sg;
+    }
+    const bool valid = kg >= 0 && all_ok;
+    float ce = 0.f;
+    if (valid) {
+        const float m = wave_max_f32(lane < K ? s : -__builtin_inff());
+        const float e = lane < K ? expf(s - m) : 0.f;
+        const float sum = wave_sum_f32(e);
+        ce = m + logf(sum) - __shfl(s, kg);
+    }
+    if (lane == 0) {
+        if (out_ce) out_ce[n] = ce;
+        if (out_valid) out_valid[n] = valid ? 1 : 0;
+    }
+}
+
+// ------------------------------------------------------------------ host side
+
+hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, int r, int K,
+                                const void *h, const void *w_h, const void *A, const void *B,
+                                const int32_t *cand_ids, const float *cand_vals,
+                                const int32_t *anchors, int32_t *path, float *path_score,
+                                void *workspace, hipStream_t stream) {
+    uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
+    float *g = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
+    const int64_t N = (int64_t)n_blocks * bs;
+    hipError_t e = launch_context_proj(dtype, N, H, r, h, w_h, g, status, stream);
+    if (e != hipSuccess) return e;
+    const int n_it = (K + 15) / 16;
+    const int items = bs >= 2 ? 1 + (bs - 2) * n_it : 1;
+    int waves = items < 16 ? items : 16;
+    const dim3 block(64 * waves);
+    if (dtype == 0)
+        hipLaunchKernelGGL(selector_walk_kernel<float>, dim3(n_blocks), block, 0, stream, g,
+                           (const float *)A, (const float *)B, cand_ids, cand_vals, anchors, bs, V, r,
+                           K, path, path_score, status);
+    else
+        hipLaunchKernelGGL(selector_walk_kernel<uint16_t>, dim3(n_blocks), block, 0, stream, g,
+                           (const uint16_t *)A, (const uint16_t *)B, cand_ids, cand_vals, anchors,
+                           bs, V, r, K, path, path_score, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
+                              const void *w_h, const void *A, const void *B, const int32_t *cand_ids,
+                              const float *cand_vals, const int32_t *pred_ids,
+                              const int32_t *gold_ids, const uint8_t *force,
+                              const float *gold_logit, float *out_scores, int32_t *out_best,
+                              float *out_ce, uint8_t *out_valid, void *workspace,
+                              hipStream_t stream) {
+    uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
+    float *g = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
+    hipError_t e = launch_context_proj(dtype, N, H, r, h, w_h, g, status, stream);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)((N + 3) / 4);
+    if (dtype == 0)
+        hipLaunchKernelGGL(selector_tf_kernel<float>, dim3(grid), dim3(256), 0, stream, g,
+                           (const float *)A, (const float *)B, cand_ids, cand_vals, pred_ids, gold_ids,
+                           force, gold_logit, (long long)N, V, r, K, out_scores, out_best, out_ce,
+                           out_valid, status);
+    else
+        hipLaunchKernelGGL(selector_tf_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, g,
+                           (const uint16_t *)A, (const uint16_t *)B, cand_ids, cand_vals, pred_ids,
+                           gold_ids, force, gold_logit, (long long)N, V, r, K, out_scores, out_best,
+                           out_ce, out_valid, status);
+    return hipGetLastError();
+}
+
+}  // namespace dflash2

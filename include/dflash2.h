@@ -1,0 +1,223 @@
+/*
+ * dflash2.h - C ABI of the DFlash2 draft-block head on AMD Instinct MI355X (gfx950).
+ *
+ * Three operations of the DFlash2 drafter:
+ *   1. the block-local grouped dynamic causal convolution that wraps every
+ *      draft sublayer (dflash2_conv_prepare / dflash2_conv_finish);
+ *   2. full-vocabulary unary LM-head logits with a per-position top-K
+ *      (dflash2_unary_topk);
+ *   3. the candidate selector S_t(a,b) = U_t(b) + <A(a) * H(h_t), B(b)>,
+ *      walked greedily from the anchor (dflash2_selector_walk) or scored in one
+ *      shot with teacher-forced predecessors (dflash2_selector_score_tf).
+ *
+ * Sources, cited by page title and section:
+ *   [Speculators] "DFlash2" page of the vLLM Speculators user guide.
+ *   [SpecForge]   "DFlash2" concept page of the SpecForge docs.
+ *   [verl PR]     "feat: add DFlash2 drafter training backend" (verl-SpeCo #62).
+ *   [Explainer]   "DFlash 2 Explanation".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer is a DEVICE pointer owned by the caller, except where noted.
+ *   The library never allocates, never frees and keeps no state between calls.
+ *   Calls are re-entrant; concurrent calls must use distinct workspaces.
+ * - All work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *   stream).  No entry point synchronises, except dflash2_read_device_status.
+ * - Matrices are row-major.  Weights follow the [out, in] layout of a linear
+ *   layer: w_lm [V, H], w_proj [2*T*G, H], w_h [r, H]; the selector codebooks
+ *   are materialised tables cb_pred = A [V, r] and cb_succ = B [V, r].
+ * - `dtype` (dflash2_dtype) is the storage type of every activation and weight
+ *   argument marked "dtype" below: IEEE float32, or bf16 (the high 16 bits of
+ *   a float32).  All arithmetic accumulates in float32.
+ * - Errors the host can see are returned BEFORE anything is enqueued:
+ *   DFLASH2_ERR_NULL for a missing required pointer, DFLASH2_ERR_SHAPE for a
+ *   size that breaks a rule of the method, DFLASH2_ERR_UNSUPPORTED for a size
+ *   the kernels do not handle, DFLASH2_ERR_DTYPE for an unknown dtype,
+ *   DFLASH2_ERR_ALIAS for an output that overlaps an input it must not,
+ *   DFLASH2_ERR_WORKSPACE for a workspace smaller than
+ *   dflash2_workspace_bytes().  A failed launch returns DFLASH2_ERR_LAUNCH.
+ * - Token ids found out of range [0, V) on the device (anchors, predecessors,
+ *   gold ids, candidate ids) are never dereferenced: the affected outputs get
+ *   a sentinel (id -1, NaN score, valid 0) and a status word in the workspace
+ *   is set; dflash2_read_device_status() reports it as
+ *   DFLASH2_ERR_DEVICE_ID_RANGE.  The word is cleared at the start of every
+ *   call that takes a workspace.
+ */
+#ifndef DFLASH2_H_
+#define DFLASH2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DFLASH2_OK = 0,
+    DFLASH2_ERR_NULL = 1,
+    DFLASH2_ERR_SHAPE = 2,
+    DFLASH2_ERR_DTYPE = 3,
+    DFLASH2_ERR_UNSUPPORTED = 4,
+    DFLASH2_ERR_ALIAS = 5,
+    DFLASH2_ERR_WORKSPACE = 6,
+    DFLASH2_ERR_LAUNCH = 7,
+    DFLASH2_ERR_DEVICE_ID_RANGE = 8
+} dflash2_status;
+
+typedef enum { DFLASH2_F32 = 0, DFLASH2_BF16 = 1 } dflash2_dtype;
+
+typedef enum {
+    DFLASH2_OP_UNARY_TOPK = 0,
+    DFLASH2_OP_SELECTOR_WALK = 1,
+    DFLASH2_OP_SELECTOR_TF = 2
+} dflash2_op;
+
+/* Kernel limits (sizes beyond them return DFLASH2_ERR_UNSUPPORTED). */
+#define DFLASH2_MAX_TOP_K 64
+#define DFLASH2_MAX_TAPS 16
+#define DFLASH2_MAX_BLOCK_SIZE 64
+
+/*
+ * Pre-sublayer half of the conv wrapper ([verl PR] "What DFlash2 adds";
+ * [Speculators] "Local Convolution"; [Explainer] "Problem 2").
+ *
+ * One bias-free projection of the current hidden state gives the dynamic
+ * corrections of both the input and the output kernel:
+ *   c[n, s, j, g] = sum_h w_proj[(s*T + j)*G + g, h] * x[n, h],
+ * s = 0 input kernel, s = 1 output kernel, j < T tap, g < G = H / group_size.
+ * The input is convolved at once, block-locally:
+ *   x_out[n, h] = sum_{j <= min(T-1, n mod bs)} (base[0, j, h] + c[n, 0, j, h / gs]) * x[n - j, h]
+ * (a tap that would reach before the start of its anchor block reads zero;
+ * [verl PR] "Two deltas", item 1), and the output kernel's dynamic part is
+ * handed to dflash2_conv_finish:  k_post[n, j, g] = c[n, 1, j, g].
+ *
+ *   dtype       storage type of x, w_proj, base, x_out
+ *   n_tokens    N, flattened draft length; must be a multiple of block_size
+ *   block_size  bs, anchor-block length
+ *   hidden      H;  taps T in [1, min(block_size, 16)];  group_size divides H
+ *   x           [N, H]       sublayer input
+ *   w_proj      [2*T*G, H]   kernel projection
+ *   base        [2, T, H]    static per-channel kernels (input, output)
+ *   x_out       [N, H]       convolved input (one rounding to dtype); must not overlap x
+ *   k_post      [N, T, G]    float32, dynamic part of the output kernel
+ * Rules (DFLASH2_ERR_SHAPE): N % bs != 0, T < 1 or T > bs, H % gs != 0, sizes < 1.
+ */
+dflash2_status dflash2_conv_prepare(int dtype, int64_t n_tokens, int32_t block_size,
+                                    int32_t hidden, int32_t taps, int32_t group_size,
+                                    const void *x, const void *w_proj, const void *base,
+                                    void *x_out, float *k_post, void *stream);
+
+/*
+ * Post-sublayer half of the conv wrapper ([verl PR] "What DFlash2 adds"):
+ *   y_out[n, h] = sum_{j <= min(T-1, n mod bs)} (base[1, j, h] + k_post[n, j, h / gs]) * y[n - j, h]
+ * y [N, H] is the sublayer's output, k_post comes from dflash2_conv_prepare,
+ * y_out [N, H] must not overlap y.  Same rules as dflash2_conv_prepare.
+ */
+dflash2_status dflash2_conv_finish(int dtype, int64_t n_tokens, int32_t block_size,
+                                   int32_t hidden, int32_t taps, int32_t group_size,
+                                   const void *y, const float *k_post, const void *base,
+                                   void *y_out, void *stream);
+
+/*
+ * Unary LM-head logits over the full vocabulary and the per-row top-K
+ * candidate lattice ([Speculators] "Candidate Selector" and its full-vocabulary
+ * requirement; [Explainer] "Component Breakdown", shared lm_head and top-16
+ * per position).
+ *   U[n, v] = sum_h h[n, h] * w_lm[v, h]   (float32 accumulation; never written out)
+ *   out_ids[n, :]  the top_k ids of row n by U, value descending, lower id
+ *                  first on an exact tie;   out_vals[n, :] their U values.
+ *   If gold_ids is given: out_gold_logit[n] = U[n, gold_ids[n]] (required then).
+ *
+ *   n_rows N >= 1, hidden H, vocab V, top_k K in [1, min(V, 64)]
+ *   h [N, H] dtype; w_lm [V, H] dtype; gold_ids [N] int32 or NULL
+ *   out_ids [N, K] int32; out_vals [N, K] float32; out_gold_logit [N] float32
+ *   workspace: device bytes, at least dflash2_workspace_bytes(DFLASH2_OP_UNARY_TOPK, ...)
+ */
+dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,
+                                  int32_t top_k, const void *h, const void *w_lm,
+                                  const int32_t *gold_ids, int32_t *out_ids, float *out_vals,
+                                  float *out_gold_logit, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy selector walk per anchor block ([verl PR] "What DFlash2 adds",
+ * selector equation; [Speculators] "Candidate Selector"; [Explainer]
+ * "Problem 1" and the "One Cycle, Step by Step" diagram: candidate lists plus
+ * the last verified token in, one path out).
+ *   g[n] = w_h h[n]  (the context projection H(h_n), float32)
+ *   S_t(a, b) = cand_vals[n, slot(b)] + sum_r cb_pred[a, r] * g[n, r] * cb_succ[b, r]
+ * with n = blk*bs + t.  path[blk, 0] = anchor_ids[blk]; for t = 1..bs-1 the
+ * candidate of row n with the highest S_t(path[blk, t-1], .) is taken (lowest
+ * slot on an exact tie).  Every adjacent pair is scored in parallel; only the
+ * final pointer chase is sequential.
+ *
+ *   n_blocks, block_size (<= 64), hidden H, vocab V, rank r, top_k K (<= 64)
+ *   h [N, H] dtype (N = n_blocks*bs); w_h [r, H] dtype
+ *   cb_pred, cb_succ [V, r] dtype; cand_ids [N, K] int32; cand_vals [N, K] float32
+ *   anchor_ids [n_blocks] int32
+ *   out_path [n_blocks, bs] int32; out_path_score [n_blocks, bs] float32 or NULL
+ *   (0 at position 0, S_t of the chosen step elsewhere).
+ */
+dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_size,
+                                     int32_t hidden, int32_t vocab, int32_t rank, int32_t top_k,
+                                     const void *h, const void *w_h, const void *cb_pred,
+                                     const void *cb_succ, const int32_t *cand_ids,
+                                     const float *cand_vals, const int32_t *anchor_ids,
+                                     int32_t *out_path, float *out_path_score, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
+ * Teacher-forced selector scoring of every row at once ([verl PR] "Selector
+ * training objective"; [Speculators] "Training Objective"; [SpecForge]
+ * "Selector objective and schedule").
+ *   out_scores[n, k] = S(pred_ids[n], cand_ids[n, k]) over the strict set;
+ *   out_best_ids[n]  = the candidate with the highest score (lowest slot on ties).
+ * With gold_ids: the forced set C' replaces slot K-1 by (gold, gold_logit[n])
+ * when force[n] != 0 and the gold id is not among the candidates; a row is
+ * valid when its gold id is in C'; out_ce[n] = logsumexp_k S'[n, k] -
+ * S'[n, gold] for valid rows, 0 otherwise; out_valid[n] in {0, 1}.
+ *
+ *   h [N, H], w_h [r, H], cb_pred/cb_succ [V, r]: dtype
+ *   cand_ids [N, K] int32, cand_vals [N, K] float32, pred_ids [N] int32
+ *   gold_ids [N] int32 or NULL; force [N] uint8 or NULL (needs gold_ids);
+ *   gold_logit [N] float32, required when force is given
+ *   out_scores [N, K] float32; out_best_ids [N] int32;
+ *   out_ce [N] float32 and out_valid [N] uint8: required when gold_ids is given
+ */
+dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidden,
+                                         int32_t vocab, int32_t rank, int32_t top_k,
+                                         const void *h, const void *w_h, const void *cb_pred,
+                                         const void *cb_succ, const int32_t *cand_ids,
+                                         const float *cand_vals, const int32_t *pred_ids,
+                                         const int32_t *gold_ids, const uint8_t *force,
+                                         const float *gold_logit, float *out_scores,
+                                         int32_t *out_best_ids, float *out_ce,
+                                         uint8_t *out_valid, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes an operation needs (host only, no device call).  `op` is a
+ * dflash2_op; n_rows is N (for the walk: n_blocks * block_size).  Arguments an
+ * op does not use are ignored.  Returns 0 for an unknown op or invalid sizes.
+ */
+size_t dflash2_workspace_bytes(int op, int64_t n_rows, int32_t hidden, int32_t vocab,
+                               int32_t rank, int32_t top_k);
+
+/* Human-readable name of a status code (static string, host only). */
+const char *dflash2_status_str(int status);
+
+/*
+ * Synchronises `stream`, then reads the status word of the last call that
+ * used `workspace`: DFLASH2_OK or DFLASH2_ERR_DEVICE_ID_RANGE
+ * (DFLASH2_ERR_LAUNCH if the read itself fails).
+ */
+dflash2_status dflash2_read_device_status(const void *workspace, void *stream);
+
+/* Library version, e.g. "dflash2-gfx950 0.1.0" (static string). */
+const char *dflash2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH2_H_ */

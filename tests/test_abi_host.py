@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/dflash2.h declares, and host validation returns the documented
+status before anything reaches the device (all pointers here are fake and are
+never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash2.h")
+
+D = pytest.importorskip("block_draft_head_amd.dflash2", reason="libdflash2.so not built")
+L = D._lib
+
+import torch  # noqa: E402
+
+# The validation tests pass fake device pointers and rely on every call being
+# rejected on the host.  Never run them where a GPU is visible.
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake-pointer host checks run only without a GPU")
+P = ctypes.c_void_p
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, WS = 0, 1, 2, 3, 4, 5, 6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash2_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_entry_point_is_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    assert sorted(D.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name, val in [("DFLASH2_MAX_TOP_K", D.MAX_TOP_K), ("DFLASH2_MAX_TAPS", D.MAX_TAPS),
+                      ("DFLASH2_MAX_BLOCK_SIZE", D.MAX_BLOCK_SIZE)]:
+        assert re.search(rf"#define {name} {val}\b", text)
+    for code, name in D.STATUS.items():
+        assert re.search(rf"{name} = {code}\b", text)
+
+
+def test_status_strings_and_version():
+    assert D.version().startswith("dflash2-gfx950")
+    for code in range(9):
+        assert D.status_str(code) and D.status_str(code) != "unknown status"
+    assert D.status_str(99) == "unknown status"
+
+
+def fake(i):
+    return P(0x100000 * (i + 1))
+
+
+def prep(dtype=1, n=16, bs=8, h=256, t=2, gs=16, x=fake(0), w=fake(1), b=fake(2), xo=fake(3), kp=fake(4)):
+    return L.dflash2_conv_prepare(dtype, n, bs, h, t, gs, x, w, b, xo, kp, None)
+
+
+def fin(dtype=1, n=16, bs=8, h=256, t=2, gs=16, y=fake(0), kp=fake(1), b=fake(2), yo=fake(3)):
+    return L.dflash2_conv_finish(dtype, n, bs, h, t, gs, y, kp, b, yo, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("call", [prep, fin])
+def test_conv_rules(call):
+    assert call(n=12) == SHAPE           # draft length not a whole number of blocks
+    assert call(t=0) == SHAPE and call(t=9) == SHAPE   # taps outside [1, block_size]
+    assert call(gs=24) == SHAPE          # group size must divide hidden
+    assert call(n=0) == SHAPE and call(bs=0) == SHAPE and call(h=0) == SHAPE
+    assert call(dtype=2) == DTYPE
+    assert call(h=96, gs=16) == UNSUP    # hidden not a multiple of 64
+    assert call(n=34, bs=17, t=17) == UNSUP  # taps above the kernel limit
+
+
+@no_gpu
+def test_conv_pointer_and_alias_rules():
+    assert prep(x=None) == NULL and prep(kp=None) == NULL and prep(w=None) == NULL
+    assert fin(yo=None) == NULL and fin(kp=None) == NULL
+    assert prep(xo=fake(0)) == ALIAS     # output on the input
+    assert prep(xo=P(0x100000 + 64)) == ALIAS  # partial overlap
+    assert fin(yo=fake(0)) == ALIAS
+
+
+def topk(dtype=1, n=8, h=256, v=4096, k=16, hp=fake(0), w=fake(1), gold=None, ids=fake(2), vals=fake(3),
+         gl=None, ws=fake(4), wsb=None):
+    if wsb is None:
+        wsb = D.workspace_bytes(D.OP_UNARY_TOPK, n, h, v, 0, k) if n > 0 else 1 << 20
+    return L.dflash2_unary_topk(dtype, n, h, v, k, hp, w, gold, ids, vals, gl, ws, wsb, None)
+
+
+@no_gpu
+def test_unary_topk_rules():
+    assert topk(k=0) == SHAPE and topk(k=4097) == SHAPE and topk(v=0) == SHAPE and topk(n=0) == SHAPE
+    assert topk(k=65) == UNSUP and topk(h=100) == UNSUP
+    assert topk(dtype=-1) == DTYPE
+    assert topk(hp=None) == NULL and topk(ws=None) == NULL and topk(ids=None) == NULL
+    assert topk(gold=fake(5), gl=None) == NULL
+    assert topk(wsb=16) == WS
+    assert topk(ids=fake(3)) == ALIAS    # ids on vals
+
+
+def walk(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, ws=fake(9), wsb=None, path=fake(7), anchors=fake(6), ps=None):
+    if wsb is None:
+        wsb = D.workspace_bytes(D.OP_SELECTOR_WALK, nb * bs, h, v, r, k) if nb * bs > 0 else 1 << 20
+    return L.dflash2_selector_walk(dtype, nb, bs, h, v, r, k, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+                                   anchors, path, ps, ws, wsb, None)
+
+
+@no_gpu
+def test_selector_walk_rules():
+    assert walk(k=0) == SHAPE and walk(k=1001) == SHAPE and walk(r=0) == SHAPE and walk(nb=0) == SHAPE
+    assert walk(k=65) == UNSUP and walk(bs=65) == UNSUP and walk(r=12) == UNSUP and walk(h=96) == UNSUP
+    assert walk(dtype=5) == DTYPE
+    assert walk(path=None) == NULL and walk(anchors=None) == NULL and walk(ws=None) == NULL
+    assert walk(wsb=100) == WS
+    assert walk(ps=fake(7)) == ALIAS
+
+
+def tf(dtype=1, n=16, h=256, v=1000, r=32, k=16, gold=None, force=None, gl=None, ce=None, valid=None, ws=fake(12),
+       wsb=None, scores=fake(13), best=fake(14)):
+    if wsb is None:
+        wsb = D.workspace_bytes(D.OP_SELECTOR_TF, n, h, v, r, k) if n > 0 else 1 << 20
+    return L.dflash2_selector_score_tf(dtype, n, h, v, r, k, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+                                       fake(6), gold, force, gl, scores, best, ce, valid, ws, wsb, None)
+
+
+@no_gpu
+def test_selector_tf_rules():
+    assert tf(k=0) == SHAPE and tf(n=0) == SHAPE and tf(k=2000) == SHAPE
+    assert tf(k=100) == UNSUP and tf(r=20) == UNSUP
+    assert tf(force=fake(8)) == NULL                       # force needs gold ids
+    assert tf(gold=fake(7), force=fake(8), ce=fake(10), valid=fake(11)) == NULL  # and the gold logits
+    assert tf(gold=fake(7)) == NULL                        # gold ids need ce and valid outputs
+    assert tf(scores=None) == NULL and tf(ws=None) == NULL
+    assert tf(wsb=8) == WS
+    assert tf(scores=fake(14)) == ALIAS
+
+
+def test_workspace_sizes():
+    # walk / TF: status header plus the float32 context projection
+    assert D.workspace_bytes(D.OP_SELECTOR_WALK, 8, 4096, 151936, 256, 16) == 256 + 8 * 256 * 4
+    assert D.workspace_bytes(D.OP_SELECTOR_TF, 4096, 4096, 151936, 256, 16) == 256 + 4096 * 256 * 4
+    # top-K: one sorted list of K 8-byte keys per row per vocabulary slice
+    b = D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16)
+    assert b > 256 and (b - 256) % (8 * 16 * 8) == 0
+    assert D.workspace_bytes(D.OP_UNARY_TOPK, 0, 4096, 151936, 0, 16) == 0
+    assert D.workspace_bytes(7, 8, 4096, 151936, 0, 16) == 0

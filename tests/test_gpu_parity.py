@@ -1,0 +1,289 @@
+"""GPU parity: the HIP library, called through the C ABI, against the CPU
+oracle on the same seeded inputs.  Sizes span several tiles with ragged tails
+in both kernel regimes (weight streaming for <= 8 rows, LDS-tiled MFMA for
+more); full-size workloads are in test_gpu_workloads.py."""
+import numpy as np
+import pytest
+import torch
+
+from block_draft_head_amd.inputs import Workload, make_inputs
+from oracle import dflash2_oracle as O
+from tests.helpers import (act_ok, close, compare_tf, compare_topk, compare_walk, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def D():
+    from block_draft_head_amd import dflash2
+    assert torch.cuda.is_available(), "no GPU visible"
+    return dflash2
+
+
+def wl(name="t", n_blocks=4, block_size=8, hidden=256, vocab=4096, dtype="bf16", taps=2, group_size=16,
+       rank=32, top_k=16, mode="walk+tf"):
+    return Workload(name, n_blocks, block_size, hidden, vocab, dtype, taps, group_size, rank, top_k, mode)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# --------------------------------------------------------------------- conv
+
+CONV_CASES = [
+    # (n_blocks, bs, H, T, gs, dtype): streaming (N <= 8) and tiled, ragged row tiles
+    (1, 8, 256, 2, 16, "bf16"), (1, 8, 256, 2, 16, "f32"), (2, 4, 512, 3, 8, "bf16"),
+    (1, 4, 256, 1, 64, "bf16"), (1, 8, 256, 8, 32, "bf16"),
+    (17, 8, 256, 2, 16, "bf16"), (17, 8, 256, 2, 16, "f32"), (9, 16, 384, 8, 32, "bf16"),
+    (40, 4, 256, 3, 4, "bf16"), (5, 16, 256, 16, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("nb,bs,H,T,gs,dtype", CONV_CASES)
+def test_conv_prepare_and_finish(D, nb, bs, H, T, gs, dtype):
+    log(f"conv nb={nb} bs={bs} H={H} T={T} gs={gs} {dtype}")
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, taps=T, group_size=gs, dtype=dtype)
+    # a larger projection so the dynamic part is well above rounding noise
+    inp = make_inputs(w, seed=3, fields=["h", "y", "base", "w_proj"])
+    if dtype == "f32":
+        inp["w_proj"] = inp["w_proj"] * np.float32(4.0)
+    xo, kp = D.conv_prepare(to_dev(inp["h"]), to_dev(inp["w_proj"]), to_dev(inp["base"]), bs, T, gs)
+    xo_r, kp_r, ex = O.conv_prepare(inp["h"], inp["w_proj"], inp["base"], bs, T, gs, dtype)
+    ok = act_ok(to_np(xo), ex, dtype)
+    assert ok.all(), f"{(~ok).sum()} x_out mismatches, first at {np.argwhere(~ok)[:3]}"
+    assert close(to_np(kp), kp_r).all()
+    # finish, fed the same float32 k_post on both sides
+    kp32 = kp_r.astype(np.float32)
+    yo = D.conv_finish(to_dev(inp["y"]), to_dev(kp32), to_dev(inp["base"]), bs, T, gs)
+    _, ey = O.conv_finish(inp["y"], kp32, inp["base"], bs, T, gs, dtype)
+    ok = act_ok(to_np(yo), ey, dtype)
+    assert ok.all(), f"{(~ok).sum()} y_out mismatches"
+
+
+@pytest.mark.parametrize("nb,bs", [(1, 8), (16, 8)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_conv_identity_init_is_exact_on_device(D, nb, bs, dtype):
+    H, T, gs = 256, 2, 16
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, taps=T, group_size=gs, dtype=dtype)
+    inp = make_inputs(w, seed=4, fields=["h", "y"])
+    f = torch.float32 if dtype == "f32" else torch.bfloat16
+    base = torch.zeros((2, T, H), dtype=f, device="cuda")
+    base[:, 0] = 1
+    wp = torch.zeros((2 * T * (H // gs), H), dtype=f, device="cuda")
+    x = to_dev(inp["h"])
+    xo, kp = D.conv_prepare(x, wp, base, bs, T, gs)
+    assert torch.equal(xo.float(), x.float()) and not kp.any()
+    y = to_dev(inp["y"])
+    assert torch.equal(D.conv_finish(y, kp, base, bs, T, gs).float(), y.float())
+
+
+def test_conv_does_not_leak_across_blocks_on_device(D):
+    nb, bs, H, T, gs = 6, 8, 256, 3, 16
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, taps=T, group_size=gs)
+    inp = make_inputs(w, seed=5, fields=["h", "y", "base", "w_proj"])
+    x, y, base, wp = (to_dev(inp[k]) for k in ("h", "y", "base", "w_proj"))
+    xo, kp = D.conv_prepare(x, wp, base, bs, T, gs)
+    yo = D.conv_finish(y, kp, base, bs, T, gs)
+    for blk in range(1, nb):
+        x2, y2 = x.clone(), y.clone()
+        x2[: blk * bs] = 100 * torch.randn_like(x2[: blk * bs].float()).to(x2.dtype)
+        y2[: blk * bs] = -100 * torch.randn_like(y2[: blk * bs].float()).to(y2.dtype)
+        xo2, kp2 = D.conv_prepare(x2, wp, base, bs, T, gs)
+        yo2 = D.conv_finish(y2, kp, base, bs, T, gs)
+        sl = slice(blk * bs, None)
+        assert torch.equal(xo2[sl], xo[sl]) and torch.equal(kp2[sl], kp[sl]) and torch.equal(yo2[sl], yo[sl])
+
+
+# --------------------------------------------------------------- unary top-K
+
+TOPK_CASES = [
+    # (N, H, V, K, dtype): streaming for N <= 8, tiled above; ragged vocab tails
+    (1, 256, 4133, 16, "bf16"), (8, 256, 4133, 16, "bf16"), (5, 512, 3001, 64, "bf16"),
+    (8, 256, 4096, 1, "f32"), (3, 256, 2000, 16, "f32"), (8, 1024, 20000, 16, "bf16"),
+    (9, 256, 3000, 16, "bf16"), (128, 256, 4096, 16, "f32"), (300, 256, 5000, 64, "bf16"),
+    (130, 512, 2999, 7, "bf16"), (64, 256, 16, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("N,H,V,K,dtype", TOPK_CASES)
+def test_unary_topk(D, N, H, V, K, dtype):
+    log(f"topk N={N} H={H} V={V} K={K} {dtype}")
+    w = wl(n_blocks=N, block_size=1, hidden=H, vocab=V, top_k=K, dtype=dtype)
+    inp = make_inputs(w, seed=6, fields=["h", "w_lm", "gold"])
+    ids, vals, gl = D.unary_topk(to_dev(inp["h"]), to_dev(inp["w_lm"]), K, gold_ids=to_dev(inp["gold"]))
+    U = O.lm_logits(inp["h"], inp["w_lm"], dtype)
+    fails, flags, msgs = compare_topk(to_np(ids), to_np(vals), U, K)
+    log(f"  fails={fails} flags={flags}")
+    assert fails == 0, msgs[:5]
+    assert flags <= max(1, N // 50)
+    assert close(to_np(gl), U[np.arange(N), inp["gold"]]).all()
+
+
+@pytest.mark.parametrize("N", [8, 40])
+def test_unary_topk_exact_ties_take_the_lower_id(D, N):
+    H, V, K = 256, 1000, 16
+    h = torch.randn(N, H, device="cuda").bfloat16()
+    row = torch.randn(H, device="cuda").bfloat16()
+    w = torch.randn(V, H, device="cuda").bfloat16() * 0.01
+    tied = torch.tensor([977, 3, 500, 41, 42, 700, 5, 999], device="cuda")
+    w[tied] = row
+    h[:, :] = row  # every row's best direction is the tied one
+    ids, vals, _ = D.unary_topk(h, w, K)
+    want = torch.sort(tied).values.int()
+    assert torch.equal(ids[:, :8], want.expand(N, 8))
+    assert torch.equal(vals[:, :8], vals[:, :1].expand(N, 8))
+
+
+def test_unary_topk_is_deterministic(D):
+    w = wl(n_blocks=300, block_size=1, hidden=256, vocab=7000, top_k=16)
+    inp = make_inputs(w, seed=8, fields=["h", "w_lm"])
+    h, wl_ = to_dev(inp["h"]), to_dev(inp["w_lm"])
+    a = D.unary_topk(h, wl_, 16)
+    b = D.unary_topk(h, wl_, 16)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ selector
+
+def rand_cands(rng, N, V, K):
+    ids = np.stack([rng.permutation(V)[:K] for _ in range(N)]).astype(np.int32)
+    vals = (-np.sort(-rng.standard_normal((N, K)), axis=1)).astype(np.float32)
+    return ids, vals
+
+
+WALK_CASES = [
+    # (n_blocks, bs, H, V, r, K, dtype)
+    (1, 8, 256, 1000, 32, 16, "f32"), (3, 8, 256, 1000, 256, 16, "bf16"), (16, 8, 256, 4096, 32, 16, "f32"),
+    (5, 16, 256, 3000, 40, 20, "bf16"), (4, 16, 512, 5000, 512, 64, "bf16"), (7, 2, 256, 500, 64, 1, "bf16"),
+    (2, 3, 256, 800, 256, 33, "bf16"), (64, 8, 256, 2000, 256, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("nb,bs,H,V,r,K,dtype", WALK_CASES)
+def test_selector_walk_and_tf(D, nb, bs, H, V, r, K, dtype):
+    log(f"walk nb={nb} bs={bs} H={H} V={V} r={r} K={K} {dtype}")
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, vocab=V, rank=r, top_k=K, dtype=dtype)
+    inp = make_inputs(w, seed=9, fields=["h", "w_h", "cb_pred", "cb_succ", "anchors", "pred", "gold", "force"])
+    # larger codebooks so the selector overrides the unary pick regularly
+    if dtype == "f32":
+        inp["cb_pred"] *= np.float32(6)
+        inp["cb_succ"] *= np.float32(6)
+    rng = np.random.default_rng(nb * 1000 + K)
+    N = nb * bs
+    ids, vals = rand_cands(rng, N, V, K)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    path, ps = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids), to_dev(vals),
+                               dev["anchors"], bs)
+    g64 = O.context_projection(inp["h"], inp["w_h"], dtype)
+    u64 = vals.astype(np.float64)
+    fails, flags, teeth, msgs = compare_walk(to_np(path), to_np(ps), g64, inp["cb_pred"], inp["cb_succ"], ids, u64,
+                                             inp["anchors"], bs, dtype)
+    log(f"  walk fails={fails} flags={flags} teeth={teeth}/{nb * (bs - 1)}")
+    assert fails == 0, msgs[:5]
+    if flags == 0:
+        ref_path, _ = O.selector_walk(g64, inp["cb_pred"], inp["cb_succ"], ids, u64, inp["anchors"], bs, dtype)
+        assert np.array_equal(to_np(path), ref_path)
+    # teacher forcing with random predecessors, gold ids and forcing
+    gold = inp["gold"].copy()
+    gold[::3] = ids[::3, K // 2]  # a third of the rows have the gold in the set
+    glog = rng.standard_normal(N).astype(np.float32)
+    gpu = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids), to_dev(vals),
+                              dev["pred"], gold_ids=to_dev(gold), force=dev["force"], gold_logit=to_dev(glog))
+    ref = O.selector_score_tf(g64, inp["cb_pred"], inp["cb_succ"], ids, u64, inp["pred"], dtype, gold_ids=gold,
+                              force=inp["force"], gold_logit=glog.astype(np.float64))
+    fails, flags, msgs = compare_tf(tuple(to_np(t) for t in gpu), ref, ids)
+    log(f"  tf fails={fails} flags={flags}")
+    assert fails == 0, msgs[:5]
+    # replay: the walk's own predecessors through teacher forcing give the walk
+    pred = np.zeros(N, np.int32)
+    P = to_np(path)
+    for b in range(nb):
+        pred[b * bs + 1:(b + 1) * bs] = P[b, :-1]
+    pred[::bs] = inp["anchors"]  # position 0 is not scored by the walk
+    sc, best, _, _ = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids),
+                                         to_dev(vals), to_dev(pred))
+    best, sc = to_np(best).reshape(nb, bs), to_np(sc).reshape(nb, bs, K)
+    assert np.array_equal(best[:, 1:], P[:, 1:])
+    assert np.array_equal(sc.max(axis=2)[:, 1:], to_np(ps)[:, 1:])  # bit-exact replay
+
+
+def test_zero_successor_codebook_walks_the_unary_argmax(D):
+    nb, bs, H, V, r, K = 8, 8, 256, 1000, 64, 16
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, vocab=V, rank=r, top_k=K)
+    inp = make_inputs(w, seed=10, fields=["h", "w_h", "cb_pred", "anchors"])
+    rng = np.random.default_rng(1)
+    ids, vals = rand_cands(rng, nb * bs, V, K)
+    zero_b = torch.zeros((V, r), dtype=torch.bfloat16, device="cuda")
+    path, ps = D.selector_walk(to_dev(inp["h"]), to_dev(inp["w_h"]), to_dev(inp["cb_pred"]), zero_b, to_dev(ids),
+                               to_dev(vals), to_dev(inp["anchors"]), bs)
+    P = to_np(path)
+    assert np.array_equal(P[:, 1:], ids.reshape(nb, bs, K)[:, 1:, 0])
+    assert np.array_equal(to_np(ps)[:, 1:], vals.reshape(nb, bs, K)[:, 1:, 0])
+
+
+def test_out_of_range_ids_are_flagged_not_read(D):
+    nb, bs, H, V, r, K = 4, 8, 256, 1000, 32, 16
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, vocab=V, rank=r, top_k=K)
+    inp = make_inputs(w, seed=11, fields=["h", "w_h", "cb_pred", "cb_succ", "anchors", "w_lm"])
+    rng = np.random.default_rng(2)
+    ids, vals = rand_cands(rng, nb * bs, V, K)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    ws = D.make_workspace(D.OP_SELECTOR_WALK, nb * bs, H, V, r, K, "cuda")
+    anchors = inp["anchors"].copy()
+    anchors[1] = V + 5
+    anchors[2] = -1
+    path, ps = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids), to_dev(vals),
+                               to_dev(anchors), bs, workspace=ws)
+    assert D.read_device_status(ws) == 8
+    P = to_np(path)
+    assert np.all(P[1] == -1) and np.all(P[2] == -1) and np.all(P[0] >= 0) and np.all(P[3] >= 0)
+    # a clean call on the same workspace clears the word
+    D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids), to_dev(vals),
+                    dev["anchors"], bs, workspace=ws)
+    assert D.read_device_status(ws) == 0
+    # gold ids out of range in the LM head
+    ws2 = D.make_workspace(D.OP_UNARY_TOPK, nb * bs, H, V, 0, K, "cuda")
+    gold = np.arange(nb * bs, dtype=np.int32)
+    gold[3] = V
+    _, _, gl = D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=to_dev(gold), workspace=ws2)
+    assert D.read_device_status(ws2) == 8 and torch.isnan(gl[3]) and not torch.isnan(gl[4])
+    # predecessor out of range in teacher forcing
+    ws3 = D.make_workspace(D.OP_SELECTOR_TF, nb * bs, H, V, r, K, "cuda")
+    pred = np.zeros(nb * bs, np.int32)
+    pred[5] = -7
+    _, best, _, _ = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids),
+                                        to_dev(vals), to_dev(pred), workspace=ws3)
+    assert D.read_device_status(ws3) == 8 and int(best[5]) == -1 and int(best[4]) >= 0
+
+
+# -------------------------------------------------------------- end to end
+
+def test_tiny_fp32_workload_end_to_end(D):
+    """16 blocks x 8, H 256, V 4096, fp32: LM head -> walk and teacher forcing."""
+    from block_draft_head_amd.inputs import WORKLOADS
+    w = WORKLOADS["tiny_fp32_16x8_h256_v4096"]
+    inp = make_inputs(w)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    bs, T, gs, K = w.block_size, w.taps, w.group_size, w.top_k
+    xo, kp = D.conv_prepare(dev["h"], dev["w_proj"], dev["base"], bs, T, gs)
+    _, kp_r, ex = O.conv_prepare(inp["h"], inp["w_proj"], inp["base"], bs, T, gs, "f32")
+    assert act_ok(to_np(xo), ex, "f32").all() and close(to_np(kp), kp_r).all()
+    ids, vals, gl = D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=dev["gold"])
+    U = O.lm_logits(inp["h"], inp["w_lm"], "f32")
+    fails, flags, msgs = compare_topk(to_np(ids), to_np(vals), U, K)
+    assert fails == 0, msgs[:5]
+    gids = to_np(ids)
+    u64 = U[np.arange(U.shape[0])[:, None], gids]
+    g64 = O.context_projection(inp["h"], inp["w_h"], "f32")
+    path, ps = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"], bs)
+    fails, flags, teeth, msgs = compare_walk(to_np(path), to_np(ps), g64, inp["cb_pred"], inp["cb_succ"], gids, u64,
+                                             inp["anchors"], bs, "f32")
+    log(f"tiny walk fails={fails} flags={flags} teeth={teeth}")
+    assert fails == 0, msgs[:5]
+    gpu = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"],
+                              gold_ids=dev["gold"], force=dev["force"], gold_logit=gl)
+    ref = O.selector_score_tf(g64, inp["cb_pred"], inp["cb_succ"], gids, u64, inp["pred"], "f32",
+                              gold_ids=inp["gold"], force=inp["force"], gold_logit=U[np.arange(U.shape[0]), inp["gold"]])
+    fails, flags, msgs = compare_tf(tuple(to_np(t) for t in gpu), ref, gids)
+    assert fails == 0, msgs[:5]
