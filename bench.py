@@ -1,0 +1,278 @@
+"""Throughput of the DFlash2 draft-block head on one MI355X.
+
+A step is one pass of the whole draft-head path over one batch of synthetic
+input, inputs resident in HBM:
+  walk workloads:  conv prepare + conv finish (one wrapped sublayer),
+                   unary LM-head top-K, context projection + greedy walk;
+  packed TF:       the same conv, unary top-K with gold logits, context
+                   projection + teacher-forced scores and K-way CE.
+The teacher-forced scorer is also timed on walk workloads (field "tf_ms").
+
+Prints ONE JSON line (rank 0):  value = anchor blocks per second.
+The roofline object covers the dominant op (LM head + top-K): algorithmic
+bytes (or FLOPs) per launch over its average duration from HIP events on the
+launch stream inside the timed region.  cpu_baseline is the CPU oracle timed
+on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DFlash2 draft-head blocks/s + % of HBM/MFMA roofline, Qwen3-8B shape"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+LMHEAD_SOURCES = ["lmhead.hip", "gemm.hpp", "common.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_1x8_h4096_v151936")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def lmhead_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in LMHEAD_SOURCES:
+        with open(os.path.join(ROOT, "block_draft_head_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def lmhead_work(w):
+    """Algorithmic bytes and FLOPs of one LM-head + top-K launch: the weights
+    stream once, activations are read once, ids and values are written once;
+    logits never leave the chip."""
+    es = 4 if w.dtype == "f32" else 2
+    N = w.n_rows
+    bytes_ = w.vocab * w.hidden * es + N * w.hidden * es + N * w.top_k * 8
+    flops = 2.0 * N * w.vocab * w.hidden
+    return bytes_, flops
+
+
+def traffic_for(w, launches_key):
+    """HBM bytes per launch from committed rocprofv3 counters, or None when
+    they are missing or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    e = t.get(launches_key)
+    if not e or e.get("source_hash") != lmhead_source_hash():
+        return None
+    return e["fetch_kib"] * 1024.0 * e["fetch_scale"] + e["write_kib"] * 1024.0 * e["write_scale"]
+
+
+def cpu_baseline(w, inp, budget_s):
+    """The oracle as it stands, on the host: whole steps of the same workload
+    on a bounded sample of anchor blocks (all blocks when they fit)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dflash2_oracle as O
+
+    bs = w.block_size
+    blocks = 1
+    t_all = 0.0
+    reps = 0
+    rows = slice(0, blocks * bs)
+    while True:
+        t0 = time.perf_counter()
+        h = inp["h"][rows]
+        xo, kp, _ = O.conv_prepare(h, inp["w_proj"], inp["base"], bs, w.taps, w.group_size, w.dtype)
+        O.conv_finish(inp["y"][rows], kp, inp["base"], bs, w.taps, w.group_size, w.dtype)
+        ids, vals, gl = O.unary_topk(h, inp["w_lm"], w.top_k, w.dtype,
+                                     gold_ids=inp["gold"][rows] if w.mode == "tf" else None)
+        g = O.context_projection(h, inp["w_h"], w.dtype)
+        if w.mode == "tf":
+            O.selector_score_tf(g, inp["cb_pred"], inp["cb_succ"], ids, vals, inp["pred"][rows], w.dtype,
+                                gold_ids=inp["gold"][rows], force=inp["force"][rows], gold_logit=gl)
+        else:
+            O.selector_walk(g, inp["cb_pred"], inp["cb_succ"], ids, vals, inp["anchors"][:blocks], bs, w.dtype)
+        t_all += time.perf_counter() - t0
+        reps += 1
+        if t_all >= budget_s or reps >= 50:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": reps * blocks / t_all, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{reps} whole oracle step(s) on {blocks} anchor block(s) of {w.name} "
+                  f"(float64 numpy, {t_all:.1f} s); host has {os.cpu_count()} CPUs",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              f"multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_draft_head_amd import dflash2 as D
+    from block_draft_head_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = make_inputs(w)
+    dev = {}
+    for k, a in inp.items():
+        if a.dtype == np.uint16:
+            dev[k] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            dev[k] = torch.from_numpy(a).cuda()
+    torch.cuda.synchronize()
+    print("[bench] inputs resident on the GPU", file=sys.stderr, flush=True)
+
+    bs, T, gs, K, r = w.block_size, w.taps, w.group_size, w.top_k, w.rank
+    N, H, V = w.n_rows, w.hidden, w.vocab
+    ws_topk = D.make_workspace(D.OP_UNARY_TOPK, N, H, V, 0, K, "cuda")
+    ws_sel = D.make_workspace(D.OP_SELECTOR_WALK if w.mode != "tf" else D.OP_SELECTOR_TF, N, H, V, r, K, "cuda")
+    ws_tf = D.make_workspace(D.OP_SELECTOR_TF, N, H, V, r, K, "cuda")
+    x_out = torch.empty_like(dev["h"])
+    k_post = torch.empty((N, T, H // gs), dtype=torch.float32, device="cuda")
+    y_out = torch.empty_like(dev["y"])
+    tf_mode = w.mode == "tf"
+    gold = dev["gold"] if tf_mode else None
+
+    OPS = ("conv", "lmhead", "selector")
+
+    def new_events():
+        return {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in OPS}
+
+    def step(ev=None):
+        """One pass of the path; `ev` brackets each op with events on the launch stream."""
+        def mark(k, i):
+            if ev is not None:
+                ev[k][i].record()
+        mark("conv", 0)
+        D.conv_prepare(dev["h"], dev["w_proj"], dev["base"], bs, T, gs, out=x_out, k_post=k_post)
+        D.conv_finish(dev["y"], k_post, dev["base"], bs, T, gs, out=y_out)
+        mark("conv", 1)
+        mark("lmhead", 0)
+        ids, vals, gl = D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=gold, workspace=ws_topk)
+        mark("lmhead", 1)
+        mark("selector", 0)
+        if tf_mode:
+            res = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"],
+                                      gold_ids=gold, force=dev["force"], gold_logit=gl, workspace=ws_sel)
+        else:
+            res = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"],
+                                  bs, workspace=ws_sel)
+        mark("selector", 1)
+        return ids, vals, res
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    events = [new_events() for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        ids, vals, res = step(events[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(stop)
+    op_ms = {k: [e[k][0].elapsed_time(e[k][1]) for e in events] for k in OPS}
+    ms_per_step = gpu_ms / args.steps
+
+    # teacher-forced scoring of the walk's own path (walk workloads), timed apart
+    tf_ms = None
+    if not tf_mode:
+        path = res[0]
+        pred = torch.empty(N, dtype=torch.int32, device="cuda")
+        pred.view(w.n_blocks, bs)[:, 1:] = path[:, :-1]
+        pred.view(w.n_blocks, bs)[:, 0] = dev["anchors"]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred, workspace=ws_tf)
+        a.record()
+        for _ in range(args.steps):
+            D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred, workspace=ws_tf)
+        b.record()
+        torch.cuda.synchronize()
+        tf_ms = a.elapsed_time(b) / args.steps
+        sc, best, _, _ = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred,
+                                             workspace=ws_tf)
+        replay_ok = bool(torch.equal(best.view(w.n_blocks, bs)[:, 1:], path[:, 1:]))
+    else:
+        replay_ok = None
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    lm_bytes, lm_flops = lmhead_work(w)
+    lm_ms = float(np.mean(op_ms["lmhead"]))
+    mfma_bound = lm_flops / lm_bytes > (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) and w.dtype == "bf16"
+    if mfma_bound:
+        achieved = lm_flops / (lm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(w, w.name)
+    roof["kernel"] = "unary LM head + top-K (lmhead kernel + slab merge)"
+    roof["algorithmic_bytes"] = lm_bytes
+    roof["avg_ms"] = lm_ms
+
+    out = {
+        "metric": METRIC,
+        "value": w.n_blocks * args.steps / (gpu_ms * 1e-3),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_blocks": w.n_blocks, "block_size": bs, "hidden": H, "vocab": V,
+                   "taps": T, "group_size": gs, "rank": r, "top_k": K, "mode": w.mode},
+        "roofline": roof,
+        "ops_ms": {k: float(np.mean(v)) for k, v in op_ms.items()},
+        "selector_plus_conv_over_lmhead": (float(np.mean(op_ms["conv"])) + float(np.mean(op_ms["selector"]))) / lm_ms,
+        "tf_ms": tf_ms,
+        "tf_replays_walk": replay_ok,
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
