@@ -173,6 +173,107 @@ __device__ __forceinline__ uint64_t sorted_insert(uint64_t cur, uint64_t key, in
     return cur;
 }
 
+// readlane of a 64-bit value from a wave-uniform lane.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Orders this wave's LDS accesses before and after the call with respect to
+// each other (a wave's LDS instructions execute in program order).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Top K (K <= 64) of up to 64*R keys held R per lane (key 0 = empty), by one
+// wave.  Lane j < K returns the j-th largest key (0 past the last key).
+// `scratch` is 128 keys of LDS owned by the wave.
+// A lower bound comes first: the largest v such that at least K lanes hold a
+// key whose high word is >= v (those K keys are all >= v << 32), found bit
+// by bit from ballot counts.  If that admits more than 64 keys, the bound is
+// redone over every key (the K-th largest high word).  The keys above it are
+// compacted to one per lane and ranked by one broadcast loop; only when more
+// than 64 keys share the bound's high word is every passing key ranked in
+// place instead (exact, slower).
+template <int R>
+__device__ __forceinline__ uint64_t wave_topk(const uint64_t (&k)[R], int K, uint64_t *scratch) {
+    const int lane = lane_id();
+    uint32_t lmh = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const uint32_t hw = (uint32_t)(k[i] >> 32);
+        lmh = hw > lmh ? hw : lmh;
+    }
+    uint32_t v = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t t = v | (1u << b);
+        if (__popcll(__ballot(lmh >= t)) >= K) v = t;
+    }
+    int C = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) C += __popcll(__ballot(k[i] != 0ull && (uint32_t)(k[i] >> 32) >= v));
+    if (C > 64) {
+        // tighten: the largest v with at least K keys whose high word is >= v
+        v = 0;
+        for (int b = 31; b >= 0; --b) {
+            const uint32_t t = v | (1u << b);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < R; ++i) cnt += __popcll(__ballot((uint32_t)(k[i] >> 32) >= t));
+            if (cnt >= K) v = t;
+        }
+    }
+    const uint64_t th = (uint64_t)v << 32;
+    bool pass[R];
+    C = 0;
+    wave_lds_fence();
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        pass[i] = k[i] != 0ull && k[i] >= th;
+        const unsigned long long m = __ballot(pass[i]);
+        const int pos = C + lanes_below(m);
+        if (pass[i] && pos < 64) scratch[pos] = k[i];
+        C += __popcll(m);
+    }
+    wave_lds_fence();
+    if (C <= 64) {
+        const uint64_t c = lane < C ? scratch[lane] : 0ull;
+        int rank = 0;
+        for (int j = 0; j < C; ++j) rank += readlane_u64(c, j) > c ? 1 : 0;
+        if (lane < C && rank < K) scratch[64 + rank] = c;
+    } else {
+        int rank[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) rank[i] = 0;
+#pragma unroll
+        for (int i2 = 0; i2 < R; ++i2) {
+            unsigned long long m = __ballot(pass[i2]);
+            while (m) {
+                const int src = __builtin_ctzll(m);
+                m &= m - 1;
+                const uint64_t cand = readlane_u64(k[i2], src);
+#pragma unroll
+                for (int i = 0; i < R; ++i) rank[i] += cand > k[i] ? 1 : 0;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            if (pass[i] && rank[i] < K) scratch[64 + rank[i]] = k[i];
+    }
+    wave_lds_fence();
+    const int kept = C < K ? C : K;
+    const uint64_t out = lane < kept ? scratch[64 + lane] : 0ull;
+    wave_lds_fence();
+    return out;
+}
+
 // Sets a bit of the status word (kernels that meet an out-of-range id).
 __device__ __forceinline__ void flag_status(uint32_t *status, uint32_t bit) {
     if (status) atomicOr(status, bit);

@@ -17,9 +17,10 @@ constexpr uint32_t kStatusIdRange = 1u;
 
 struct LmheadPlan {
     bool streaming;
-    int nw, tiles_per_wave, n_tiles;
+    int nw, prefetch, n_tiles;
     int grid_x, grid_y, n_lists;
-    size_t lds, partial_bytes;
+    int merge_rows;
+    size_t lds, merge_lds, partial_bytes;
 };
 LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
 

@@ -1,7 +1,7 @@
 // Unary LM-head logits over the full vocabulary with a fused per-row top-K.
 //
 // U[n, v] = <h[n], w_lm[v]> is formed tile by tile on the MFMA units and
-// filtered into per-row sorted candidate lists in LDS; logits never reach HBM.
+// filtered into per-row candidate lists in LDS; logits never reach HBM.
 // Each workgroup emits one sorted list of K keys per row for its slice of the
 // vocabulary, and topk_merge_kernel merges the slices.  A key orders
 // candidates by value, then by lower id (see make_key), so the result does not
@@ -12,42 +12,7 @@
 
 namespace dflash2 {
 
-// Merge `n_lists` descending lists of K keys (list c starts at src + c*stride)
-// into the top K, by one wave: every lane tracks the heads of the lists
-// lane, lane + 64, ...; each round the wave takes the largest head.  Lane k
-// returns the k-th key of the result (0 where fewer than K keys exist).
-template <int MAXL>
-__device__ uint64_t wave_merge_lists(const uint64_t *src, int n_lists, int stride, int K) {
-    const int l = lane_id();
-    int ptr[MAXL];
-    uint64_t head[MAXL];
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < MAXL; ++j) {
-        const int c = l + 64 * j;
-        ptr[j] = 0;
-        head[j] = c < n_lists ? src[(size_t)c * stride] : 0ull;
-        best = head[j] > best ? head[j] : best;
-    }
-    uint64_t mine = 0;
-    for (int k = 0; k < K; ++k) {
-        const uint64_t w = wave_max_u64(best);
-        if (l == k) mine = w;
-        if (w == 0) break;
-        if (best == w) {  // keys are unique: exactly one lane owns the winner
-            best = 0;
-#pragma unroll
-            for (int j = 0; j < MAXL; ++j) {
-                if (head[j] == w) {
-                    ++ptr[j];
-                    head[j] = ptr[j] < K ? src[(size_t)(l + 64 * j) * stride + ptr[j]] : 0ull;
-                }
-                best = head[j] > best ? head[j] : best;
-            }
-        }
-    }
-    return mine;
-}
+constexpr int kMergeChunk = 512;
 
 // Bitonic sort, descending, of 128 keys held two per lane (element 2*lane+h).
 __device__ __forceinline__ void bitonic128_desc(uint64_t &x0, uint64_t &x1) {
@@ -89,29 +54,49 @@ __device__ __forceinline__ void insert_survivors(uint64_t &cur, uint64_t &thr, u
 
 // ---------------------------------------------------------------- streaming
 //
-// At most 8 rows.  Every wave owns a contiguous run of 16-row vocabulary
-// tiles and streams each tile's rows of w_lm through MFMA (A = h from LDS).
-// Lane (n = l % 16, q = l / 16) holds the logits of vocabulary row
-// tile*16 + n for rows 4q .. 4q+3.  Each wave keeps its own sorted list per
-// row in LDS; the workgroup merges its waves' lists at the end.
-template <typename T, int NW>
+// At most 8 rows (decode).  One workgroup per CU owns a balanced contiguous
+// range of 16-row vocabulary tiles; its waves pull tiles from an LDS counter
+// and stream each tile's rows of w_lm through MFMA (A = h, from LDS in
+// fragment order).  A ring of P 16-byte loads per lane runs across tile
+// boundaries, so the next tile is already in flight while a tile's logits are
+// filtered.  Lane (n = l % 16, q = l / 16) holds the logits of vocabulary row
+// tile*16 + n for rows 4q .. 4q+3.  Each wave appends the logits above its
+// per-row threshold to an LDS candidate buffer (ballot compaction, no sort)
+// and shrinks a buffer to its top K only when it fills; the workgroup
+// reduces its waves' lists at the end.
+constexpr int kStreamWGs = 256;       // one per CU of an MI355X
+constexpr int kStreamMinLds = 81 * 1024;  // > half the CU's LDS: one workgroup per CU
+constexpr int kCandCap = 128;             // candidate slots per wave and row
+
+template <typename T, int NW, int P>
 __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
     const T *__restrict__ h, const T *__restrict__ w, int M, int H, int V, int K, int n_tiles,
-    int tiles_per_wave, const int32_t *__restrict__ gold, float *__restrict__ gold_logit,
-    uint64_t *__restrict__ partial, uint32_t *__restrict__ status) {
+    const int32_t *__restrict__ gold, float *__restrict__ gold_logit, uint64_t *__restrict__ partial,
+    uint32_t *__restrict__ status) {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int KC = 16 / (int)sizeof(T);
-    const int S = H / kstep_elems<T>();
+    constexpr int KS = 4 * KC;
+    const int S = H / KS;
     uint4 *afrag = reinterpret_cast<uint4 *>(smem);
-    uint64_t *lists = reinterpret_cast<uint64_t *>(smem + (size_t)S * 32 * 16);  // [NW][8][K]
+    uint64_t *bufs = reinterpret_cast<uint64_t *>(smem + (size_t)S * 32 * 16);  // [NW][8][kCandCap]
+    uint64_t *scratch = bufs + NW * 8 * kCandCap;                                // [NW][128]
+    int *cnts = reinterpret_cast<int *>(scratch + NW * 128);                     // [NW][8]
+    int *qctr = cnts + NW * 8;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     if (blockIdx.x == 0 && threadIdx.x == 0 && status) *status = 0u;
 
     load_afrag<T>(afrag, h, M, H);
-    for (int i = threadIdx.x; i < NW * 8 * K; i += blockDim.x) lists[i] = 0ull;
+    if (threadIdx.x == 0) *qctr = 0;
     __syncthreads();
 
-    uint64_t *mylists = lists + wave * 8 * K;
+    const int t0 = (int)((long long)blockIdx.x * n_tiles / gridDim.x);
+    const int t1 = (int)((long long)(blockIdx.x + 1) * n_tiles / gridDim.x);
+    auto grab = [&]() -> int {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(qctr, 1);
+        return t0 + __shfl(v, 0);
+    };
+    uint64_t *mybuf = bufs + wave * 8 * kCandCap;
     const int n = lane & 15, q = lane >> 4;
     int grow[4];
     uint64_t thr[4];
@@ -121,39 +106,95 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
         grow[e] = (gold && row < M) ? gold[row] : -1;
         thr[e] = 0ull;
     }
-    const int gw = blockIdx.x * NW + wave;
-    const int t0 = gw * tiles_per_wave;
-    const int t1 = min(t0 + tiles_per_wave, n_tiles);
-    for (int t = t0; t < t1; ++t) {
-        const int v = t * 16 + n;
-        const T *brow = w + (size_t)min(v, V - 1) * H + q * KC;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        stream_accumulate<T>(acc, afrag, brow, 0, S);
+    int cnt[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 4 * q + e;
-            const bool ok = row < M && v < V;
-            const uint64_t key = ok ? make_key(acc[e], (uint32_t)v) : 0ull;
-            if (ok && grow[e] == v) gold_logit[row] = acc[e];
-            unsigned long long mask = __ballot(key > thr[e]);
-            while (mask) {
-                const int src = __ffsll((unsigned long long)mask) - 1;
-                mask &= mask - 1;
-                const uint64_t k = shfl_u64(key, src);
-                const int r = 4 * (src >> 4) + e;
-                uint64_t *L = mylists + r * K;
-                uint64_t cur = lane < K ? L[lane] : 0ull;
-                cur = sorted_insert(cur, k, K);
-                if (lane < K) L[lane] = cur;
-                const uint64_t tail = shfl_u64(cur, K - 1);
-                if (4 * q + e == r) thr[e] = tail;
+    for (int r = 0; r < 8; ++r) cnt[r] = 0;
+    uint64_t *myscratch = scratch + wave * 128;
+    // Shrink row r's candidates to its top K and raise its threshold.
+    auto compact = [&](int r) {
+        uint64_t *B = mybuf + r * kCandCap;
+        uint64_t k[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) k[i] = lane + 64 * i < cnt[r] ? B[lane + 64 * i] : 0ull;
+        const uint64_t top = wave_topk<2>(k, K, myscratch);
+        const int kept = cnt[r] < K ? cnt[r] : K;
+        if (lane < K) B[lane] = top;
+        cnt[r] = kept;
+        const uint64_t kth = readlane_u64(top, K - 1);
+        if (q == (r >> 2)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e == (r & 3)) thr[e] = kth;
+        }
+    };
+    auto row_ptr = [&](int t) -> const T * {
+        return w + (size_t)min(t * 16 + n, V - 1) * H + q * KC;
+    };
+
+    int t = grab();
+    if (t < t1) {
+        uint4 ring[P];
+        const T *cur = row_ptr(t);
+#pragma unroll
+        for (int i = 0; i < P; ++i) ring[i] = *reinterpret_cast<const uint4 *>(cur + (size_t)i * KS);
+        while (true) {
+            const int tn = grab();
+            const T *nxt = row_ptr(tn < t1 ? tn : t);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < S; s0 += P) {
+                const bool same = s0 + P < S;
+#pragma unroll
+                for (int i = 0; i < P; ++i) {
+                    const uint4 b = ring[i];
+                    if (same)
+                        ring[i] = *reinterpret_cast<const uint4 *>(cur + (size_t)(s0 + P + i) * KS);
+                    else if (tn < t1)
+                        ring[i] = *reinterpret_cast<const uint4 *>(nxt + (size_t)i * KS);
+                    mma16<T>(acc, afrag_get(afrag, s0 + i, lane), b);
+                }
             }
+            const int v = t * 16 + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 4 * q + e;
+                const bool ok = row < M && v < V;
+                const uint64_t key = ok ? make_key(acc[e], (uint32_t)v) : 0ull;
+                if (ok && grow[e] == v) gold_logit[row] = acc[e];
+                const bool pass = key > thr[e];
+                const unsigned long long mask = __ballot(pass);
+                const int c0 = __popcll(mask & 0xffffull), c1 = __popcll(mask & 0xffff0000ull);
+                if (pass) {
+                    const int pos = lanes_below(mask) - (q ? c0 : 0);
+                    mybuf[row * kCandCap + (q ? cnt[4 + e] : cnt[e]) + pos] = key;
+                }
+                cnt[e] += c0;
+                cnt[4 + e] += c1;
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (cnt[r] > kCandCap - 16) compact(r);
+            if (tn >= t1) break;
+            t = tn;
+            cur = nxt;
         }
     }
+    if (lane < 8) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (lane == r) cnts[wave * 8 + r] = cnt[r];
+    }
     __syncthreads();
+    // the workgroup's list per row: top K over every wave's candidates
     for (int row = wave; row < M; row += NW) {
-        const uint64_t key = wave_merge_lists<(NW + 63) / 64>(lists + row * K, NW, 8 * K, K);
-        if (lane < K) partial[((size_t)row * gridDim.x + blockIdx.x) * K + lane] = key;
+        constexpr int R = 2 * NW;
+        uint64_t k[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int ww = i >> 1, slot = lane + 64 * (i & 1);
+            k[i] = slot < cnts[ww * 8 + row] ? bufs[(ww * 8 + row) * kCandCap + slot] : 0ull;
+        }
+        const uint64_t top = wave_topk<R>(k, K, myscratch);
+        if (lane < K) partial[((size_t)row * gridDim.x + blockIdx.x) * K + lane] = top;
     }
 }
 
@@ -229,23 +270,70 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
 }
 
 // ---------------------------------------------------------------- merge
-// One wave per row: merge the row's per-slab lists into the final top-K.
-__global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t *__restrict__ partial, int M,
+// One workgroup of 8 waves per row.  The row's n_lists sorted lists (K keys
+// each) are cut into chunks of 512 keys; each wave reduces chunks to their
+// top K in LDS; the survivors are reduced again until one chunk is left.
+
+__device__ __forceinline__ void merge_stage(const uint64_t *src, int n, int K, uint64_t *dst,
+                                            bool final_stage, int32_t *out_ids, float *out_vals,
+                                            uint64_t *scratch) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int chunks = (n + kMergeChunk - 1) / kMergeChunk;
+    for (int c = wave; c < chunks; c += nw) {
+        const int base = c * kMergeChunk, nc = min(kMergeChunk, n - base);
+        uint64_t top;
+        if (nc <= 128) {
+            // small chunk: two keys per lane, so most lanes hold a key
+            uint64_t k[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) k[i] = lane + 64 * i < nc ? src[base + lane + 64 * i] : 0ull;
+            top = wave_topk<2>(k, K, scratch + wave * 128);
+        } else {
+            // lane l holds keys [8l, 8l + 8): runs of sorted lists, so the
+            // lane maxima are mostly list heads
+            uint64_t k[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) k[i] = lane * 8 + i < nc ? src[base + lane * 8 + i] : 0ull;
+            top = wave_topk<8>(k, K, scratch + wave * 128);
+        }
+        if (lane < K) {
+            if (final_stage) {
+                out_ids[lane] = top ? (int32_t)key_id(top) : -1;
+                out_vals[lane] = top ? key_val(top) : -__builtin_inff();
+            } else {
+                dst[(size_t)c * K + lane] = top;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(512) void topk_merge_kernel(const uint64_t *__restrict__ partial, int M,
                                                          int n_lists, int K, int V,
                                                          int32_t *__restrict__ out_ids,
                                                          float *__restrict__ out_vals,
                                                          const int32_t *__restrict__ gold,
                                                          float *__restrict__ gold_logit,
-                                                         uint32_t *__restrict__ status) {
-    const int lane = lane_id();
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
-    const uint64_t key = wave_merge_lists<16>(partial + (size_t)row * n_lists * K, n_lists, K, K);
-    if (lane < K) {
-        out_ids[(size_t)row * K + lane] = key ? (int32_t)key_id(key) : -1;
-        out_vals[(size_t)row * K + lane] = key ? key_val(key) : -__builtin_inff();
+                                                         uint32_t *__restrict__ status, int lds_keys) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint64_t *bufA = reinterpret_cast<uint64_t *>(smem);
+    uint64_t *bufB = bufA + lds_keys;
+    uint64_t *scratch = bufB + lds_keys;  // 8 waves x 128 keys
+    const int row = blockIdx.x;
+    int n = n_lists * K;
+    const uint64_t *src = partial + (size_t)row * n;
+    uint64_t *dst = bufA;
+    int32_t *oi = out_ids + (size_t)row * K;
+    float *ov = out_vals + (size_t)row * K;
+    while (true) {
+        const bool fin = n <= kMergeChunk;
+        merge_stage(src, n, K, dst, fin, oi, ov, scratch);
+        if (fin) break;
+        __syncthreads();
+        n = (n + kMergeChunk - 1) / kMergeChunk * K;
+        src = dst;
+        dst = dst == bufA ? bufB : bufA;
     }
-    if (gold && lane == 0) {
+    if (gold && threadIdx.x == 0) {
         const int g = gold[row];
         if (g < 0 || g >= V) {
             gold_logit[row] = __builtin_nanf("");
@@ -256,22 +344,26 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const uint64_t *__restr
 
 // ---------------------------------------------------------------- host side
 
+static int first_stage_keys(int n_lists, int K) {
+    return (n_lists * K + kMergeChunk - 1) / kMergeChunk * K;
+}
+
 LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
     LmheadPlan p{};
     const int es = dtype == 0 ? 4 : 2;
-    const size_t stream_lds = (size_t)(H / (4 * (16 / es))) * 32 * 16 + (size_t)8 * 8 * K * 8;
+    const int S = H / (4 * (16 / es));
+    const int nw = 8;
+    size_t stream_lds = (size_t)S * 32 * 16 + (size_t)nw * (8 * kCandCap + 128) * 8 + (size_t)nw * 8 * 4 + 16;
+    if (stream_lds < (size_t)kStreamMinLds) stream_lds = kStreamMinLds;
     if (M <= kStreamMaxRows && stream_lds <= 160 * 1024) {
         p.streaming = true;
-        p.nw = 8;
-        const int n_tiles = (V + 15) / 16;
-        const int target_waves = 256 * 16;  // 256 CUs x 16 resident waves
-        p.tiles_per_wave = (n_tiles + target_waves - 1) / target_waves;
-        const int n_waves = (n_tiles + p.tiles_per_wave - 1) / p.tiles_per_wave;
-        p.grid_x = (n_waves + p.nw - 1) / p.nw;
+        p.nw = nw;
+        p.n_tiles = (V + 15) / 16;
+        p.grid_x = p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs;
         p.grid_y = 1;
         p.n_lists = p.grid_x;
-        p.n_tiles = n_tiles;
         p.lds = stream_lds;
+        p.prefetch = S % 16 == 0 ? 16 : S % 8 == 0 ? 8 : S % 4 == 0 ? 4 : S % 2 == 0 ? 2 : 1;
     } else {
         p.streaming = false;
         const int n_mt = (int)((M + 127) / 128);
@@ -288,14 +380,30 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         const size_t ctile = (size_t)128 * (128 + 4) * 4;
         p.lds = (stage > ctile ? stage : ctile) + (size_t)128 * K * 8;
     }
+    // merge: LDS for the first reduction stage's survivors (later stages are smaller)
+    const int first = first_stage_keys(p.n_lists, K);
+    p.merge_rows = 1;
+    p.merge_lds = (size_t)2 * first * 8 + 8 * 128 * 8;
     p.partial_bytes = (size_t)M * p.n_lists * K * 8;
     return p;
 }
 
-template <typename T, class F>
+template <class F>
 static hipError_t set_lds(F *kernel, size_t lds) {
     return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <typename T, int P>
+static hipError_t launch_stream(const LmheadPlan &p, int64_t M, int H, int V, int K, const void *h,
+                                const void *w, const int32_t *gold, float *gold_logit,
+                                uint64_t *partial, uint32_t *status, hipStream_t stream) {
+    auto kern = lmhead_stream_kernel<T, 8, P>;
+    hipError_t e = set_lds(kern, p.lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(64 * 8), p.lds, stream, (const T *)h, (const T *)w,
+                       (int)M, H, V, K, p.n_tiles, gold, gold_logit, partial, status);
+    return hipGetLastError();
 }
 
 template <typename T>
@@ -305,21 +413,26 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
                              hipStream_t stream) {
     hipError_t e;
     if (p.streaming) {
-        auto kern = lmhead_stream_kernel<T, 8>;
-        if ((e = set_lds<T>(kern, p.lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(64 * 8), p.lds, stream, (const T *)h,
-                           (const T *)w, (int)M, H, V, K, p.n_tiles, p.tiles_per_wave, gold,
-                           gold_logit, partial, status);
+        switch (p.prefetch) {
+            case 16: e = launch_stream<T, 16>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
+            case 8: e = launch_stream<T, 8>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
+            case 4: e = launch_stream<T, 4>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
+            case 2: e = launch_stream<T, 2>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
+            default: e = launch_stream<T, 1>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
+        }
     } else {
         auto kern = lmhead_tiled_kernel<T>;
-        if ((e = set_lds<T>(kern, p.lds)) != hipSuccess) return e;
+        if ((e = set_lds(kern, p.lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(p.grid_x, p.grid_y), dim3(256), p.lds, stream, (const T *)h,
                            (const T *)w, (int)M, H, V, K, p.n_tiles, gold, gold_logit, partial,
                            status);
+        e = hipGetLastError();
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream,
-                       partial, (int)M, p.n_lists, K, V, out_ids, out_vals, gold, gold_logit, status);
+    if (e != hipSuccess) return e;
+    if ((e = set_lds(topk_merge_kernel, p.merge_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)M), dim3(512), p.merge_lds, stream, partial, (int)M,
+                       p.n_lists, K, V, out_ids, out_vals, gold, gold_logit, status,
+                       first_stage_keys(p.n_lists, K));
     return hipGetLastError();
 }
 
