@@ -154,74 +154,66 @@ def main():
     tf_mode = w.mode == "tf"
     gold = dev["gold"] if tf_mode else None
 
-    OPS = ("conv", "lmhead", "selector")
-
-    def new_events():
-        return {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in OPS}
-
-    def step(ev=None):
-        """One pass of the path; `ev` brackets each op with events on the launch stream."""
-        def mark(k, i):
-            if ev is not None:
-                ev[k][i].record()
-        mark("conv", 0)
+    def op_conv():
         D.conv_prepare(dev["h"], dev["w_proj"], dev["base"], bs, T, gs, out=x_out, k_post=k_post)
         D.conv_finish(dev["y"], k_post, dev["base"], bs, T, gs, out=y_out)
-        mark("conv", 1)
-        mark("lmhead", 0)
-        ids, vals, gl = D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=gold, workspace=ws_topk)
-        mark("lmhead", 1)
-        mark("selector", 0)
+
+    def op_lmhead():
+        return D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=gold, workspace=ws_topk)
+
+    def op_selector(ids, vals, gl):
         if tf_mode:
-            res = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"],
-                                      gold_ids=gold, force=dev["force"], gold_logit=gl, workspace=ws_sel)
-        else:
-            res = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"],
-                                  bs, workspace=ws_sel)
-        mark("selector", 1)
-        return ids, vals, res
+            return D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"],
+                                       gold_ids=gold, force=dev["force"], gold_logit=gl, workspace=ws_sel)
+        return D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"],
+                               bs, workspace=ws_sel)
+
+    def step():
+        op_conv()
+        ids, vals, gl = op_lmhead()
+        return ids, vals, gl, op_selector(ids, vals, gl)
+
+    def timed(fn, n):
+        """Average device time of `fn` over n back-to-back calls, from events
+        recorded on the launch stream (torch's current stream)."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            out = fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n, out
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    events = [new_events() for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # headline: whole steps, events only at the two ends of the timed region
     t0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        ids, vals, res = step(events[i])
-    stop.record()
-    torch.cuda.synchronize()
+    ms_per_step, (ids, vals, gl, res) = timed(step, args.steps)
     wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(stop)
-    op_ms = {k: [e[k][0].elapsed_time(e[k][1]) for e in events] for k in OPS}
-    ms_per_step = gpu_ms / args.steps
+    gpu_ms = ms_per_step * args.steps
 
-    # teacher-forced scoring of the walk's own path (walk workloads), timed apart
+    # per-op device time (the LM-head figure feeds the roofline)
+    op_ms = {}
+    op_ms["conv"], _ = timed(op_conv, args.steps)
+    op_ms["lmhead"], _ = timed(op_lmhead, args.steps)
+    op_ms["selector"], _ = timed(lambda: op_selector(ids, vals, gl), args.steps)
+
+    # teacher-forced scoring of the walk's own path (walk workloads)
     tf_ms = None
+    replay_ok = None
     if not tf_mode:
         path = res[0]
         pred = torch.empty(N, dtype=torch.int32, device="cuda")
         pred.view(w.n_blocks, bs)[:, 1:] = path[:, :-1]
         pred.view(w.n_blocks, bs)[:, 0] = dev["anchors"]
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(3):
-            D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred, workspace=ws_tf)
-        a.record()
-        for _ in range(args.steps):
-            D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred, workspace=ws_tf)
-        b.record()
-        torch.cuda.synchronize()
-        tf_ms = a.elapsed_time(b) / args.steps
-        sc, best, _, _ = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred,
-                                             workspace=ws_tf)
+        tf = lambda: D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred,
+                                         workspace=ws_tf)
+        tf()
+        tf_ms, (sc, best, _, _) = timed(tf, args.steps)
         replay_ok = bool(torch.equal(best.view(w.n_blocks, bs)[:, 1:], path[:, 1:]))
-    else:
-        replay_ok = None
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
@@ -230,7 +222,7 @@ def main():
         torch.cuda.synchronize()
 
     lm_bytes, lm_flops = lmhead_work(w)
-    lm_ms = float(np.mean(op_ms["lmhead"]))
+    lm_ms = op_ms["lmhead"]
     mfma_bound = lm_flops / lm_bytes > (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) and w.dtype == "bf16"
     if mfma_bound:
         achieved = lm_flops / (lm_ms * 1e-3) / 1e12
@@ -260,8 +252,8 @@ def main():
         "config": {"workload": w.name, "n_blocks": w.n_blocks, "block_size": bs, "hidden": H, "vocab": V,
                    "taps": T, "group_size": gs, "rank": r, "top_k": K, "mode": w.mode},
         "roofline": roof,
-        "ops_ms": {k: float(np.mean(v)) for k, v in op_ms.items()},
-        "selector_plus_conv_over_lmhead": (float(np.mean(op_ms["conv"])) + float(np.mean(op_ms["selector"]))) / lm_ms,
+        "ops_ms": op_ms,
+        "selector_plus_conv_over_lmhead": (op_ms["conv"] + op_ms["selector"]) / lm_ms,
         "tf_ms": tf_ms,
         "tf_replays_walk": replay_ok,
         "wall_s_timed": wall,

@@ -45,7 +45,8 @@ dflash2_status check_selector(int dtype, int64_t n_rows, int32_t hidden, int32_t
     if (!dtype_ok(dtype)) return DFLASH2_ERR_DTYPE;
     if (n_rows < 1 || hidden < 1 || vocab < 1 || rank < 1) return DFLASH2_ERR_SHAPE;
     if (top_k < 1 || top_k > vocab) return DFLASH2_ERR_SHAPE;
-    if (top_k > DFLASH2_MAX_TOP_K || rank % 8 != 0 || !hidden_supported(hidden)) return DFLASH2_ERR_UNSUPPORTED;
+    if (top_k > DFLASH2_MAX_TOP_K || rank % 8 != 0 || rank > DFLASH2_MAX_RANK || !hidden_supported(hidden))
+        return DFLASH2_ERR_UNSUPPORTED;
     if (n_rows > INT_MAX) return DFLASH2_ERR_UNSUPPORTED;
     return DFLASH2_OK;
 }
@@ -157,6 +158,7 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
     dflash2_status s = check_selector(dtype, N, hidden, vocab, rank, top_k);
     if (s != DFLASH2_OK) return s;
     if (block_size > DFLASH2_MAX_BLOCK_SIZE) return DFLASH2_ERR_UNSUPPORTED;
+    if ((size_t)block_size * rank * 4 > 96 * 1024) return DFLASH2_ERR_UNSUPPORTED;  // block's context rows in LDS
     if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path || !workspace)
         return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))

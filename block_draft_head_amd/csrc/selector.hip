@@ -15,25 +15,36 @@ namespace dflash2 {
 
 // P[m][c] = sum_r B[cid_m, r] * (A[pid_c, r] * grow[r]) where lane l holds
 // candidate cid (row l % 16) and predecessor pid (column l % 16); a negative
-// id is a zero row/column.  r is a multiple of 8.  acc[i] of lane l is
-// P[4 * (l / 16) + i][l % 16].
+// id is a zero row/column.  r is a multiple of 8; grow (the context row, r
+// floats) is in LDS.  The rank index is visited 32 at a time (8 per lane
+// group), in batches of 4 whose loads are all issued before their MFMAs.
+// acc[i] of lane l is P[4 * (l / 16) + i][l % 16].
 template <typename T>
 __device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__restrict__ B,
-                                           const float *__restrict__ grow, int pid, int cid, int r) {
+                                           const float *grow, int pid, int cid, int r) {
     const int q = lane_id() >> 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int rho0 = 0; rho0 < r; rho0 += 32) {
-        const int rho = rho0 + q * 8;
-        float a[8], b[8], gg[8];
+    for (int rho0 = 0; rho0 < r; rho0 += 128) {
+        float a[4][8], b[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = b[e] = gg[e] = 0.f;
-        if (rho < r) {
-            if (pid >= 0) load8<T>(A + (size_t)pid * r + rho, a);
-            if (cid >= 0) load8<T>(B + (size_t)cid * r + rho, b);
-            load8<float>(grow + rho, gg);
+        for (int u = 0; u < 4; ++u) {
+            const int rho = rho0 + u * 32 + q * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[u][e] = b[u][e] = 0.f;
+            if (rho < r) {
+                if (pid >= 0) load8<T>(A + (size_t)pid * r + rho, a[u]);
+                if (cid >= 0) load8<T>(B + (size_t)cid * r + rho, b[u]);
+            }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mma16_f32x1(acc, b[e], a[e] * gg[e]);
+        for (int u = 0; u < 4; ++u) {
+            const int rho = rho0 + u * 32 + q * 8;
+            float gg[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gg[e] = rho < r ? grow[rho + e] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mma16_f32x1(acc, b[u][e], a[u][e] * gg[e]);
+        }
     }
     return acc;
 }
@@ -50,6 +61,7 @@ __global__ __launch_bounds__(1024) void selector_walk_kernel(
     const int32_t *__restrict__ anchors, int bs, int V, int r, int K, int32_t *__restrict__ path,
     float *__restrict__ path_score, uint32_t *__restrict__ status) {
     __shared__ uint64_t best[DFLASH2_MAX_BLOCK_SIZE * DFLASH2_MAX_TOP_K];
+    extern __shared__ __align__(16) float gblk[];  // [bs][r] context rows of this block
     const int blk = blockIdx.x;
     const int lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int q = lane >> 4, c = lane & 15;
@@ -58,6 +70,12 @@ __global__ __launch_bounds__(1024) void selector_walk_kernel(
     const int anchor = anchors[blk];
     const bool anchor_ok = anchor >= 0 && anchor < V;
     if (!anchor_ok && threadIdx.x == 0) flag_status(status, kStatusIdRange);
+    {
+        const float4 *src = reinterpret_cast<const float4 *>(g + (size_t)blk * bs * r);
+        float4 *dst = reinterpret_cast<float4 *>(gblk);
+        for (int i = threadIdx.x; i < bs * r / 4; i += blockDim.x) dst[i] = src[i];
+    }
+    __syncthreads();
 
     for (int item = wave; item < n_items; item += nwaves) {
         const int t = item == 0 ? 1 : 2 + (item - 1) / n_it;
@@ -83,7 +101,7 @@ __global__ __launch_bounds__(1024) void selector_walk_kernel(
             bool cok = j < K && cid >= 0 && cid < V;
             if (j < K && !cok) flag_status(status, kStatusIdRange);
             if (!cok) cid = -1;
-            const f32x4 P = pair_tile<T>(A, B, g + n * r, pid, cid, r);
+            const f32x4 P = pair_tile<T>(A, B, gblk + (size_t)t * r, pid, cid, r);
             uint64_t local = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -133,15 +151,19 @@ __global__ __launch_bounds__(256) void selector_tf_kernel(
     const uint8_t *__restrict__ force, const float *__restrict__ gold_logit, long long N, int V, int r,
     int K, float *__restrict__ out_scores, int32_t *__restrict__ out_best, float *__restrict__ out_ce,
     uint8_t *__restrict__ out_valid, uint32_t *__restrict__ status) {
+    extern __shared__ __align__(16) float gsm[];  // [4 waves][r]
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const long long n = (long long)blockIdx.x * 4 + wave;
     if (n >= N) return;
+    float *grow = gsm + wave * r;
+    for (int i = lane; i < r / 4; i += 64)
+        reinterpret_cast<float4 *>(grow)[i] = reinterpret_cast<const float4 *>(g + (size_t)n * r)[i];
+    wave_lds_fence();
     const int c = lane & 15;
     const int p = pred_ids[n];
     const bool p_ok = p >= 0 && p < V;
     const int pid = (c == 0 && p_ok) ? p : -1;
     const int n_jt = (K + 15) / 16;
-    const float *grow = g + (size_t)n * r;
     // lane k (< K) ends up with the score of slot k
     float s = -__builtin_inff();
     bool mine_ok = false;
@@ -208,12 +230,19 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
     const int items = bs >= 2 ? 1 + (bs - 2) * n_it : 1;
     int waves = items < 16 ? items : 16;
     const dim3 block(64 * waves);
+    const size_t lds = (size_t)bs * r * 4;
+    hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void *>(selector_walk_kernel<float>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t b = hipFuncSetAttribute(reinterpret_cast<const void *>(selector_walk_kernel<uint16_t>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (a != hipSuccess) return a;
+    if (b != hipSuccess) return b;
     if (dtype == 0)
-        hipLaunchKernelGGL(selector_walk_kernel<float>, dim3(n_blocks), block, 0, stream, g,
+        hipLaunchKernelGGL(selector_walk_kernel<float>, dim3(n_blocks), block, (size_t)bs * r * 4, stream, g,
                            (const float *)A, (const float *)B, cand_ids, cand_vals, anchors, bs, V, r,
                            K, path, path_score, status);
     else
-        hipLaunchKernelGGL(selector_walk_kernel<uint16_t>, dim3(n_blocks), block, 0, stream, g,
+        hipLaunchKernelGGL(selector_walk_kernel<uint16_t>, dim3(n_blocks), block, (size_t)bs * r * 4, stream, g,
                            (const uint16_t *)A, (const uint16_t *)B, cand_ids, cand_vals, anchors,
                            bs, V, r, K, path, path_score, status);
     return hipGetLastError();
@@ -232,12 +261,12 @@ hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, 
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((N + 3) / 4);
     if (dtype == 0)
-        hipLaunchKernelGGL(selector_tf_kernel<float>, dim3(grid), dim3(256), 0, stream, g,
+        hipLaunchKernelGGL(selector_tf_kernel<float>, dim3(grid), dim3(256), (size_t)4 * r * 4, stream, g,
                            (const float *)A, (const float *)B, cand_ids, cand_vals, pred_ids, gold_ids,
                            force, gold_logit, (long long)N, V, r, K, out_scores, out_best, out_ce,
                            out_valid, status);
     else
-        hipLaunchKernelGGL(selector_tf_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, g,
+        hipLaunchKernelGGL(selector_tf_kernel<uint16_t>, dim3(grid), dim3(256), (size_t)4 * r * 4, stream, g,
                            (const uint16_t *)A, (const uint16_t *)B, cand_ids, cand_vals, pred_ids,
                            gold_ids, force, gold_logit, (long long)N, V, r, K, out_scores, out_best,
                            out_ce, out_valid, status);

@@ -23,7 +23,7 @@ STATUS = {
 }
 OP_UNARY_TOPK, OP_SELECTOR_WALK, OP_SELECTOR_TF = 0, 1, 2
 F32, BF16 = 0, 1
-MAX_TOP_K, MAX_TAPS, MAX_BLOCK_SIZE = 64, 16, 64
+MAX_TOP_K, MAX_TAPS, MAX_BLOCK_SIZE, MAX_RANK = 64, 16, 64, 4096
 
 EXPORTS = ["dflash2_conv_prepare", "dflash2_conv_finish", "dflash2_unary_topk",
            "dflash2_selector_walk", "dflash2_selector_score_tf", "dflash2_workspace_bytes",

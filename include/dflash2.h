@@ -77,6 +77,7 @@ typedef enum {
 #define DFLASH2_MAX_TOP_K 64
 #define DFLASH2_MAX_TAPS 16
 #define DFLASH2_MAX_BLOCK_SIZE 64
+#define DFLASH2_MAX_RANK 4096     /* selector rank; the walk also needs block_size * rank <= 24576 */
 
 /*
  * Pre-sublayer half of the conv wrapper ([verl PR] "What DFlash2 adds";
@@ -152,7 +153,8 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
  * slot on an exact tie).  Every adjacent pair is scored in parallel; only the
  * final pointer chase is sequential.
  *
- *   n_blocks, block_size (<= 64), hidden H, vocab V, rank r, top_k K (<= 64)
+ *   n_blocks, block_size (<= 64), hidden H, vocab V, rank r (multiple of 8, <= 4096,
+ *   block_size * r <= 24576), top_k K (<= 64)
  *   h [N, H] dtype (N = n_blocks*bs); w_h [r, H] dtype
  *   cb_pred, cb_succ [V, r] dtype; cand_ids [N, K] int32; cand_vals [N, K] float32
  *   anchor_ids [n_blocks] int32
