@@ -52,10 +52,40 @@ def bf16_bracketed(gpu_bits: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return (g == ref) | adjacent
 
 
-def act_ok(gpu: np.ndarray, ref: np.ndarray, dtype: str) -> np.ndarray:
+def act_ok(gpu: np.ndarray, ref: np.ndarray, dtype: str, scale: np.ndarray = None) -> np.ndarray:
+    """Conv outputs.  bf16: the GPU value must be one of the two bf16 values
+    bracketing the exact one, or the round-to-nearest-even of some value within
+    delta = 2^-16 * scale of it, where scale is the magnitude of the
+    float32 terms the kernel sums (conv_term_scale).  Away from cancellation
+    delta is far below half a bf16 ulp and this is the one-ulp bracket; where
+    the taps nearly cancel, a correct float32 sum can sit a few float32 ulps
+    of the terms from the exact value and round one bf16 step further out."""
     if dtype == "f32":
         return np.abs(gpu.astype(np.float64) - ref) <= 2e-3 + 1e-3 * np.abs(ref)
-    return bf16_bracketed(gpu, ref)
+    ok = bf16_bracketed(gpu, ref)
+    if scale is None:
+        return ok
+    # the values a round-to-nearest-even of any x in [ref - d, ref + d] can take
+    d = np.ldexp(np.asarray(scale, np.float64), -16)
+    g = O.widen(gpu, "bf16")
+    lo, hi = O.widen(O.round_bf16(ref - d), "bf16"), O.widen(O.round_bf16(ref + d), "bf16")
+    return ok | ((g >= lo) & (g <= hi))
+
+
+def conv_term_scale(v, corr, base_s, block_size: int, group_size: int, dtype: str) -> np.ndarray:
+    """sum_j |base_s[j, h] + corr[n, j, h // gs]| * |v[n - j, h]| over the taps
+    inside the block: the size of the terms whose float32 sum a conv output
+    rounds.  v and base_s in storage dtype, corr float [N, T, G]."""
+    V = np.abs(O.widen(v, dtype))
+    Bs = O.widen(base_s, dtype)
+    N, H = V.shape
+    T = Bs.shape[0]
+    gh = np.arange(H) // group_size
+    out = np.zeros((N, H), np.float64)
+    for n in range(N):
+        for j in range(min(T - 1, n % block_size) + 1):
+            out[n] += np.abs(Bs[j] + np.asarray(corr, np.float64)[n, j, gh]) * V[n - j]
+    return out
 
 
 def close(gpu, ref, rtol=RTOL, atol=ATOL) -> np.ndarray:

@@ -8,7 +8,8 @@ import torch
 
 from block_draft_head_amd.inputs import Workload, make_inputs
 from oracle import dflash2_oracle as O
-from tests.helpers import (act_ok, close, compare_tf, compare_topk, compare_walk, to_dev, to_np)
+from tests.helpers import (act_ok, close, compare_tf, compare_topk, compare_walk, conv_term_scale, to_dev,
+                           to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,14 +51,15 @@ def test_conv_prepare_and_finish(D, nb, bs, H, T, gs, dtype):
         inp["w_proj"] = inp["w_proj"] * np.float32(4.0)
     xo, kp = D.conv_prepare(to_dev(inp["h"]), to_dev(inp["w_proj"]), to_dev(inp["base"]), bs, T, gs)
     xo_r, kp_r, ex = O.conv_prepare(inp["h"], inp["w_proj"], inp["base"], bs, T, gs, dtype)
-    ok = act_ok(to_np(xo), ex, dtype)
+    c_pre = O.conv_projection(inp["h"], inp["w_proj"], T, gs, dtype)[:, 0]
+    ok = act_ok(to_np(xo), ex, dtype, conv_term_scale(inp["h"], c_pre, inp["base"][0], bs, gs, dtype))
     assert ok.all(), f"{(~ok).sum()} x_out mismatches, first at {np.argwhere(~ok)[:3]}"
     assert close(to_np(kp), kp_r).all()
     # finish, fed the same float32 k_post on both sides
     kp32 = kp_r.astype(np.float32)
     yo = D.conv_finish(to_dev(inp["y"]), to_dev(kp32), to_dev(inp["base"]), bs, T, gs)
     _, ey = O.conv_finish(inp["y"], kp32, inp["base"], bs, T, gs, dtype)
-    ok = act_ok(to_np(yo), ey, dtype)
+    ok = act_ok(to_np(yo), ey, dtype, conv_term_scale(inp["y"], kp32, inp["base"][1], bs, gs, dtype))
     assert ok.all(), f"{(~ok).sum()} y_out mismatches"
 
 

@@ -1,0 +1,127 @@
+"""GPU parity at the full workload sizes, in the launch configuration that
+bench.py times (same shapes, same seeded inputs, same workspaces).
+
+The oracle cannot redo a whole full-size pass in seconds, so each stage is
+checked on what it can compute one by one:
+
+* conv prepare / finish on sampled whole anchor blocks (the conv never
+  crosses a block, so a block's rows are exact on their own);
+* unary top-K on sampled rows, each against that row's exact logits over the
+  full vocabulary (plus the gold logit on the teacher-forced workload);
+* the selector on every block / row, the oracle fed the GPU's candidate ids
+  with its own exact logits for them (stage-wise, so a top-K near-tie cannot
+  cascade).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_draft_head_amd.inputs import WORKLOAD_ORDER, WORKLOADS, make_inputs
+from oracle import dflash2_oracle as O
+from tests.helpers import (act_ok, close, compare_tf, compare_topk, compare_walk, conv_term_scale, oracle_logits_rows,
+                           to_dev, to_np)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module")
+def D():
+    from block_draft_head_amd import dflash2
+    assert torch.cuda.is_available(), "no GPU visible"
+    return dflash2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def mismatch(gpu, ref, ok, dt):
+    idx = np.argwhere(~ok)[:4]
+    return [(tuple(map(int, i)), float(O.widen(gpu[tuple(i)], dt)), float(ref[tuple(i)])) for i in idx]
+
+
+def sample(n, k, rng):
+    """First, last and k - 2 random distinct indices of range(n)."""
+    pick = {0, n - 1}
+    while len(pick) < min(k, n):
+        pick.add(int(rng.integers(0, n)))
+    return sorted(pick)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", [n for n in WORKLOAD_ORDER if not n.startswith("tiny")])
+def test_full_size_workload(D, name):
+    w = WORKLOADS[name]
+    bs, T, gs, K, r = w.block_size, w.taps, w.group_size, w.top_k, w.rank
+    N, H, V, dt = w.n_rows, w.hidden, w.vocab, w.dtype
+    tf_mode = w.mode == "tf"
+    rng = np.random.default_rng(1234)
+    log(f"[{name}] generating inputs")
+    inp = make_inputs(w)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+
+    # ---- conv, on sampled whole blocks
+    log(f"[{name}] conv")
+    x_out = torch.empty_like(dev["h"])
+    y_out = torch.empty_like(dev["y"])
+    k_post = torch.empty((N, T, H // gs), dtype=torch.float32, device="cuda")
+    D.conv_prepare(dev["h"], dev["w_proj"], dev["base"], bs, T, gs, out=x_out, k_post=k_post)
+    D.conv_finish(dev["y"], k_post, dev["base"], bs, T, gs, out=y_out)
+    blocks = sample(w.n_blocks, 4, rng)
+    rows = np.concatenate([np.arange(b * bs, (b + 1) * bs) for b in blocks])
+    xo, kp, yo = to_np(x_out[rows]), to_np(k_post[rows]), to_np(y_out[rows])
+    _, kp_r, ex = O.conv_prepare(inp["h"][rows], inp["w_proj"], inp["base"], bs, T, gs, dt)
+    c_pre = O.conv_projection(inp["h"][rows], inp["w_proj"], T, gs, dt)[:, 0]
+    ok = act_ok(xo, ex, dt, conv_term_scale(inp["h"][rows], c_pre, inp["base"][0], bs, gs, dt))
+    assert ok.all(), f"x_out: {(~ok).sum()} mismatches in blocks {blocks}: {mismatch(xo, ex, ok, dt)}"
+    assert close(kp, kp_r).all(), "k_post differs"
+    _, ey = O.conv_finish(inp["y"][rows], kp, inp["base"], bs, T, gs, dt)
+    ok = act_ok(yo, ey, dt, conv_term_scale(inp["y"][rows], kp, inp["base"][1], bs, gs, dt))
+    assert ok.all(), f"y_out: {(~ok).sum()} mismatches in blocks {blocks}: {mismatch(yo, ey, ok, dt)}"
+
+    # ---- unary top-K, on sampled rows against the exact full-vocabulary logits
+    log(f"[{name}] unary top-K")
+    ws = D.make_workspace(D.OP_UNARY_TOPK, N, H, V, 0, K, "cuda")
+    gold = dev["gold"] if tf_mode else None
+    ids, vals, gl = D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=gold, workspace=ws)
+    assert D.read_device_status(ws) == 0
+    gids, gvals = to_np(ids), to_np(vals)
+    srows = sample(N, 4, rng)
+    U = oracle_logits_rows(inp["h"][srows], inp["w_lm"], dt)
+    fails, flags, msgs = compare_topk(gids[srows], gvals[srows], U, K)
+    log(f"[{name}] top-K rows {srows}: fails {fails} flags {flags}")
+    assert fails == 0, msgs
+    if tf_mode:
+        assert close(to_np(gl)[srows], U[np.arange(len(srows)), inp["gold"][srows]]).all(), "gold logit differs"
+
+    # ---- selector, every block / row, oracle fed the GPU candidates
+    log(f"[{name}] selector")
+    u_at = O.logits_at(inp["h"], inp["w_lm"], gids, dt)
+    g64 = O.context_projection(inp["h"], inp["w_h"], dt)
+    if tf_mode:
+        gold_exact = O.logits_at(inp["h"], inp["w_lm"], inp["gold"][:, None], dt)[:, 0]
+        assert close(to_np(gl), gold_exact).all(), "gold logit differs"
+        ws_sel = D.make_workspace(D.OP_SELECTOR_TF, N, H, V, r, K, "cuda")
+        res = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"],
+                                  gold_ids=gold, force=dev["force"], gold_logit=gl, workspace=ws_sel)
+        gpu = tuple(to_np(t) for t in res)
+        ref = O.selector_score_tf(g64, inp["cb_pred"], inp["cb_succ"], gids, u_at, inp["pred"], dt,
+                                  gold_ids=inp["gold"], force=inp["force"], gold_logit=gold_exact)
+        fails, flags, msgs = compare_tf(gpu, ref, gids)
+        cov = float(np.mean(gpu[3]))
+        log(f"[{name}] TF: fails {fails} flags {flags} coverage {cov:.4f}")
+        assert fails == 0, msgs
+        # forced rows always hold gold; the rest only when it is a candidate
+        assert 0.75 < cov < 0.85
+    else:
+        ws_sel = D.make_workspace(D.OP_SELECTOR_WALK, N, H, V, r, K, "cuda")
+        path, ps = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"],
+                                   bs, workspace=ws_sel)
+        assert D.read_device_status(ws_sel) == 0
+        fails, flags, teeth, msgs = compare_walk(to_np(path), to_np(ps), g64, inp["cb_pred"], inp["cb_succ"], gids,
+                                                 u_at, inp["anchors"], bs, dt)
+        steps = w.n_blocks * (bs - 1)
+        log(f"[{name}] walk: {steps} steps, fails {fails} flags {flags} selector overrides {teeth}")
+        assert fails == 0, msgs
+        assert flags <= max(1, steps // 100)
+    torch.cuda.synchronize()

@@ -2,7 +2,8 @@
 import numpy as np
 
 from oracle import dflash2_oracle as O
-from tests.helpers import bf16_bracketed, compare_topk
+from block_draft_head_amd.inputs import WORKLOADS, make_inputs
+from tests.helpers import act_ok, bf16_bracketed, compare_topk, conv_term_scale
 
 
 def test_bf16_bracket_accepts_both_neighbours_and_nothing_else():
@@ -29,3 +30,35 @@ def test_topk_comparison_flags_near_ties_and_fails_real_errors():
     assert compare_topk(np.array([[0, 1, 3]]), np.array([[5.0, 4.0, 2.9995]]), U, 3)[:2] == (0, 1)
     assert compare_topk(np.array([[0, 1, 4]]), np.array([[5.0, 4.0, 1.0]]), U, 3)[:2] == (1, 0)
     assert compare_topk(np.array([[0, 1, 2]]), np.array([[5.0, 4.0, 3.1]]), U, 3)[:2] == (1, 0)
+
+
+def test_conv_rule_accepts_a_float32_sum_and_rejects_a_wrong_ulp():
+    """A float32 evaluation of the conv (float32 projection, float32 taps, one
+    rounding) passes the conv rule everywhere, including where the taps nearly
+    cancel; moving any output one bf16 step further from the exact value fails
+    it wherever the output is not near cancellation."""
+    w = WORKLOADS["serve_64x8_h5120_v248320"]
+    inp = make_inputs(w, fields=["h", "w_proj", "base"])
+    bs, T, gs = w.block_size, w.taps, w.group_size
+    rows = np.concatenate([np.arange(b * bs, (b + 1) * bs) for b in (0, 24, 62, 63)])
+    h = inp["h"][rows]
+    _, _, ex = O.conv_prepare(h, inp["w_proj"], inp["base"], bs, T, gs, "bf16")
+    c64 = O.conv_projection(h, inp["w_proj"], T, gs, "bf16")
+    x32 = O.widen(h, "bf16").astype(np.float32)
+    c32 = (x32 @ O.widen(inp["w_proj"], "bf16").astype(np.float32).T).reshape(c64.shape)
+    b32 = O.widen(inp["base"], "bf16").astype(np.float32)
+    gh = np.arange(w.hidden) // gs
+    f32 = np.zeros_like(x32)
+    for n in range(len(rows)):
+        for j in range(min(T - 1, n % bs) + 1):
+            f32[n] = f32[n] + (b32[0, j] + c32[n, 0, j, gh]) * x32[n - j]
+    got = O.round_bf16(f32.astype(np.float64))
+    scale = conv_term_scale(h, c64[:, 0], inp["base"][0], bs, gs, "bf16")
+    assert not bf16_bracketed(got, ex).all()  # the strict bracket alone rejects a correct float32 sum here
+    assert act_ok(got, ex, "bf16", scale).all()
+    # one step further out from the exact value, away from cancellation
+    g = O.widen(got, "bf16")
+    away = np.where((g >= ex) == (g >= 0), 1, -1)  # +1 grows the magnitude
+    worse = (got.astype(np.int64) + away).astype(np.uint16)
+    far = np.abs(ex) > np.ldexp(scale, -6)
+    assert not act_ok(worse, ex, "bf16", scale)[far & (g != ex)].any()
