@@ -174,8 +174,8 @@ def main():
         return ids, vals, gl, op_selector(ids, vals, gl)
 
     def timed(fn, n):
-        """Average device time of `fn` over n back-to-back calls, from events
-        recorded on the launch stream (torch's current stream)."""
+        """Device time of n back-to-back calls of `fn`, from events recorded on
+        the launch stream (torch's current stream) at the two ends."""
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(n):
@@ -185,7 +185,22 @@ def main():
         return a.elapsed_time(b) / n, out
 
     for _ in range(args.warmup):
-        step()
+        ids, vals, gl, res = step()
+    torch.cuda.synchronize()
+
+    # teacher-forced scoring of the walk's own path (walk workloads): the same
+    # predecessors every step, so it can ride along in the attribution pass
+    pred = None
+    if not tf_mode:
+        path = res[0]
+        pred = torch.empty(N, dtype=torch.int32, device="cuda")
+        pred.view(w.n_blocks, bs)[:, 1:] = path[:, :-1]
+        pred.view(w.n_blocks, bs)[:, 0] = dev["anchors"]
+
+    def op_tf(ids, vals):
+        return D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred,
+                                   workspace=ws_tf)
+
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
 
@@ -195,25 +210,30 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = ms_per_step * args.steps
 
-    # per-op device time (the LM-head figure feeds the roofline)
-    op_ms = {}
-    op_ms["conv"], _ = timed(op_conv, args.steps)
-    op_ms["lmhead"], _ = timed(op_lmhead, args.steps)
-    op_ms["selector"], _ = timed(lambda: op_selector(ids, vals, gl), args.steps)
-
-    # teacher-forced scoring of the walk's own path (walk workloads)
-    tf_ms = None
+    # attribution pass: the same steps with events between the ops.  The host
+    # enqueues far faster than the GPU drains a step (the LM head alone is
+    # hundreds of microseconds), so each op's events bracket its kernels as
+    # the GPU runs them back to back; the LM-head figure feeds the roofline.
+    names = ["conv", "lmhead", "selector"] + ([] if tf_mode else ["tf"])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record()
+        op_conv()
+        e[1].record()
+        i_, v_, g_ = op_lmhead()
+        e[2].record()
+        op_selector(i_, v_, g_)
+        e[3].record()
+        if not tf_mode:
+            op_tf(i_, v_)
+            e[4].record()
+    torch.cuda.synchronize()
+    op_ms = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(names)}
+    tf_ms = op_ms.pop("tf", None)
     replay_ok = None
     if not tf_mode:
-        path = res[0]
-        pred = torch.empty(N, dtype=torch.int32, device="cuda")
-        pred.view(w.n_blocks, bs)[:, 1:] = path[:, :-1]
-        pred.view(w.n_blocks, bs)[:, 0] = dev["anchors"]
-        tf = lambda: D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, pred,
-                                         workspace=ws_tf)
-        tf()
-        tf_ms, (sc, best, _, _) = timed(tf, args.steps)
-        replay_ok = bool(torch.equal(best.view(w.n_blocks, bs)[:, 1:], path[:, 1:]))
+        _, best, _, _ = op_tf(ids, vals)
+        replay_ok = bool(torch.equal(best.view(w.n_blocks, bs)[:, 1:], res[0][:, 1:]))
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
@@ -232,7 +252,8 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(w, w.name)
-    roof["kernel"] = "unary LM head + top-K (lmhead kernel + slab merge)"
+    roof["kernel"] = ("lmhead_stream_kernel + topk_merge_kernel" if N <= 8 else
+                      "lmhead_tiled_kernel + topk_merge_kernel")
     roof["algorithmic_bytes"] = lm_bytes
     roof["avg_ms"] = lm_ms
 

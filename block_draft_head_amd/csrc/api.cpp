@@ -158,7 +158,6 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
     dflash2_status s = check_selector(dtype, N, hidden, vocab, rank, top_k);
     if (s != DFLASH2_OK) return s;
     if (block_size > DFLASH2_MAX_BLOCK_SIZE) return DFLASH2_ERR_UNSUPPORTED;
-    if ((size_t)block_size * rank * 4 > 96 * 1024) return DFLASH2_ERR_UNSUPPORTED;  // block's context rows in LDS
     if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path || !workspace)
         return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))

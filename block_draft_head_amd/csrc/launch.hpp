@@ -24,6 +24,9 @@ struct LmheadPlan {
 };
 LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
 
+// LDS of one walk workgroup: the block's best-successor keys and candidate ids.
+inline size_t walk_lds_bytes(int bs, int K) { return (size_t)bs * K * (8 + 4); }
+
 hipError_t launch_conv_prepare(int dtype, int64_t N, int bs, int H, int taps, int gs, const void *x,
                                const void *w_proj, const void *base, void *x_out, float *k_post,
                                hipStream_t stream);

@@ -196,6 +196,7 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
         const uint64_t top = wave_topk<R>(k, K, myscratch);
         if (lane < K) partial[((size_t)row * gridDim.x + blockIdx.x) * K + lane] = top;
     }
+
 }
 
 // ---------------------------------------------------------------- tiled
@@ -396,8 +397,8 @@ static hipError_t set_lds(F *kernel, size_t lds) {
 
 template <typename T, int P>
 static hipError_t launch_stream(const LmheadPlan &p, int64_t M, int H, int V, int K, const void *h,
-                                const void *w, const int32_t *gold, float *gold_logit,
-                                uint64_t *partial, uint32_t *status, hipStream_t stream) {
+                                const void *w, const int32_t *gold, float *gold_logit, uint64_t *partial,
+                                uint32_t *status, hipStream_t stream) {
     auto kern = lmhead_stream_kernel<T, 8, P>;
     hipError_t e = set_lds(kern, p.lds);
     if (e != hipSuccess) return e;
@@ -413,13 +414,15 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
                              hipStream_t stream) {
     hipError_t e;
     if (p.streaming) {
+#define DF2_STREAM(PP) launch_stream<T, PP>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream)
         switch (p.prefetch) {
-            case 16: e = launch_stream<T, 16>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
-            case 8: e = launch_stream<T, 8>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
-            case 4: e = launch_stream<T, 4>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
-            case 2: e = launch_stream<T, 2>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
-            default: e = launch_stream<T, 1>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream); break;
+            case 16: e = DF2_STREAM(16); break;
+            case 8: e = DF2_STREAM(8); break;
+            case 4: e = DF2_STREAM(4); break;
+            case 2: e = DF2_STREAM(2); break;
+            default: e = DF2_STREAM(1); break;
         }
+#undef DF2_STREAM
     } else {
         auto kern = lmhead_tiled_kernel<T>;
         if ((e = set_lds(kern, p.lds)) != hipSuccess) return e;

@@ -9,78 +9,130 @@
 // predecessor in column 0 of the same routine, so replaying a walk's own
 // predecessors reproduces the walk's scores bit for bit.
 #include "common.hpp"
+#include "gemv.hpp"
 #include "launch.hpp"
 
 namespace dflash2 {
 
+// 8 codebook elements as packed 16-byte words (one for bf16, two for float32),
+// unpacked to float32 at their MFMA step.
+template <typename T> constexpr int kWords8 = (int)sizeof(T) / 2;
+__device__ __forceinline__ void unpack_words8(const uint4 (&w)[1], float (&o)[8]) { unpack16(w[0], o); }
+__device__ __forceinline__ void unpack_words8(const uint4 (&w)[2], float (&o)[8]) {
+    float a[4], b[4];
+    unpack16(w[0], a);
+    unpack16(w[1], b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = a[e], o[4 + e] = b[e];
+}
+
+// v = hi + lo + d with hi, lo bf16 and |d| < 2^-15 |v|: hi is v truncated to
+// bf16 (the float32 remainder v - hi is exact), lo that remainder truncated.
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], uint4 &hi, uint4 &lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = __float_as_uint(v[e]) & 0xffff0000u;
+        l[e] = __float_as_uint(v[e] - __uint_as_float(h[e])) & 0xffff0000u;
+    }
+    hi = make_uint4((h[0] >> 16) | h[1], (h[2] >> 16) | h[3], (h[4] >> 16) | h[5], (h[6] >> 16) | h[7]);
+    lo = make_uint4((l[0] >> 16) | l[1], (l[2] >> 16) | l[3], (l[4] >> 16) | l[5], (l[6] >> 16) | l[7]);
+}
+
 // P[m][c] = sum_r B[cid_m, r] * (A[pid_c, r] * grow[r]) where lane l holds
 // candidate cid (row l % 16) and predecessor pid (column l % 16); a negative
-// id is a zero row/column.  r is a multiple of 8; grow (the context row, r
-// floats) is in LDS.  The rank index is visited 32 at a time (8 per lane
-// group), in batches of 4 whose loads are all issued before their MFMAs.
+// id is a zero row/column.  r is a multiple of 8; grow is the context row (r
+// floats, global memory or LDS).  The rank index is visited 32 at a time (8
+// per lane group); a batch of steps (256 ranks of bf16, 128 of float32) has
+// all of its gathers and context loads issued before its MFMAs.
+//   bf16 codebooks: the B rows enter a bf16 MFMA exactly; A(a) * g is split
+//   into bf16 high and low parts (relative error below 2^-15), two 16x16x32
+//   MFMAs per step, summed in two accumulators.
+//   float32 codebooks: 16x16x4 float32 MFMAs, element e of a step feeding
+//   accumulator e % 4.
+// Every caller visits the same order, so equal inputs give bit-equal tiles.
 // acc[i] of lane l is P[4 * (l / 16) + i][l % 16].
 template <typename T>
 __device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__restrict__ B,
                                            const float *grow, int pid, int cid, int r) {
+    constexpr int S = sizeof(T) == 2 ? 8 : 4;
+    constexpr int W = kWords8<T>;
     const int q = lane_id() >> 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int rho0 = 0; rho0 < r; rho0 += 128) {
-        float a[4][8], b[4][8];
+    const T *arow = pid >= 0 ? A + (size_t)pid * r : nullptr;
+    const T *brow = cid >= 0 ? B + (size_t)cid * r : nullptr;
+    f32x4 acc[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rho0 = 0; rho0 < r; rho0 += 32 * S) {
+        uint4 ra[S][W], rb[S][W];
+        float gg[S][8];
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
             const int rho = rho0 + u * 32 + q * 8;
+            const bool in = rho < r;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[u][e] = b[u][e] = 0.f;
-            if (rho < r) {
-                if (pid >= 0) load8<T>(A + (size_t)pid * r + rho, a[u]);
-                if (cid >= 0) load8<T>(B + (size_t)cid * r + rho, b[u]);
+            for (int i = 0; i < W; ++i) {
+                ra[u][i] = (in && arow) ? reinterpret_cast<const uint4 *>(arow + rho)[i] : make_uint4(0u, 0u, 0u, 0u);
+                rb[u][i] = (in && brow) ? reinterpret_cast<const uint4 *>(brow + rho)[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+            const float4 g0 = in ? reinterpret_cast<const float4 *>(grow + rho)[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 g1 = in ? reinterpret_cast<const float4 *>(grow + rho)[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+            gg[u][0] = g0.x, gg[u][1] = g0.y, gg[u][2] = g0.z, gg[u][3] = g0.w;
+            gg[u][4] = g1.x, gg[u][5] = g1.y, gg[u][6] = g1.z, gg[u][7] = g1.w;
+        }
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            float a[8], ag[8];
+            unpack_words8(ra[u], a);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ag[e] = a[e] * gg[u][e];
+            if constexpr (sizeof(T) == 2) {
+                uint4 hi, lo;
+                split_bf16x8(ag, hi, lo);
+                mma16<uint16_t>(acc[0], rb[u][0], hi);
+                mma16<uint16_t>(acc[1], rb[u][0], lo);
+            } else {
+                float b[8];
+                unpack_words8(rb[u], b);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mma16_f32x1(acc[e & 3], b[e], ag[e]);
             }
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int rho = rho0 + u * 32 + q * 8;
-            float gg[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gg[e] = rho < r ? grow[rho + e] : 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mma16_f32x1(acc, b[u][e], a[u][e] * gg[e]);
-        }
     }
-    return acc;
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // ------------------------------------------------------------------ walk
 // One workgroup per anchor block.  Work item (t, it): position t and the
-// predecessor tile it (16 slots of C_{t-1}; at t = 1 the single anchor).
-// For each predecessor the item keeps the best successor as a key
-// (score, lowest slot on ties) in LDS; thread 0 then chases the pointers.
+// predecessor tile it (16 slots of C_{t-1}; at t = 1 the single anchor).  A
+// wave reads its item's candidate ids and context row from global memory, so
+// its gathers start at once, and keeps each predecessor's best successor as a
+// key (score, lowest slot on ties) in LDS.  Wave 0 then chases the pointers:
+// the keys of 8 positions at a time sit in its registers (lane = slot) and
+// each step is a register read-lane.
+// LDS (walk_lds_bytes): best [bs][K] u64, ids [bs][K] int.
 template <typename T>
-__global__ __launch_bounds__(1024) void selector_walk_kernel(
-    const float *__restrict__ g, const T *__restrict__ A, const T *__restrict__ B,
-    const int32_t *__restrict__ cand_ids, const float *__restrict__ cand_vals,
-    const int32_t *__restrict__ anchors, int bs, int V, int r, int K, int32_t *__restrict__ path,
-    float *__restrict__ path_score, uint32_t *__restrict__ status) {
-    __shared__ uint64_t best[DFLASH2_MAX_BLOCK_SIZE * DFLASH2_MAX_TOP_K];
-    extern __shared__ __align__(16) float gblk[];  // [bs][r] context rows of this block
-    const int blk = blockIdx.x;
+__device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *__restrict__ g, const T *__restrict__ A,
+                           const T *__restrict__ B, const int32_t *__restrict__ cand_ids,
+                           const float *__restrict__ cand_vals, const int32_t *__restrict__ anchors, int bs,
+                           int V, int r, int K, int32_t *__restrict__ path, float *__restrict__ path_score,
+                           uint32_t *__restrict__ status) {
+    uint64_t *best = reinterpret_cast<uint64_t *>(wsm);
+    int32_t *cids = reinterpret_cast<int32_t *>(best + bs * K);
     const int lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int q = lane >> 4, c = lane & 15;
     const int n_it = (K + 15) / 16, n_jt = n_it;
     const int n_items = bs >= 2 ? 1 + (bs - 2) * n_it : 0;
+    const size_t row0 = (size_t)blk * bs;
     const int anchor = anchors[blk];
     const bool anchor_ok = anchor >= 0 && anchor < V;
     if (!anchor_ok && threadIdx.x == 0) flag_status(status, kStatusIdRange);
-    {
-        const float4 *src = reinterpret_cast<const float4 *>(g + (size_t)blk * bs * r);
-        float4 *dst = reinterpret_cast<float4 *>(gblk);
-        for (int i = threadIdx.x; i < bs * r / 4; i += blockDim.x) dst[i] = src[i];
-    }
-    __syncthreads();
+    for (int i = threadIdx.x; i < bs * K; i += blockDim.x) cids[i] = cand_ids[row0 * K + i];  // for the chase
 
     for (int item = wave; item < n_items; item += nwaves) {
         const int t = item == 0 ? 1 : 2 + (item - 1) / n_it;
         const int it = item == 0 ? 0 : (item - 1) % n_it;
-        const size_t n = (size_t)blk * bs + t;
+        const size_t n = row0 + t;
         int pid = -1;
         bool col_used;
         if (t == 1) {
@@ -101,7 +153,7 @@ __global__ __launch_bounds__(1024) void selector_walk_kernel(
             bool cok = j < K && cid >= 0 && cid < V;
             if (j < K && !cok) flag_status(status, kStatusIdRange);
             if (!cok) cid = -1;
-            const f32x4 P = pair_tile<T>(A, B, gblk + (size_t)t * r, pid, cid, r);
+            const f32x4 P = pair_tile<T>(A, B, g + n * r, pid, cid, r);
             uint64_t local = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -117,28 +169,48 @@ __global__ __launch_bounds__(1024) void selector_walk_kernel(
             local = o > local ? o : local;
             bestkey = local > bestkey ? local : bestkey;
         }
-        if (q == 0 && col_used) best[t * DFLASH2_MAX_TOP_K + (t == 1 ? 0 : it * 16 + c)] = bestkey;
+        if (q == 0 && col_used) best[t * K + (t == 1 ? 0 : it * 16 + c)] = bestkey;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const size_t p0 = (size_t)blk * bs;
-        path[p0] = anchor_ok ? anchor : -1;
-        if (path_score) path_score[p0] = 0.f;
+    if (wave == 0) {
+        const size_t p0 = row0;
+        if (lane == 0) {
+            path[p0] = anchor_ok ? anchor : -1;
+            if (path_score) path_score[p0] = 0.f;
+        }
         bool alive = anchor_ok;
-        int slot = 0;
-        for (int t = 1; t < bs; ++t) {
-            const uint64_t key = alive ? best[t * DFLASH2_MAX_TOP_K + slot] : 0ull;
-            if (key == 0) {
-                alive = false;
-                path[p0 + t] = -1;
-                if (path_score) path_score[p0 + t] = __builtin_nanf("");
-                continue;
+        int slot = 0;  // wave-uniform
+        for (int t0 = 1; t0 < bs; t0 += 8) {
+            uint64_t kk[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u;
+                kk[u] = (t < bs && lane < K) ? best[t * K + lane] : 0ull;
             }
-            slot = (int)key_id(key);
-            path[p0 + t] = cand_ids[(p0 + t) * K + slot];
-            if (path_score) path_score[p0 + t] = key_val(key);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u;
+                if (t >= bs) break;
+                const uint64_t key = alive ? readlane_u64(kk[u], slot) : 0ull;
+                if (key == 0) alive = false;
+                else slot = (int)key_id(key);
+                if (lane == 0) {
+                    path[p0 + t] = alive ? cids[t * K + slot] : -1;
+                    if (path_score) path_score[p0 + t] = alive ? key_val(key) : __builtin_nanf("");
+                }
+            }
         }
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(512) void selector_walk_kernel(
+    const float *__restrict__ g, const T *__restrict__ A, const T *__restrict__ B,
+    const int32_t *__restrict__ cand_ids, const float *__restrict__ cand_vals,
+    const int32_t *__restrict__ anchors, int bs, int V, int r, int K, int32_t *__restrict__ path,
+    float *__restrict__ path_score, uint32_t *__restrict__ status) {
+    extern __shared__ __align__(16) uint8_t wsm[];
+    walk_block<T>(blockIdx.x, wsm, g, A, B, cand_ids, cand_vals, anchors, bs, V, r, K, path, path_score, status);
 }
 
 // ------------------------------------------------------------------ teacher forcing
@@ -224,13 +296,13 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
     uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
     float *g = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
     const int64_t N = (int64_t)n_blocks * bs;
+    const size_t lds = walk_lds_bytes(bs, K);
     hipError_t e = launch_context_proj(dtype, N, H, r, h, w_h, g, status, stream);
     if (e != hipSuccess) return e;
     const int n_it = (K + 15) / 16;
     const int items = bs >= 2 ? 1 + (bs - 2) * n_it : 1;
-    int waves = items < 16 ? items : 16;
+    int waves = items < 8 ? items : 8;
     const dim3 block(64 * waves);
-    const size_t lds = (size_t)bs * r * 4;
     hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void *>(selector_walk_kernel<float>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipError_t b = hipFuncSetAttribute(reinterpret_cast<const void *>(selector_walk_kernel<uint16_t>),
@@ -238,11 +310,11 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
     if (a != hipSuccess) return a;
     if (b != hipSuccess) return b;
     if (dtype == 0)
-        hipLaunchKernelGGL(selector_walk_kernel<float>, dim3(n_blocks), block, (size_t)bs * r * 4, stream, g,
+        hipLaunchKernelGGL(selector_walk_kernel<float>, dim3(n_blocks), block, lds, stream, g,
                            (const float *)A, (const float *)B, cand_ids, cand_vals, anchors, bs, V, r,
                            K, path, path_score, status);
     else
-        hipLaunchKernelGGL(selector_walk_kernel<uint16_t>, dim3(n_blocks), block, (size_t)bs * r * 4, stream, g,
+        hipLaunchKernelGGL(selector_walk_kernel<uint16_t>, dim3(n_blocks), block, lds, stream, g,
                            (const uint16_t *)A, (const uint16_t *)B, cand_ids, cand_vals, anchors,
                            bs, V, r, K, path, path_score, status);
     return hipGetLastError();

@@ -42,6 +42,9 @@
  *   is set; dflash2_read_device_status() reports it as
  *   DFLASH2_ERR_DEVICE_ID_RANGE.  The word is cleared at the start of every
  *   call that takes a workspace.
+ * - Workspaces: caller-owned device memory of at least
+ *   dflash2_workspace_bytes() bytes, any contents.  Calls that share a
+ *   workspace must not run concurrently.
  */
 #ifndef DFLASH2_H_
 #define DFLASH2_H_
@@ -77,7 +80,7 @@ typedef enum {
 #define DFLASH2_MAX_TOP_K 64
 #define DFLASH2_MAX_TAPS 16
 #define DFLASH2_MAX_BLOCK_SIZE 64
-#define DFLASH2_MAX_RANK 4096     /* selector rank; the walk also needs block_size * rank <= 24576 */
+#define DFLASH2_MAX_RANK 4096     /* selector rank */
 
 /*
  * Pre-sublayer half of the conv wrapper ([verl PR] "What DFlash2 adds";
@@ -153,8 +156,8 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
  * slot on an exact tie).  Every adjacent pair is scored in parallel; only the
  * final pointer chase is sequential.
  *
- *   n_blocks, block_size (<= 64), hidden H, vocab V, rank r (multiple of 8, <= 4096,
- *   block_size * r <= 24576), top_k K (<= 64)
+ *   n_blocks, block_size (<= 64), hidden H, vocab V, rank r (multiple of 8, <= 4096),
+ *   top_k K (<= 64)
  *   h [N, H] dtype (N = n_blocks*bs); w_h [r, H] dtype
  *   cb_pred, cb_succ [V, r] dtype; cand_ids [N, K] int32; cand_vals [N, K] float32
  *   anchor_ids [n_blocks] int32

@@ -115,7 +115,8 @@ def walk(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, ws=fake(9), wsb=None, p
 def test_selector_walk_rules():
     assert walk(k=0) == SHAPE and walk(k=1001) == SHAPE and walk(r=0) == SHAPE and walk(nb=0) == SHAPE
     assert walk(k=65) == UNSUP and walk(bs=65) == UNSUP and walk(r=12) == UNSUP and walk(h=96) == UNSUP
-    assert walk(r=4104) == UNSUP and walk(bs=64, r=512) == UNSUP  # rank limit; block context rows in LDS
+    assert walk(r=4104) == UNSUP  # rank limit
+    assert walk(bs=64, r=4096, k=64) != UNSUP
     assert walk(dtype=5) == DTYPE
     assert walk(path=None) == NULL and walk(anchors=None) == NULL and walk(ws=None) == NULL
     assert walk(wsb=100) == WS

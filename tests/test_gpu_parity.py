@@ -146,6 +146,28 @@ def test_unary_topk_is_deterministic(D):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("N,K", [(8, 16), (5, 64), (1, 1)])
+def test_reused_workspace_gives_identical_results(D, N, K):
+    """A workspace reused call after call (any contents) gives the same result."""
+    w = wl(n_blocks=1, block_size=N, hidden=512, vocab=20011, top_k=K, rank=64)
+    inp = make_inputs(w, seed=9)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    ws = D.make_workspace(D.OP_UNARY_TOPK, N, 512, 20011, 0, K, "cuda").fill_(0xA5)
+    wsw = D.make_workspace(D.OP_SELECTOR_WALK, N, 512, 20011, 64, K, "cuda").fill_(0x5A)
+    ref = None
+    for _ in range(4):
+        ids, vals, _ = D.unary_topk(dev["h"], dev["w_lm"], K, workspace=ws)
+        path, ps = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals,
+                                   dev["anchors"], N, workspace=wsw)
+        out = (ids.clone(), vals.clone(), path.clone(), ps.clone())
+        if ref is None:
+            ref = out
+        assert all(torch.equal(a, b) for a, b in zip(out, ref))
+    U = O.lm_logits(inp["h"], inp["w_lm"], "bf16")
+    fails, _, msgs = compare_topk(to_np(ref[0]), to_np(ref[1]), U, K)
+    assert fails == 0, msgs
+
+
 # ------------------------------------------------------------------ selector
 
 def rand_cands(rng, N, V, K):
