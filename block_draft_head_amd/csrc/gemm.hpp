@@ -163,4 +163,154 @@ __device__ __forceinline__ void tiled_store_c(float *ctile, const f32x4 (&acc)[C
             }
 }
 
+
+// ------------------------------------------------------------------ 256 x 256 bf16 tile
+//
+// The contraction for many rows.  256 threads, 4 waves in a 2 x 2 grid; each
+// wave owns a 128 x 128 block of the output as 4 x 4 tiles of the
+// 32 x 32 x 16 bf16 MFMA (float32 accumulators, 256 registers).  The k loop
+// walks 64-element stages: A and B rows of a stage (128 bytes each) sit in one
+// of two LDS buffers, chunk c of row r at slot c ^ ((r >> 1) & 7), so the 16
+// rows that one quarter of a wave reads for an MFMA fragment fall on 16
+// different 16-byte bank groups.  While a stage is multiplied, the next one
+// is fetched from HBM into registers and, during the stage's last k16 step,
+// written to the idle buffer; inside a stage the fragments of k16 step s + 1
+// are read from LDS between the MFMAs of step s.
+namespace big {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+constexpr int ROWB = BK * 2;                   // bytes per row per stage
+constexpr int CH = BK / 8;                     // 16-byte chunks per row per stage
+constexpr int KS = BK / 16;                    // k16 steps per stage
+constexpr int STAGE = (BM + BN) * ROWB;        // 64 KB
+constexpr int LDS_BYTES = 2 * STAGE;           // 128 KB
+constexpr int LPT = BM * CH / NT;              // chunks per thread per stage, of A and of B
+
+__device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ ((row >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// Output layout: acc[tm][tn][i] of lane l of wave (wm, wn) is
+//   C[wm*128 + tm*32 + 8*(i/4) + 4*(l/32) + i%4][wn*128 + tn*32 + l%32].
+__device__ __forceinline__ int acc_row(int wm, int tm, int i, int lane) {
+    return wm * 128 + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// acc = A[a_rows] . B[b_rows]^T over all of H (H % 64 == 0).  Row r of the A
+// (B) tile is A + a_off[r] (B + b_off[r]) elements: callers clamp rows past
+// the end to a valid row and mask those outputs.  Returns with a barrier, so
+// the caller may reuse all LDS_BYTES of `lds`.
+template <class AOff, class BOff>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *lds, const uint16_t *__restrict__ A,
+                                         const uint16_t *__restrict__ B, AOff a_off, BOff b_off, int H) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint16_t *ap[LPT], *bp[LPT];
+    int aoff[LPT], boff[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+        const int id = t + NT * i, row = id / CH, c = id % CH;
+        ap[i] = A + a_off(row) + c * 8;
+        bp[i] = B + b_off(row) + c * 8;
+        aoff[i] = swz(row, c);
+        boff[i] = BM * ROWB + swz(row, c);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+    u32x4 ra[LPT], rb[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+        ra[i] = *reinterpret_cast<const u32x4 *>(ap[i]);
+        rb[i] = *reinterpret_cast<const u32x4 *>(bp[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+        *reinterpret_cast<u32x4 *>(lds + aoff[i]) = ra[i];
+        *reinterpret_cast<u32x4 *>(lds + boff[i]) = rb[i];
+    }
+    __syncthreads();
+    const int r32 = lane & 31, hk = lane >> 5;
+    int aro[4], bro[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        aro[i] = wm * 128 + i * 32 + r32;
+        bro[i] = wn * 128 + i * 32 + r32;
+    }
+    u32x4 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fa[0][i] = *reinterpret_cast<const u32x4 *>(lds + swz(aro[i], hk));
+        fb[0][i] = *reinterpret_cast<const u32x4 *>(lds + BM * ROWB + swz(bro[i], hk));
+    }
+    const int KT = H / BK;
+    for (int kt = 0; kt < KT; ++kt) {
+        const uint8_t *st = lds + (kt & 1) * STAGE;
+        uint8_t *nx = lds + ((kt + 1) & 1) * STAGE;
+        // next stage into registers (the last iteration re-reads its own stage, in bounds)
+        const int k0 = min(kt + 1, KT - 1) * BK;
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            ra[i] = *reinterpret_cast<const u32x4 *>(ap[i] + k0);
+            rb[i] = *reinterpret_cast<const u32x4 *>(bp[i] + k0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int cur = s & 1, nxt = cur ^ 1;
+            if (s + 1 < KS) {
+                const int c = 2 * (s + 1) + hk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    fa[nxt][i] = *reinterpret_cast<const u32x4 *>(st + swz(aro[i], c));
+                    fb[nxt][i] = *reinterpret_cast<const u32x4 *>(st + BM * ROWB + swz(bro[i], c));
+                }
+            }
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32(fa[cur][tm], fb[cur][tn], acc[tm][tn]);
+            if (s + 1 < KS) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            } else {
+                // the next stage goes to the idle buffer (read by nobody since the last barrier)
+#pragma unroll
+                for (int i = 0; i < LPT; ++i) {
+                    *reinterpret_cast<u32x4 *>(nx + aoff[i]) = ra[i];
+                    *reinterpret_cast<u32x4 *>(nx + boff[i]) = rb[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 2 * LPT; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        if (kt + 1 < KT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fa[0][i] = *reinterpret_cast<const u32x4 *>(nx + swz(aro[i], hk));
+                fb[0][i] = *reinterpret_cast<const u32x4 *>(nx + BM * ROWB + swz(bro[i], hk));
+            }
+        }
+    }
+}
+
+}  // namespace big
 }  // namespace dflash2

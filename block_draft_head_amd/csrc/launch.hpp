@@ -16,7 +16,8 @@ constexpr size_t kStatusBytes = 256;
 constexpr uint32_t kStatusIdRange = 1u;
 
 struct LmheadPlan {
-    bool streaming;
+    bool streaming, big;  // big: 256 x 256 bf16 MFMA tiles (many rows)
+    int n_mt;
     int nw, prefetch, n_tiles;
     int grid_x, grid_y, n_lists;
     int merge_rows;

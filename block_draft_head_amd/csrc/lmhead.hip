@@ -270,6 +270,168 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
     }
 }
 
+// ---------------------------------------------------------------- many rows, bf16
+//
+// Workgroup (mt, slab) owns rows [256 mt, 256 mt + 256) and the 256-wide
+// vocabulary tiles of its slab; big::mainloop forms each 256 x 256 logit tile
+// in registers.  Row r's running top-K list lives in the workspace (the slab's
+// partial list) and its K-th value in LDS as the row's threshold.
+//  * Filter: a logit at or above its row's threshold becomes a candidate key
+//    in the row's LDS bucket (the stage buffers are free between tiles).
+//  * Merge: thread r inserts row r's bucket into the row's list (insertion
+//    into a register array) and raises the threshold.
+//  * The first tile of a slab, or a tile where some bucket overflows, goes
+//    through LDS instead: 128 rows at a time, each row's 256 logits and its
+//    list are reduced to the new list by one wave (wave_topk).
+// Every path keeps the exact top-K under the key order, so the result does
+// not depend on the tile order or on which path a tile took.
+constexpr int kBucket = 64;  // candidate slots per row and tile
+
+struct BigLds {
+    static constexpr int THR = big::LDS_BYTES;   // float [256]
+    static constexpr int CNT = THR + 256 * 4;     // int [256]
+    static constexpr int GCOL = CNT + 256 * 4;    // int [256]: gold id of the row, -1 if none
+    static constexpr int SCR = GCOL + 256 * 4;    // u64 [4 waves][128]
+    static constexpr int BYTES = SCR + 4 * 128 * 8;
+};
+
+// (row tile, slab) of workgroup `bid`: the workgroups of one XCD (bid % 8)
+// take a block of up to 4 row tiles x consecutive slabs, so they share the
+// A rows and B rows they stream in that XCD's L2.
+__device__ __forceinline__ void big_tile_of(int bid, int G, int n_mt, int n_slabs, int &mt, int &slab) {
+    int L = bid;
+    if (G % 8 == 0) L = (bid & 7) * (G >> 3) + (bid >> 3);
+    const int Mx = (n_mt % 4 == 0) ? 4 : (n_mt % 2 == 0) ? 2 : 1;
+    mt = (L / (Mx * n_slabs)) * Mx + L % Mx;
+    slab = (L / Mx) % n_slabs;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_big_kernel(
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K, int n_mt,
+    int n_slabs, int n_vt, const int32_t *__restrict__ gold, float *__restrict__ gold_logit,
+    uint64_t *__restrict__ partial, uint32_t *__restrict__ status) {
+    using namespace big;
+    extern __shared__ __align__(16) uint8_t smem[];
+    float *thr = reinterpret_cast<float *>(smem + BigLds::THR);
+    int *cnt = reinterpret_cast<int *>(smem + BigLds::CNT);
+    int *gcol = reinterpret_cast<int *>(smem + BigLds::GCOL);
+    uint64_t *scratch = reinterpret_cast<uint64_t *>(smem + BigLds::SCR);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+    int mt, slab;
+    big_tile_of(blockIdx.x, gridDim.x, n_mt, n_slabs, mt, slab);
+    const int m0 = mt * BM;
+    if (blockIdx.x == 0 && t == 0 && status) *status = 0u;
+    const int vt0 = (int)((long long)slab * n_vt / n_slabs), vt1 = (int)((long long)(slab + 1) * n_vt / n_slabs);
+    thr[t] = -__builtin_inff();
+    cnt[t] = 0;
+    gcol[t] = (gold && m0 + t < M) ? gold[m0 + t] : -1;
+    uint64_t *mylist = partial + ((size_t)min(m0 + t, M - 1) * n_slabs + slab) * K;  // row t's list
+    __syncthreads();
+    for (int vt = vt0; vt < vt1; ++vt) {
+        const int v0 = vt * BN;
+        f32x16 acc[4][4];
+        mainloop(acc, smem, h, w, [&](int r) { return (size_t)min(m0 + r, M - 1) * H; },
+                 [&](int r) { return (size_t)min(v0 + r, V - 1) * H; }, H);
+        const bool first = vt == vt0;
+        uint64_t *bucket = reinterpret_cast<uint64_t *>(smem);  // [256][kBucket]
+        // ---- filter (and the gold logits)
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                const int rb = acc_row(wm, tm, ib * 4, lane);  // 4 consecutive rows rb .. rb + 3
+                const float4 th = *reinterpret_cast<const float4 *>(thr + rb);
+                const int4 gc = *reinterpret_cast<const int4 *>(gcol + rb);
+                const float thv[4] = {th.x, th.y, th.z, th.w};
+                const int gcv[4] = {gc.x, gc.y, gc.z, gc.w};
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn) {
+                    const int col = v0 + wn * 128 + tn * 32 + (lane & 31);
+                    const bool colok = col < V;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const float v = acc[tm][tn][ib * 4 + ii];
+                        if (colok && gcv[ii] == col) gold_logit[m0 + rb + ii] = v;
+                        if (!first && colok && v >= thv[ii]) {
+                            const int p = atomicAdd(&cnt[rb + ii], 1);
+                            if (p < kBucket) bucket[(rb + ii) * kBucket + p] = make_key(v, (uint32_t)col);
+                        }
+                    }
+                }
+            }
+        __syncthreads();  // every candidate is counted and stored
+        if (!__syncthreads_or(first || cnt[t] > kBucket)) {
+            // ---- merge: thread t inserts row t's bucket into its list
+            const int n = cnt[t];
+            if (n > 0 && m0 + t < M) {
+                uint64_t L[KMAX];
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j) L[j] = j < K ? mylist[j] : 0ull;
+                for (int e = 0; e < n; ++e) {
+                    uint64_t x = bucket[t * kBucket + e];
+#pragma unroll
+                    for (int j = 0; j < KMAX; ++j) {
+                        if (j < K && x > L[j]) {
+                            const uint64_t y = L[j];
+                            L[j] = x;
+                            x = y;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j)
+                    if (j < K) mylist[j] = L[j];
+                uint64_t kth = 0;
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j)
+                    if (j == K - 1) kth = L[j];
+                thr[t] = kth ? key_val(kth) : -__builtin_inff();
+            }
+            cnt[t] = 0;
+        } else {
+            // ---- through LDS, 128 rows at a time (first tile of the slab, or an overflow)
+            cnt[t] = 0;
+            float *Ct = reinterpret_cast<float *>(smem);  // [128][256]
+            for (int half = 0; half < 2; ++half) {
+                if (wm == half) {
+#pragma unroll
+                    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i)
+                                Ct[(acc_row(0, tm, i, lane)) * BN + wn * 128 + tn * 32 + (lane & 31)] = acc[tm][tn][i];
+                }
+                __syncthreads();
+                for (int rr = wave; rr < 128; rr += 4) {
+                    const int row = half * 128 + rr;
+                    if (m0 + row >= M) break;
+                    uint64_t *lst = partial + ((size_t)(m0 + row) * n_slabs + slab) * K;
+                    constexpr int R = 4 + (KMAX + 63) / 64;
+                    uint64_t k[R];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = v0 + lane + 64 * q;
+                        k[q] = col < V ? make_key(Ct[rr * BN + lane + 64 * q], (uint32_t)col) : 0ull;
+                    }
+#pragma unroll
+                    for (int q = 4; q < R; ++q) {
+                        const int idx = lane + 64 * (q - 4);
+                        k[q] = (!first && idx < K) ? lst[idx] : 0ull;
+                    }
+                    const uint64_t top = wave_topk<R>(k, K, scratch + wave * 128);
+                    if (lane < K) lst[lane] = top;
+                    const uint64_t kth = readlane_u64(top, K - 1);
+                    if (lane == 0) thr[row] = kth ? key_val(kth) : -__builtin_inff();
+                }
+                __syncthreads();
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- merge
 // One workgroup of 8 waves per row.  The row's n_lists sorted lists (K keys
 // each) are cut into chunks of 512 keys; each wave reduces chunks to their
@@ -365,6 +527,17 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.n_lists = p.grid_x;
         p.lds = stream_lds;
         p.prefetch = S % 16 == 0 ? 16 : S % 8 == 0 ? 8 : S % 4 == 0 ? 4 : S % 2 == 0 ? 2 : 1;
+    } else if (dtype != 0) {
+        p.streaming = false;
+        p.big = true;
+        p.n_mt = (int)((M + big::BM - 1) / big::BM);
+        p.n_tiles = (V + big::BN - 1) / big::BN;
+        int slabs = (256 + p.n_mt - 1) / p.n_mt;
+        slabs = slabs < 1 ? 1 : slabs > p.n_tiles ? p.n_tiles : slabs;
+        p.grid_x = p.n_mt * slabs;
+        p.grid_y = 1;
+        p.n_lists = slabs;
+        p.lds = BigLds::BYTES;
     } else {
         p.streaming = false;
         const int n_mt = (int)((M + 127) / 128);
@@ -423,6 +596,17 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
             default: e = DF2_STREAM(1); break;
         }
 #undef DF2_STREAM
+    } else if (p.big) {
+        if constexpr (sizeof(T) == 2) {
+            auto kern = K <= 16 ? lmhead_big_kernel<16> : lmhead_big_kernel<64>;
+            if ((e = set_lds(kern, p.lds)) != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(big::NT), p.lds, stream, (const uint16_t *)h,
+                               (const uint16_t *)w, (int)M, H, V, K, p.n_mt, p.n_lists, p.n_tiles, gold, gold_logit,
+                               partial, status);
+            e = hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else {
         auto kern = lmhead_tiled_kernel<T>;
         if ((e = set_lds(kern, p.lds)) != hipSuccess) return e;
