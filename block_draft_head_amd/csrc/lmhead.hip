@@ -274,26 +274,25 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
 //
 // Workgroup (mt, slab) owns rows [256 mt, 256 mt + 256) and the 256-wide
 // vocabulary tiles of its slab; big::mainloop forms each 256 x 256 logit tile
-// in registers.  Row r's running top-K list lives in the workspace (the slab's
-// partial list) and its K-th value in LDS as the row's threshold.
-//  * Filter: a logit at or above its row's threshold becomes a candidate key
-//    in the row's LDS bucket (the stage buffers are free between tiles).
-//  * Merge: thread r inserts row r's bucket into the row's list (insertion
-//    into a register array) and raises the threshold.
-//  * The first tile of a slab, or a tile where some bucket overflows, goes
-//    through LDS instead: 128 rows at a time, each row's 256 logits and its
-//    list are reduced to the new list by one wave (wave_topk).
-// Every path keeps the exact top-K under the key order, so the result does
-// not depend on the tile order or on which path a tile took.
-constexpr int kBucket = 64;  // candidate slots per row and tile
-
-struct BigLds {
-    static constexpr int THR = big::LDS_BYTES;   // float [256]
-    static constexpr int CNT = THR + 256 * 4;     // int [256]
-    static constexpr int GCOL = CNT + 256 * 4;    // int [256]: gold id of the row, -1 if none
-    static constexpr int SCR = GCOL + 256 * 4;    // u64 [4 waves][128]
-    static constexpr int BYTES = SCR + 4 * 128 * 8;
-};
+// in registers.  Thread r owns row r for the whole kernel: the row's running
+// top-K list lives in the workspace (the slab's partial list) and its K-th
+// value in a register as the row's threshold.  After each tile the logits go
+// to LDS, 128 rows at a time (the accumulators are only ever stored, in
+// straight-line code), and the threads of those rows scan their own row:
+// 256 logits against the threshold, a logit at or above it inserted into the
+// row's list held in registers (no cross-lane work at all).  A row's list is
+// fetched before the scan and written back only when it changed.  Insertion
+// keeps the exact top-K under the key order, so the result does not depend
+// on the tiling.
+// Staged logits: 128 rows of 256, row stride 260 floats, so the 16 rows that
+// one quarter of a wave scans at once fall on 16 different 16-byte bank groups.
+// After them: each thread's candidate buffer.
+constexpr int kCtStride = big::BN + 4;
+constexpr int kCtBytes = 128 * kCtStride * 4;
+constexpr int kCandPerThread = 12;  // at most 4 land past the check of a 4-wide step
+constexpr int kCandBytes = 128 * (kCandPerThread + 4) * 8;  // the 128 threads scanning at once
+constexpr int kBigLds = (kCtBytes > big::LDS_BYTES ? kCtBytes : big::LDS_BYTES) + kCandBytes;
+static_assert(kBigLds <= 160 * 1024, "LM-head workgroup LDS");
 
 // (row tile, slab) of workgroup `bid`: the workgroups of one XCD (bid % 8)
 // take a block of up to 4 row tiles x consecutive slabs, so they share the
@@ -306,6 +305,19 @@ __device__ __forceinline__ void big_tile_of(int bid, int G, int n_mt, int n_slab
     slab = (L / Mx) % n_slabs;
 }
 
+
+template <int KMAX>
+__device__ __forceinline__ void list_insert(uint64_t (&L)[KMAX], uint64_t x, int K) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < K && x > L[j]) {
+            const uint64_t y = L[j];
+            L[j] = x;
+            x = y;
+        }
+    }
+}
+
 template <int KMAX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_big_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K, int n_mt,
@@ -313,122 +325,144 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint64_t *__restrict__ partial, uint32_t *__restrict__ status) {
     using namespace big;
     extern __shared__ __align__(16) uint8_t smem[];
-    float *thr = reinterpret_cast<float *>(smem + BigLds::THR);
-    int *cnt = reinterpret_cast<int *>(smem + BigLds::CNT);
-    int *gcol = reinterpret_cast<int *>(smem + BigLds::GCOL);
-    uint64_t *scratch = reinterpret_cast<uint64_t *>(smem + BigLds::SCR);
+    float *Ct = reinterpret_cast<float *>(smem);  // [128][kCtStride] staged logits (over the stage buffers)
+    uint64_t *cand = reinterpret_cast<uint64_t *>(smem + (kCtBytes > LDS_BYTES ? kCtBytes : LDS_BYTES));
+    // long lists (K > 16): per-row thresholds and wave_topk scratch over the candidate buffers
+    float *row_thr = reinterpret_cast<float *>(cand);          // [256]
+    uint64_t *wscr = cand + 128;                                // [4 waves][128]
+    if constexpr (KMAX > 16) row_thr[threadIdx.x] = -__builtin_inff();
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
     int mt, slab;
     big_tile_of(blockIdx.x, gridDim.x, n_mt, n_slabs, mt, slab);
     const int m0 = mt * BM;
     if (blockIdx.x == 0 && t == 0 && status) *status = 0u;
     const int vt0 = (int)((long long)slab * n_vt / n_slabs), vt1 = (int)((long long)(slab + 1) * n_vt / n_slabs);
-    thr[t] = -__builtin_inff();
-    cnt[t] = 0;
-    gcol[t] = (gold && m0 + t < M) ? gold[m0 + t] : -1;
-    uint64_t *mylist = partial + ((size_t)min(m0 + t, M - 1) * n_slabs + slab) * K;  // row t's list
-    __syncthreads();
+    // thread t's row: tile row t, staged in half t / 128 as staged row t % 128
+    const int my_half = t >> 7, my_rr = t & 127;
+    const bool my_ok = m0 + t < M;
+    const int my_gold = (gold && my_ok) ? gold[m0 + t] : -1;
+    uint64_t *my_list = partial + ((size_t)(my_ok ? m0 + t : 0) * n_slabs + slab) * K;
+    float my_thr = -__builtin_inff();
     for (int vt = vt0; vt < vt1; ++vt) {
         const int v0 = vt * BN;
+        const bool first = vt == vt0;
         f32x16 acc[4][4];
         mainloop(acc, smem, h, w, [&](int r) { return (size_t)min(m0 + r, M - 1) * H; },
                  [&](int r) { return (size_t)min(v0 + r, V - 1) * H; }, H);
-        const bool first = vt == vt0;
-        uint64_t *bucket = reinterpret_cast<uint64_t *>(smem);  // [256][kBucket]
-        // ---- filter (and the gold logits)
+        for (int half = 0; half < 2; ++half) {
+            if (wm == half) {
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
+                for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                const int rb = acc_row(wm, tm, ib * 4, lane);  // 4 consecutive rows rb .. rb + 3
-                const float4 th = *reinterpret_cast<const float4 *>(thr + rb);
-                const int4 gc = *reinterpret_cast<const int4 *>(gcol + rb);
-                const float thv[4] = {th.x, th.y, th.z, th.w};
-                const int gcv[4] = {gc.x, gc.y, gc.z, gc.w};
+                    for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn) {
-                    const int col = v0 + wn * 128 + tn * 32 + (lane & 31);
-                    const bool colok = col < V;
+                        for (int i = 0; i < 16; ++i)
+                            Ct[acc_row(0, tm, i, lane) * kCtStride + wn * 128 + tn * 32 + (lane & 31)] = acc[tm][tn][i];
+            }
+            __syncthreads();
+            if constexpr (KMAX > 16) {
+                // long lists: one wave per row, the list one key per lane; this
+                // wave's 32 rows 16 at a time, the batch's lists fetched together
+                for (int j0 = 0; j0 < 32; j0 += 16) {
+                    uint64_t lk[16];
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        const float v = acc[tm][tn][ib * 4 + ii];
-                        if (colok && gcv[ii] == col) gold_logit[m0 + rb + ii] = v;
-                        if (!first && colok && v >= thv[ii]) {
-                            const int p = atomicAdd(&cnt[rb + ii], 1);
-                            if (p < kBucket) bucket[(rb + ii) * kBucket + p] = make_key(v, (uint32_t)col);
+                    for (int j = 0; j < 16; ++j) {
+                        const int row = min(half * 128 + wave + 4 * (j0 + j), M - 1 - m0);
+                        lk[j] = (!first && lane < K) ? partial[((size_t)(m0 + row) * n_slabs + slab) * K + lane] : 0ull;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int rr = wave + 4 * (j0 + j), row = half * 128 + rr;
+                        if (m0 + row >= M) break;
+                        const float4 v4 = *reinterpret_cast<const float4 *>(Ct + rr * kCtStride + 4 * lane);
+                        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+                        const float th = row_thr[row];
+                        const int g = gold ? gold[m0 + row] : -1;
+                        uint64_t k[5];
+                        unsigned long long anym = 0;
+                        int npass = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int col = v0 + 4 * lane + e;
+                            if (col == g && col < V) gold_logit[m0 + row] = vv[e];
+                            const bool p = col < V && vv[e] >= th;
+                            k[e] = p ? make_key(vv[e], (uint32_t)col) : 0ull;
+                            const unsigned long long m = __ballot(p);
+                            anym |= m;
+                            npass += __popcll(m);
                         }
+                        if (!anym) continue;
+                        uint64_t top;
+                        if (npass <= 8 && !first) {  // a few candidates: insert one by one
+                            uint64_t cur = lk[j];
+                            uint64_t thk = readlane_u64(cur, K - 1);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                unsigned long long m = __ballot(k[e] > thk);
+                                while (m) {
+                                    const int src = __builtin_ctzll(m);
+                                    m &= m - 1;
+                                    const uint64_t x = readlane_u64(k[e], src);
+                                    if (x > thk) {
+                                        cur = sorted_insert(cur, x, K);
+                                        thk = readlane_u64(cur, K - 1);
+                                    }
+                                }
+                            }
+                            top = cur;
+                        } else {
+                            k[4] = lk[j];
+                            top = wave_topk<5>(k, K, wscr + wave * 128);
+                        }
+                        if (lane < K) partial[((size_t)(m0 + row) * n_slabs + slab) * K + lane] = top;
+                        const uint64_t kth = readlane_u64(top, K - 1);
+                        if (lane == 0) row_thr[row] = kth ? key_val(kth) : -__builtin_inff();
                     }
                 }
-            }
-        __syncthreads();  // every candidate is counted and stored
-        if (!__syncthreads_or(first || cnt[t] > kBucket)) {
-            // ---- merge: thread t inserts row t's bucket into its list
-            const int n = cnt[t];
-            if (n > 0 && m0 + t < M) {
+            } else if (my_half == half && my_ok) {
+                // scan the row from position q0 on; candidates go to the thread's
+                // buffer; a full buffer is merged, the threshold raised and the
+                // scan resumed where it stopped (no logit is inserted twice)
+                const float *row = Ct + my_rr * kCtStride;
+                uint64_t *buf = cand + my_rr * (kCandPerThread + 4);
+                bool loaded = false, changed = false;
                 uint64_t L[KMAX];
+                int q0 = 0;
+                while (q0 < BN / 4) {
+                    int n = 0, q = q0;
+                    for (; q < BN / 4 && n < kCandPerThread; ++q) {
+                        const float4 v4 = *reinterpret_cast<const float4 *>(row + 4 * q);
+                        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-                for (int j = 0; j < KMAX; ++j) L[j] = j < K ? mylist[j] : 0ull;
-                for (int e = 0; e < n; ++e) {
-                    uint64_t x = bucket[t * kBucket + e];
-#pragma unroll
-                    for (int j = 0; j < KMAX; ++j) {
-                        if (j < K && x > L[j]) {
-                            const uint64_t y = L[j];
-                            L[j] = x;
-                            x = y;
+                        for (int e = 0; e < 4; ++e) {
+                            const int col = v0 + 4 * q + e;
+                            if (col == my_gold && col < V) gold_logit[m0 + t] = vv[e];
+                            if (vv[e] >= my_thr && col < V) buf[n++] = make_key(vv[e], (uint32_t)col);
                         }
                     }
-                }
+                    q0 = q;
+                    if (n == 0) break;
+                    if (!loaded) {
 #pragma unroll
-                for (int j = 0; j < KMAX; ++j)
-                    if (j < K) mylist[j] = L[j];
-                uint64_t kth = 0;
-#pragma unroll
-                for (int j = 0; j < KMAX; ++j)
-                    if (j == K - 1) kth = L[j];
-                thr[t] = kth ? key_val(kth) : -__builtin_inff();
-            }
-            cnt[t] = 0;
-        } else {
-            // ---- through LDS, 128 rows at a time (first tile of the slab, or an overflow)
-            cnt[t] = 0;
-            float *Ct = reinterpret_cast<float *>(smem);  // [128][256]
-            for (int half = 0; half < 2; ++half) {
-                if (wm == half) {
-#pragma unroll
-                    for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-                        for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-                            for (int i = 0; i < 16; ++i)
-                                Ct[(acc_row(0, tm, i, lane)) * BN + wn * 128 + tn * 32 + (lane & 31)] = acc[tm][tn][i];
-                }
-                __syncthreads();
-                for (int rr = wave; rr < 128; rr += 4) {
-                    const int row = half * 128 + rr;
-                    if (m0 + row >= M) break;
-                    uint64_t *lst = partial + ((size_t)(m0 + row) * n_slabs + slab) * K;
-                    constexpr int R = 4 + (KMAX + 63) / 64;
-                    uint64_t k[R];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int col = v0 + lane + 64 * q;
-                        k[q] = col < V ? make_key(Ct[rr * BN + lane + 64 * q], (uint32_t)col) : 0ull;
+                        for (int j = 0; j < KMAX; ++j) L[j] = (!first && j < K) ? my_list[j] : 0ull;
+                        loaded = true;
                     }
+                    for (int i = 0; i < n; ++i) list_insert<KMAX>(L, buf[i], K);
+                    uint64_t kth = 0;
 #pragma unroll
-                    for (int q = 4; q < R; ++q) {
-                        const int idx = lane + 64 * (q - 4);
-                        k[q] = (!first && idx < K) ? lst[idx] : 0ull;
-                    }
-                    const uint64_t top = wave_topk<R>(k, K, scratch + wave * 128);
-                    if (lane < K) lst[lane] = top;
-                    const uint64_t kth = readlane_u64(top, K - 1);
-                    if (lane == 0) thr[row] = kth ? key_val(kth) : -__builtin_inff();
+                    for (int j = 0; j < KMAX; ++j)
+                        if (j == K - 1) kth = L[j];
+                    my_thr = kth ? key_val(kth) : -__builtin_inff();
+                    changed = true;
                 }
-                __syncthreads();
+                if (changed) {
+#pragma unroll
+                    for (int j = 0; j < KMAX; ++j)
+                        if (j < K) my_list[j] = L[j];
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -537,7 +571,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.grid_x = p.n_mt * slabs;
         p.grid_y = 1;
         p.n_lists = slabs;
-        p.lds = BigLds::BYTES;
+        p.lds = kBigLds;
     } else {
         p.streaming = false;
         const int n_mt = (int)((M + 127) / 128);
