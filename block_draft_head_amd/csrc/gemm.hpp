@@ -180,14 +180,14 @@ namespace big {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
 constexpr int ROWB = BK * 2;                   // bytes per row per stage
-constexpr int CH = BK / 8;                     // 16-byte chunks per row per stage
 constexpr int KS = BK / 16;                    // k16 steps per stage
-constexpr int STAGE = (BM + BN) * ROWB;        // 64 KB
-constexpr int LDS_BYTES = 2 * STAGE;           // 128 KB
-constexpr int LPT = BM * CH / NT;              // chunks per thread per stage, of A and of B
+constexpr int HALF = BM * ROWB;                // 32 KB: the A (or B) part of a stage
+constexpr int STAGE = 2 * HALF;                // 64 KB: A rows, then B rows
+constexpr int LW = HALF / 1024 / (NT / 64);    // 1 KB copies per wave per operand per stage (8)
 
 __device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ ((row >> 1) & 7)) << 4); }
 
@@ -202,83 +202,71 @@ __device__ __forceinline__ int acc_row(int wm, int tm, int i, int lane) {
     return wm * 128 + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
-// acc = A[a_rows] . B[b_rows]^T over all of H (H % 64 == 0).  Row r of the A
-// (B) tile is A + a_off[r] (B + b_off[r]) elements: callers clamp rows past
-// the end to a valid row and mask those outputs.  Returns with a barrier, so
-// the caller may reuse all LDS_BYTES of `lds`.
-template <class AOff, class BOff>
-__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *lds, const uint16_t *__restrict__ A,
-                                         const uint16_t *__restrict__ B, AOff a_off, BOff b_off, int H) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const uint16_t *ap[LPT], *bp[LPT];
-    int aoff[LPT], boff[LPT];
+// The operands go from global memory straight into LDS (global_load_lds_dwordx4):
+// one instruction of a wave fills 1 KB of consecutive LDS, 16 bytes per lane,
+// so each lane fetches the global chunk that the swizzled layout puts at its
+// slot.  No staging registers and no LDS write instructions.  The two stage
+// buffers must be distinct __shared__ arrays: the compiler's wait tracking
+// then sees that reading one stage does not depend on the copies still
+// filling the other, and the only wait for the copies is the one before the
+// barrier that ends each k-tile.
+struct Pipe {
+    const uint8_t *A, *B;       // first row of the A tile / B tile
+    uint32_t ao[LW], bo[LW];     // byte offset of this lane's chunk of copy j, k-slice 0
+    int wbase;                   // wave-uniform LDS offset of this wave's copies
+    int aro[4], bro[4], hk;
+
+    // Rows past a_rows (b_rows) read row a_rows - 1 (b_rows - 1); 256 * H * 2 < 2^32.
+    __device__ __forceinline__ void init(const uint16_t *A_, int a_rows, const uint16_t *B_, int b_rows, int H) {
+        const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        A = reinterpret_cast<const uint8_t *>(A_);
+        B = reinterpret_cast<const uint8_t *>(B_);
+        wbase = wave * LW * 1024;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const int id = t + NT * i, row = id / CH, c = id % CH;
-        ap[i] = A + a_off(row) + c * 8;
-        bp[i] = B + b_off(row) + c * 8;
-        aoff[i] = swz(row, c);
-        boff[i] = BM * ROWB + swz(row, c);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-    u32x4 ra[LPT], rb[LPT];
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4 *>(ap[i]);
-        rb[i] = *reinterpret_cast<const u32x4 *>(bp[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        *reinterpret_cast<u32x4 *>(lds + aoff[i]) = ra[i];
-        *reinterpret_cast<u32x4 *>(lds + boff[i]) = rb[i];
-    }
-    __syncthreads();
-    const int r32 = lane & 31, hk = lane >> 5;
-    int aro[4], bro[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        aro[i] = wm * 128 + i * 32 + r32;
-        bro[i] = wn * 128 + i * 32 + r32;
-    }
-    u32x4 fa[2][4], fb[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        fa[0][i] = *reinterpret_cast<const u32x4 *>(lds + swz(aro[i], hk));
-        fb[0][i] = *reinterpret_cast<const u32x4 *>(lds + BM * ROWB + swz(bro[i], hk));
-    }
-    const int KT = H / BK;
-    for (int kt = 0; kt < KT; ++kt) {
-        const uint8_t *st = lds + (kt & 1) * STAGE;
-        uint8_t *nx = lds + ((kt + 1) & 1) * STAGE;
-        // next stage into registers (the last iteration re-reads its own stage, in bounds)
-        const int k0 = min(kt + 1, KT - 1) * BK;
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            ra[i] = *reinterpret_cast<const u32x4 *>(ap[i] + k0);
-            rb[i] = *reinterpret_cast<const u32x4 *>(bp[i] + k0);
+        for (int j = 0; j < LW; ++j) {
+            const int row = (wave * LW + j) * 8 + (lane >> 3), c = (lane & 7) ^ ((row >> 1) & 7);
+            ao[j] = (uint32_t)min(row, a_rows - 1) * (uint32_t)H * 2u + (uint32_t)c * 16u;
+            bo[j] = (uint32_t)min(row, b_rows - 1) * (uint32_t)H * 2u + (uint32_t)c * 16u;
         }
+        const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31;
+        hk = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            aro[i] = wm * 128 + i * 32 + r32;
+            bro[i] = wn * 128 + i * 32 + r32;
+        }
+    }
+    // k-slice at byte offset k0b into stage st
+    __device__ __forceinline__ void fill(uint8_t *st, uint32_t k0b) {
+#pragma unroll
+        for (int j = 0; j < LW; ++j) {
+            __builtin_amdgcn_global_load_lds(A + (ao[j] + k0b), (lds_void *)(st + wbase + j * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(B + (bo[j] + k0b), (lds_void *)(st + HALF + wbase + j * 1024), 16, 0,
+                                             0);
+        }
+    }
+    __device__ __forceinline__ void frags(const uint8_t *st, int s, u32x4 (&fa)[4], u32x4 (&fb)[4]) const {
+        const int c = 2 * s + hk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fa[i] = *reinterpret_cast<const u32x4 *>(st + swz(aro[i], c));
+            fb[i] = *reinterpret_cast<const u32x4 *>(st + HALF + swz(bro[i], c));
+        }
+    }
+    // One k-tile from `cur` while k-slice nk fills `nxt`; the fragments of the
+    // first k16 step of `nxt` are read after the closing barrier.
+    __device__ __forceinline__ void tile(f32x16 (&acc)[4][4], const uint8_t *cur, uint8_t *nxt, uint32_t nk,
+                                         u32x4 (&fa)[2][4], u32x4 (&fb)[2][4]) {
+        fill(nxt, nk);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const int cur = s & 1, nxt = cur ^ 1;
-            if (s + 1 < KS) {
-                const int c = 2 * (s + 1) + hk;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    fa[nxt][i] = *reinterpret_cast<const u32x4 *>(st + swz(aro[i], c));
-                    fb[nxt][i] = *reinterpret_cast<const u32x4 *>(st + BM * ROWB + swz(bro[i], c));
-                }
-            }
+            const int c0 = s & 1;
+            if (s + 1 < KS) frags(cur, s + 1, fa[c0 ^ 1], fb[c0 ^ 1]);
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32(fa[cur][tm], fb[cur][tn], acc[tm][tn]);
+                for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32(fa[c0][tm], fb[c0][tn], acc[tm][tn]);
             if (s + 1 < KS) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -286,30 +274,45 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *lds, cons
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            } else {
-                // the next stage goes to the idle buffer (read by nobody since the last barrier)
-#pragma unroll
-                for (int i = 0; i < LPT; ++i) {
-                    *reinterpret_cast<u32x4 *>(nx + aoff[i]) = ra[i];
-                    *reinterpret_cast<u32x4 *>(nx + boff[i]) = rb[i];
-                }
-#pragma unroll
-                for (int i = 0; i < 2 * LPT; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
-                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies into nxt have landed
         __syncthreads();
-        if (kt + 1 < KT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                fa[0][i] = *reinterpret_cast<const u32x4 *>(nx + swz(aro[i], hk));
-                fb[0][i] = *reinterpret_cast<const u32x4 *>(nx + BM * ROWB + swz(bro[i], hk));
-            }
-        }
+        frags(nxt, 0, fa[0], fb[0]);
     }
+};
+
+// acc = A[0 .. 256) . B[0 .. 256)^T over all of H (H % 64 == 0), A and B
+// pointing at the tiles' first rows (row r at r * H elements).  st0 and st1
+// are two distinct __shared__ arrays of at least STAGE bytes.  On return every
+// copy has landed and all waves have passed a barrier after their last
+// fragment read that matters; the caller may reuse st0 and st1 after one more
+// barrier (the last fragment reads are of a spare slice and unused).
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *st0, uint8_t *st1, const uint16_t *A,
+                                         int a_rows, const uint16_t *B, int b_rows, int H) {
+    Pipe P;
+    P.init(A, a_rows, B, b_rows, H);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+    P.fill(st0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    u32x4 fa[2][4], fb[2][4];
+    P.frags(st0, 0, fa[0], fb[0]);
+    const int KT = H / BK;
+    // stage buffers alternate by name, two k-tiles per trip; a tile with no
+    // next slice re-fills its idle buffer with the last slice (in bounds, unused)
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+        P.tile(acc, st0, st1, (uint32_t)(kt + 1) * BK * 2, fa, fb);
+        P.tile(acc, st1, st0, (uint32_t)min(kt + 2, KT - 1) * BK * 2, fa, fb);
+    }
+    if (kt < KT) P.tile(acc, st0, st1, (uint32_t)(KT - 1) * BK * 2, fa, fb);
 }
 
 }  // namespace big

@@ -285,14 +285,15 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
 // keeps the exact top-K under the key order, so the result does not depend
 // on the tiling.
 // Staged logits: 128 rows of 256, row stride 260 floats, so the 16 rows that
-// one quarter of a wave scans at once fall on 16 different 16-byte bank groups.
-// After them: each thread's candidate buffer.
+// one quarter of a wave scans at once fall on 16 different 16-byte bank groups;
+// rows 0-63 over the first stage buffer, rows 64-127 over the second.  Beside
+// them: each thread's candidate buffer.
 constexpr int kCtStride = big::BN + 4;
-constexpr int kCtBytes = 128 * kCtStride * 4;
+constexpr int kCtRows = 64;  // staged rows per stage buffer
+constexpr int kStageArr = kCtRows * kCtStride * 4 > big::STAGE ? kCtRows * kCtStride * 4 : big::STAGE;
 constexpr int kCandPerThread = 12;  // at most 4 land past the check of a 4-wide step
-constexpr int kCandBytes = 128 * (kCandPerThread + 4) * 8;  // the 128 threads scanning at once
-constexpr int kBigLds = (kCtBytes > big::LDS_BYTES ? kCtBytes : big::LDS_BYTES) + kCandBytes;
-static_assert(kBigLds <= 160 * 1024, "LM-head workgroup LDS");
+constexpr int kCandKeys = 128 * (kCandPerThread + 4);  // the 128 threads scanning at once
+static_assert(2 * kStageArr + kCandKeys * 8 <= 160 * 1024, "LM-head workgroup LDS");
 
 // (row tile, slab) of workgroup `bid`: the workgroups of one XCD (bid % 8)
 // take a block of up to 4 row tiles x consecutive slabs, so they share the
@@ -324,9 +325,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int n_slabs, int n_vt, const int32_t *__restrict__ gold, float *__restrict__ gold_logit,
     uint64_t *__restrict__ partial, uint32_t *__restrict__ status) {
     using namespace big;
-    extern __shared__ __align__(16) uint8_t smem[];
-    float *Ct = reinterpret_cast<float *>(smem);  // [128][kCtStride] staged logits (over the stage buffers)
-    uint64_t *cand = reinterpret_cast<uint64_t *>(smem + (kCtBytes > LDS_BYTES ? kCtBytes : LDS_BYTES));
+    __shared__ __align__(16) uint8_t st0[kStageArr];
+    __shared__ __align__(16) uint8_t st1[kStageArr];
+    __shared__ __align__(16) uint64_t cand[kCandKeys];
+    // staged row rr (0 <= rr < 128) of the current half
+    auto ct_row = [&](int rr) -> float * {
+        return reinterpret_cast<float *>(rr < kCtRows ? st0 : st1) + (rr & (kCtRows - 1)) * kCtStride;
+    };
     // long lists (K > 16): per-row thresholds and wave_topk scratch over the candidate buffers
     float *row_thr = reinterpret_cast<float *>(cand);          // [256]
     uint64_t *wscr = cand + 128;                                // [4 waves][128]
@@ -347,17 +352,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int v0 = vt * BN;
         const bool first = vt == vt0;
         f32x16 acc[4][4];
-        mainloop(acc, smem, h, w, [&](int r) { return (size_t)min(m0 + r, M - 1) * H; },
-                 [&](int r) { return (size_t)min(v0 + r, V - 1) * H; }, H);
+        mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H);
         for (int half = 0; half < 2; ++half) {
             if (wm == half) {
 #pragma unroll
-                for (int tm = 0; tm < 4; ++tm)
+                for (int tm = 0; tm < 4; ++tm) {
+                    float *Ct = reinterpret_cast<float *>(tm < 2 ? st0 : st1);
 #pragma unroll
                     for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
                         for (int i = 0; i < 16; ++i)
-                            Ct[acc_row(0, tm, i, lane) * kCtStride + wn * 128 + tn * 32 + (lane & 31)] = acc[tm][tn][i];
+                            Ct[acc_row(0, tm & 1, i, lane) * kCtStride + wn * 128 + tn * 32 + (lane & 31)] =
+                                acc[tm][tn][i];
+                }
             }
             __syncthreads();
             if constexpr (KMAX > 16) {
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     for (int j = 0; j < 16; ++j) {
                         const int rr = wave + 4 * (j0 + j), row = half * 128 + rr;
                         if (m0 + row >= M) break;
-                        const float4 v4 = *reinterpret_cast<const float4 *>(Ct + rr * kCtStride + 4 * lane);
+                        const float4 v4 = *reinterpret_cast<const float4 *>(ct_row(rr) + 4 * lane);
                         const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
                         const float th = row_thr[row];
                         const int g = gold ? gold[m0 + row] : -1;
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 // scan the row from position q0 on; candidates go to the thread's
                 // buffer; a full buffer is merged, the threshold raised and the
                 // scan resumed where it stopped (no logit is inserted twice)
-                const float *row = Ct + my_rr * kCtStride;
+                const float *row = ct_row(my_rr);
                 uint64_t *buf = cand + my_rr * (kCandPerThread + 4);
                 bool loaded = false, changed = false;
                 uint64_t L[KMAX];
@@ -561,7 +568,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.n_lists = p.grid_x;
         p.lds = stream_lds;
         p.prefetch = S % 16 == 0 ? 16 : S % 8 == 0 ? 8 : S % 4 == 0 ? 4 : S % 2 == 0 ? 2 : 1;
-    } else if (dtype != 0) {
+    } else if (dtype != 0 && (uint64_t)big::BM * H * 2 < (1ull << 32)) {  // 32-bit offsets within a tile
         p.streaming = false;
         p.big = true;
         p.n_mt = (int)((M + big::BM - 1) / big::BM);
@@ -571,7 +578,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.grid_x = p.n_mt * slabs;
         p.grid_y = 1;
         p.n_lists = slabs;
-        p.lds = kBigLds;
+        p.lds = 0;  // static LDS only
     } else {
         p.streaming = false;
         const int n_mt = (int)((M + 127) / 128);
@@ -633,7 +640,6 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
     } else if (p.big) {
         if constexpr (sizeof(T) == 2) {
             auto kern = K <= 16 ? lmhead_big_kernel<16> : lmhead_big_kernel<64>;
-            if ((e = set_lds(kern, p.lds)) != hipSuccess) return e;
             hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(big::NT), p.lds, stream, (const uint16_t *)h,
                                (const uint16_t *)w, (int)M, H, V, K, p.n_mt, p.n_lists, p.n_tiles, gold, gold_logit,
                                partial, status);
