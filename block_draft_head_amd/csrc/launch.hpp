@@ -20,6 +20,7 @@ struct LmheadPlan {
     int n_mt;
     int nw, prefetch, n_tiles;
     int grid_x, grid_y, n_lists;
+    int list_len;  // keys per partial list (>= K; the big kernel keeps a power of two)
     int merge_rows;
     size_t lds, merge_lds, partial_bytes;
 };

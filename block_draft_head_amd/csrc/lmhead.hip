@@ -293,7 +293,10 @@ constexpr int kCtRows = 64;  // staged rows per stage buffer
 constexpr int kStageArr = kCtRows * kCtStride * 4 > big::STAGE ? kCtRows * kCtStride * 4 : big::STAGE;
 constexpr int kCandPerThread = 12;  // at most 4 land past the check of a 4-wide step
 constexpr int kCandKeys = 128 * (kCandPerThread + 4);  // the 128 threads scanning at once
-static_assert(2 * kStageArr + kCandKeys * 8 <= 160 * 1024, "LM-head workgroup LDS");
+constexpr int kRowCand = 12;                           // register scan: candidate slots per tile row
+constexpr int kCandRegion = kCandKeys > big::BM * kRowCand ? kCandKeys : big::BM * kRowCand;
+static_assert(2 * kStageArr + kCandRegion * 8 + big::BM * 8 + 8 <= 160 * 1024, "LM-head workgroup LDS");
+static_assert(4 * 1024 * 4 <= kStageArr, "register-scan scratch over one stage buffer");
 
 // (row tile, slab) of workgroup `bid`: the workgroups of one XCD (bid % 8)
 // take a block of up to 4 row tiles x consecutive slabs, so they share the
@@ -307,52 +310,144 @@ __device__ __forceinline__ void big_tile_of(int bid, int G, int n_mt, int n_slab
 }
 
 
-template <int KMAX>
-__device__ __forceinline__ void list_insert(uint64_t (&L)[KMAX], uint64_t x, int K) {
+// A row's partial list: KL keys in descending order (0 = empty slot).
+template <int KL>
+__device__ __forceinline__ void list_insert(uint64_t (&L)[KL], uint64_t x) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        if (j < K && x > L[j]) {
-            const uint64_t y = L[j];
-            L[j] = x;
-            x = y;
+    for (int j = 0; j < KL; ++j) {
+        const uint64_t y = L[j];
+        const bool gt = x > y;
+        L[j] = gt ? x : y;
+        x = gt ? y : x;
+    }
+}
+template <int KL>
+__device__ __forceinline__ void load_list(uint64_t (&L)[KL], const uint64_t *src) {
+#pragma unroll
+    for (int j = 0; j < KL; j += 2) {
+        const big::u32x4 v = *reinterpret_cast<const big::u32x4 *>(src + j);
+        L[j] = (uint64_t)v.x | ((uint64_t)v.y << 32);
+        L[j + 1] = (uint64_t)v.z | ((uint64_t)v.w << 32);
+    }
+}
+template <int KL>
+__device__ __forceinline__ void store_list(const uint64_t (&L)[KL], uint64_t *dst) {
+#pragma unroll
+    for (int j = 0; j < KL; j += 2)
+        *reinterpret_cast<big::u32x4 *>(dst + j) =
+            big::u32x4{(uint32_t)L[j], (uint32_t)(L[j] >> 32), (uint32_t)L[j + 1], (uint32_t)(L[j + 1] >> 32)};
+}
+
+// Register scan of one finished tile: each lane compares its accumulators
+// with the thresholds of their rows (kept in LDS) and appends every logit at
+// or above it to that row's LDS candidate slots.  A 16-value group with a hit
+// in any lane is first copied to the wave's LDS scratch so the lane can walk
+// its hits with a runtime index.  A row with more than kRowCand hits sets
+// the tile's overflow flag; the tile is then scanned from staged logits.
+__device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], const float *thr, uint32_t *cnt,
+                                              uint64_t *slots, uint32_t *ovf, float *scr, int v0, int V) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+    const int hl = lane >> 5;
+    bool col_ok[4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) col_ok[tn] = v0 + wn * 128 + tn * 32 + (lane & 31) < V;
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+        const int rbase = wm * 128 + tm * 32 + 4 * hl;  // rows of acc[tm][*][i]: rbase + 8 (i / 4) + i % 4
+        float th[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 t4 = *reinterpret_cast<const float4 *>(thr + rbase + 8 * g);
+            th[4 * g] = t4.x;
+            th[4 * g + 1] = t4.y;
+            th[4 * g + 2] = t4.z;
+            th[4 * g + 3] = t4.w;
+        }
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+            uint32_t hb = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) hb |= (acc[tm][tn][i] >= th[i] ? 1u : 0u) << i;
+            if (!col_ok[tn]) hb = 0;
+            if (__ballot(hb != 0)) {
+                float *sc = scr + lane * 16;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4 *>(sc + 4 * q) =
+                        make_float4(acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                                    acc[tm][tn][4 * q + 3]);
+                const uint32_t col = (uint32_t)(v0 + wn * 128 + tn * 32 + (lane & 31));
+                while (hb) {
+                    const int i = __builtin_ctz(hb);
+                    hb &= hb - 1;
+                    const int r = rbase + 8 * (i >> 2) + (i & 3);
+                    const uint32_t slot = atomicAdd(cnt + r, 1u);
+                    if (slot < (uint32_t)kRowCand) slots[r * kRowCand + slot] = make_key(sc[i], col);
+                    else *ovf = 1u;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-template <int KMAX>
+template <int KL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_big_kernel(
-    const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K, int n_mt,
-    int n_slabs, int n_vt, const int32_t *__restrict__ gold, float *__restrict__ gold_logit,
-    uint64_t *__restrict__ partial, uint32_t *__restrict__ status) {
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int n_mt,
+    int n_slabs, int n_vt, uint64_t *__restrict__ partial, uint32_t *__restrict__ status) {
     using namespace big;
     __shared__ __align__(16) uint8_t st0[kStageArr];
     __shared__ __align__(16) uint8_t st1[kStageArr];
-    __shared__ __align__(16) uint64_t cand[kCandKeys];
+    __shared__ __align__(16) uint64_t cand[kCandRegion];
+    __shared__ __align__(16) float thr[BM];  // per tile row: value of its K-th key (+inf: not a row)
+    __shared__ uint32_t cnt[BM];             // per tile row: register-scan hits this tile
+    __shared__ uint32_t ovf[2];              // per tile parity: some row overflowed its slots
     // staged row rr (0 <= rr < 128) of the current half
     auto ct_row = [&](int rr) -> float * {
         return reinterpret_cast<float *>(rr < kCtRows ? st0 : st1) + (rr & (kCtRows - 1)) * kCtStride;
     };
-    // long lists (K > 16): per-row thresholds and wave_topk scratch over the candidate buffers
-    float *row_thr = reinterpret_cast<float *>(cand);          // [256]
-    uint64_t *wscr = cand + 128;                                // [4 waves][128]
-    if constexpr (KMAX > 16) row_thr[threadIdx.x] = -__builtin_inff();
+    uint64_t *wscr = cand;  // long lists' staged scan: wave_topk scratch [4 waves][128]
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
     int mt, slab;
     big_tile_of(blockIdx.x, gridDim.x, n_mt, n_slabs, mt, slab);
     const int m0 = mt * BM;
     if (blockIdx.x == 0 && t == 0 && status) *status = 0u;
     const int vt0 = (int)((long long)slab * n_vt / n_slabs), vt1 = (int)((long long)(slab + 1) * n_vt / n_slabs);
-    // thread t's row: tile row t, staged in half t / 128 as staged row t % 128
+    // thread t owns tile row t (staged in half t / 128 as staged row t % 128)
     const int my_half = t >> 7, my_rr = t & 127;
     const bool my_ok = m0 + t < M;
-    const int my_gold = (gold && my_ok) ? gold[m0 + t] : -1;
-    uint64_t *my_list = partial + ((size_t)(my_ok ? m0 + t : 0) * n_slabs + slab) * K;
-    float my_thr = -__builtin_inff();
+    uint64_t *my_list = partial + ((size_t)(my_ok ? m0 + t : 0) * n_slabs + slab) * KL;
+    thr[t] = my_ok ? -__builtin_inff() : __builtin_inff();
+    cnt[t] = 0u;
+    if (t < 2) ovf[t] = 0u;
+    // (the mainloop's barriers order these before their first use)
     for (int vt = vt0; vt < vt1; ++vt) {
-        const int v0 = vt * BN;
-        const bool first = vt == vt0;
+        const int v0 = vt * BN, par = vt & 1;
         f32x16 acc[4][4];
         mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H);
+        bool staged = vt == vt0;  // a slab's first tile fills the lists from staged logits
+        if (!staged) {
+            // the stage buffers are idle here: the wave's scratch goes over the second one
+            register_scan(acc, thr, cnt, cand, &ovf[par], reinterpret_cast<float *>(st1) + wave * 1024,
+                                v0, V);
+            __syncthreads();
+            staged = ovf[par] != 0u;
+            if (t == 0) ovf[par ^ 1] = 0u;  // last read a tile ago; next written a tile from now
+            const uint32_t n = cnt[t];
+            cnt[t] = 0u;
+            if (!staged) {
+                // the row's hits go into its list (no accumulator is live from here on)
+                if (n) {
+                    uint64_t L[KL];
+                    load_list<KL>(L, my_list);
+                    for (uint32_t i = 0; i < n; ++i) list_insert<KL>(L, cand[t * kRowCand + i]);
+                    store_list<KL>(L, my_list);
+                    thr[t] = L[KL - 1] ? key_val(L[KL - 1]) : -__builtin_inff();
+                }
+                continue;
+            }
+            // overflow: every candidate is found again below; the slots are dropped
+        }
         for (int half = 0; half < 2; ++half) {
             if (wm == half) {
 #pragma unroll
@@ -367,15 +462,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             }
             __syncthreads();
-            if constexpr (KMAX > 16) {
+            if constexpr (KL > 16) {
                 // long lists: one wave per row, the list one key per lane; this
                 // wave's 32 rows 16 at a time, the batch's lists fetched together
+                const bool fresh = vt == vt0;
                 for (int j0 = 0; j0 < 32; j0 += 16) {
                     uint64_t lk[16];
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int row = min(half * 128 + wave + 4 * (j0 + j), M - 1 - m0);
-                        lk[j] = (!first && lane < K) ? partial[((size_t)(m0 + row) * n_slabs + slab) * K + lane] : 0ull;
+                        lk[j] = (!fresh && lane < KL) ? partial[((size_t)(m0 + row) * n_slabs + slab) * KL + lane] : 0ull;
                     }
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
@@ -383,15 +479,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         if (m0 + row >= M) break;
                         const float4 v4 = *reinterpret_cast<const float4 *>(ct_row(rr) + 4 * lane);
                         const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-                        const float th = row_thr[row];
-                        const int g = gold ? gold[m0 + row] : -1;
+                        const float th = thr[row];
                         uint64_t k[5];
                         unsigned long long anym = 0;
                         int npass = 0;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int col = v0 + 4 * lane + e;
-                            if (col == g && col < V) gold_logit[m0 + row] = vv[e];
                             const bool p = col < V && vv[e] >= th;
                             k[e] = p ? make_key(vv[e], (uint32_t)col) : 0ull;
                             const unsigned long long m = __ballot(p);
@@ -400,9 +494,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         }
                         if (!anym) continue;
                         uint64_t top;
-                        if (npass <= 8 && !first) {  // a few candidates: insert one by one
+                        if (npass <= 8 && !fresh) {  // a few candidates: insert one by one
                             uint64_t cur = lk[j];
-                            uint64_t thk = readlane_u64(cur, K - 1);
+                            uint64_t thk = readlane_u64(cur, KL - 1);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 unsigned long long m = __ballot(k[e] > thk);
@@ -411,19 +505,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                     m &= m - 1;
                                     const uint64_t x = readlane_u64(k[e], src);
                                     if (x > thk) {
-                                        cur = sorted_insert(cur, x, K);
-                                        thk = readlane_u64(cur, K - 1);
+                                        cur = sorted_insert(cur, x, KL);
+                                        thk = readlane_u64(cur, KL - 1);
                                     }
                                 }
                             }
                             top = cur;
                         } else {
                             k[4] = lk[j];
-                            top = wave_topk<5>(k, K, wscr + wave * 128);
+                            top = wave_topk<5>(k, KL, wscr + wave * 128);
                         }
-                        if (lane < K) partial[((size_t)(m0 + row) * n_slabs + slab) * K + lane] = top;
-                        const uint64_t kth = readlane_u64(top, K - 1);
-                        if (lane == 0) row_thr[row] = kth ? key_val(kth) : -__builtin_inff();
+                        if (lane < KL) partial[((size_t)(m0 + row) * n_slabs + slab) * KL + lane] = top;
+                        const uint64_t kth = readlane_u64(top, KL - 1);
+                        if (lane == 0) thr[row] = kth ? key_val(kth) : -__builtin_inff();
                     }
                 }
             } else if (my_half == half && my_ok) {
@@ -432,8 +526,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 // scan resumed where it stopped (no logit is inserted twice)
                 const float *row = ct_row(my_rr);
                 uint64_t *buf = cand + my_rr * (kCandPerThread + 4);
+                const bool fresh = vt == vt0;
+                float my_thr = thr[t];
                 bool loaded = false, changed = false;
-                uint64_t L[KMAX];
+                uint64_t L[KL];
                 int q0 = 0;
                 while (q0 < BN / 4) {
                     int n = 0, q = q0;
@@ -443,29 +539,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int col = v0 + 4 * q + e;
-                            if (col == my_gold && col < V) gold_logit[m0 + t] = vv[e];
                             if (vv[e] >= my_thr && col < V) buf[n++] = make_key(vv[e], (uint32_t)col);
                         }
                     }
                     q0 = q;
                     if (n == 0) break;
                     if (!loaded) {
+                        if (fresh) {
 #pragma unroll
-                        for (int j = 0; j < KMAX; ++j) L[j] = (!first && j < K) ? my_list[j] : 0ull;
+                            for (int j = 0; j < KL; ++j) L[j] = 0ull;
+                        } else {
+                            load_list<KL>(L, my_list);
+                        }
                         loaded = true;
                     }
-                    for (int i = 0; i < n; ++i) list_insert<KMAX>(L, buf[i], K);
-                    uint64_t kth = 0;
-#pragma unroll
-                    for (int j = 0; j < KMAX; ++j)
-                        if (j == K - 1) kth = L[j];
-                    my_thr = kth ? key_val(kth) : -__builtin_inff();
+                    for (int i = 0; i < n; ++i) list_insert<KL>(L, buf[i]);
+                    my_thr = L[KL - 1] ? key_val(L[KL - 1]) : -__builtin_inff();
                     changed = true;
                 }
                 if (changed) {
-#pragma unroll
-                    for (int j = 0; j < KMAX; ++j)
-                        if (j < K) my_list[j] = L[j];
+                    store_list<KL>(L, my_list);
+                    thr[t] = my_thr;
                 }
             }
             __syncthreads();
@@ -511,19 +605,24 @@ __device__ __forceinline__ void merge_stage(const uint64_t *src, int n, int K, u
     }
 }
 
+// After the merge, a kernel whose tiles do not see the gold column (gold_h
+// set) has the workgroup form the gold logit as a float32 dot product.
+template <typename T>
 __global__ __launch_bounds__(512) void topk_merge_kernel(const uint64_t *__restrict__ partial, int M,
-                                                         int n_lists, int K, int V,
+                                                         int n_keys, int K, int V,
                                                          int32_t *__restrict__ out_ids,
                                                          float *__restrict__ out_vals,
                                                          const int32_t *__restrict__ gold,
                                                          float *__restrict__ gold_logit,
-                                                         uint32_t *__restrict__ status, int lds_keys) {
+                                                         uint32_t *__restrict__ status, int lds_keys,
+                                                         const T *__restrict__ gold_h, const T *__restrict__ gold_w,
+                                                         int H) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint64_t *bufA = reinterpret_cast<uint64_t *>(smem);
     uint64_t *bufB = bufA + lds_keys;
     uint64_t *scratch = bufB + lds_keys;  // 8 waves x 128 keys
     const int row = blockIdx.x;
-    int n = n_lists * K;
+    int n = n_keys;  // the row's partial lists, back to back
     const uint64_t *src = partial + (size_t)row * n;
     uint64_t *dst = bufA;
     int32_t *oi = out_ids + (size_t)row * K;
@@ -537,19 +636,40 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const uint64_t *__restr
         src = dst;
         dst = dst == bufA ? bufB : bufA;
     }
-    if (gold && threadIdx.x == 0) {
-        const int g = gold[row];
-        if (g < 0 || g >= V) {
-            gold_logit[row] = __builtin_nanf("");
-            flag_status(status, kStatusIdRange);
+    if (!gold) return;
+    const int g = gold[row];
+    const bool g_ok = g >= 0 && g < V;
+    if (gold_h && g_ok) {
+        __syncthreads();  // scratch is free again
+        const T *x = gold_h + (size_t)row * H, *y = gold_w + (size_t)g * H;
+        float acc = 0.f;
+        for (int c = threadIdx.x; c < H / 8; c += blockDim.x) {
+            float a[8], b[8];
+            load8<T>(x + c * 8, a);
+            load8<T>(y + c * 8, b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf(a[e], b[e], acc);
         }
+        acc = wave_sum_f32(acc);
+        float *part = reinterpret_cast<float *>(scratch);
+        if (lane_id() == 0) part[threadIdx.x >> 6] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float sum = 0.f;
+            for (int i = 0; i < (int)(blockDim.x >> 6); ++i) sum += part[i];
+            gold_logit[row] = sum;
+        }
+    }
+    if (!g_ok && threadIdx.x == 0) {
+        gold_logit[row] = __builtin_nanf("");
+        flag_status(status, kStatusIdRange);
     }
 }
 
 // ---------------------------------------------------------------- host side
 
-static int first_stage_keys(int n_lists, int K) {
-    return (n_lists * K + kMergeChunk - 1) / kMergeChunk * K;
+static int first_stage_keys(int n_keys, int K) {
+    return (n_keys + kMergeChunk - 1) / kMergeChunk * K;
 }
 
 LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
@@ -579,6 +699,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.grid_y = 1;
         p.n_lists = slabs;
         p.lds = 0;  // static LDS only
+        p.list_len = K <= 8 ? 8 : K <= 16 ? 16 : K <= 32 ? 32 : 64;
     } else {
         p.streaming = false;
         const int n_mt = (int)((M + 127) / 128);
@@ -596,10 +717,11 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.lds = (stage > ctile ? stage : ctile) + (size_t)128 * K * 8;
     }
     // merge: LDS for the first reduction stage's survivors (later stages are smaller)
-    const int first = first_stage_keys(p.n_lists, K);
+    if (!p.big) p.list_len = K;
+    const int first = first_stage_keys(p.n_lists * p.list_len, K);
     p.merge_rows = 1;
     p.merge_lds = (size_t)2 * first * 8 + 8 * 128 * 8;
-    p.partial_bytes = (size_t)M * p.n_lists * K * 8;
+    p.partial_bytes = (size_t)M * p.n_lists * p.list_len * 8;
     return p;
 }
 
@@ -639,10 +761,12 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
 #undef DF2_STREAM
     } else if (p.big) {
         if constexpr (sizeof(T) == 2) {
-            auto kern = K <= 16 ? lmhead_big_kernel<16> : lmhead_big_kernel<64>;
+            auto kern = p.list_len == 8    ? lmhead_big_kernel<8>
+                        : p.list_len == 16 ? lmhead_big_kernel<16>
+                        : p.list_len == 32 ? lmhead_big_kernel<32>
+                                           : lmhead_big_kernel<64>;
             hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(big::NT), p.lds, stream, (const uint16_t *)h,
-                               (const uint16_t *)w, (int)M, H, V, K, p.n_mt, p.n_lists, p.n_tiles, gold, gold_logit,
-                               partial, status);
+                               (const uint16_t *)w, (int)M, H, V, p.n_mt, p.n_lists, p.n_tiles, partial, status);
             e = hipGetLastError();
         } else {
             return hipErrorInvalidValue;
@@ -656,10 +780,12 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    if ((e = set_lds(topk_merge_kernel, p.merge_lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)M), dim3(512), p.merge_lds, stream, partial, (int)M,
-                       p.n_lists, K, V, out_ids, out_vals, gold, gold_logit, status,
-                       first_stage_keys(p.n_lists, K));
+    auto merge = topk_merge_kernel<T>;
+    if ((e = set_lds(merge, p.merge_lds)) != hipSuccess) return e;
+    const int n_keys = p.n_lists * p.list_len;
+    hipLaunchKernelGGL(merge, dim3((unsigned)M), dim3(512), p.merge_lds, stream, partial, (int)M, n_keys, K, V,
+                       out_ids, out_vals, gold, gold_logit, status, first_stage_keys(n_keys, K),
+                       p.big ? (const T *)h : nullptr, p.big ? (const T *)w : nullptr, H);
     return hipGetLastError();
 }
 
