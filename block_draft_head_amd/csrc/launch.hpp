@@ -23,6 +23,7 @@ struct LmheadPlan {
     int list_len;  // keys per partial list (>= K; the big kernel keeps a power of two)
     int merge_rows;
     size_t lds, merge_lds, partial_bytes;
+    size_t tiles_offset;  // big: byte offset of the exact-path tile buffers after the partial lists
 };
 LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
 

@@ -274,29 +274,27 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
 //
 // Workgroup (mt, slab) owns rows [256 mt, 256 mt + 256) and the 256-wide
 // vocabulary tiles of its slab; big::mainloop forms each 256 x 256 logit tile
-// in registers.  Thread r owns row r for the whole kernel: the row's running
-// top-K list lives in the workspace (the slab's partial list) and its K-th
-// value in a register as the row's threshold.  After each tile the logits go
-// to LDS, 128 rows at a time (the accumulators are only ever stored, in
-// straight-line code), and the threads of those rows scan their own row:
-// 256 logits against the threshold, a logit at or above it inserted into the
-// row's list held in registers (no cross-lane work at all).  A row's list is
-// fetched before the scan and written back only when it changed.  Insertion
-// keeps the exact top-K under the key order, so the result does not depend
-// on the tiling.
-// Staged logits: 128 rows of 256, row stride 260 floats, so the 16 rows that
-// one quarter of a wave scans at once fall on 16 different 16-byte bank groups;
-// rows 0-63 over the first stage buffer, rows 64-127 over the second.  Beside
-// them: each thread's candidate buffer.
-constexpr int kCtStride = big::BN + 4;
-constexpr int kCtRows = 64;  // staged rows per stage buffer
-constexpr int kStageArr = kCtRows * kCtStride * 4 > big::STAGE ? kCtRows * kCtStride * 4 : big::STAGE;
-constexpr int kCandPerThread = 12;  // at most 4 land past the check of a 4-wide step
-constexpr int kCandKeys = 128 * (kCandPerThread + 4);  // the 128 threads scanning at once
-constexpr int kRowCand = 12;                           // register scan: candidate slots per tile row
-constexpr int kCandRegion = kCandKeys > big::BM * kRowCand ? kCandKeys : big::BM * kRowCand;
-static_assert(2 * kStageArr + kCandRegion * 8 + big::BM * 8 + 8 <= 160 * 1024, "LM-head workgroup LDS");
-static_assert(4 * 1024 * 4 <= kStageArr, "register-scan scratch over one stage buffer");
+// in the accumulators.  Thread r owns tile row r: the row's running top-KL
+// list (KL = K rounded up to a power of two; keeping more than K keys per
+// list never changes the merged top K) lives in the workspace as the slab's
+// partial list, the value of its KL-th key in LDS as the row's threshold.
+//
+// After a tile, every lane compares its accumulators with their rows'
+// thresholds and appends each logit at or above one to that row's LDS slots;
+// the owners then insert their slots into their lists and raise their
+// thresholds.  A slab's first tile (no thresholds yet), and a tile in which
+// some row's hits overflow its slots, take the exact path instead: the tile's
+// logits go to a per-workgroup buffer in the workspace and each owner scans
+// its whole row there.  Insertion keeps the exact top-KL under the key order,
+// so the result does not depend on the tiling or on which path a tile took.
+constexpr int kRowCand = 14;        // candidate slots per tile row
+constexpr int kScrStride = 68;      // register scan: a lane's 64 values in LDS, padded against bank conflicts
+constexpr int kCandPerThread = 8;   // exact path: buffer merged past this many (16 more land per step)
+constexpr int kCandStride = kCandPerThread + 16;
+constexpr size_t kBigTileFloats = (size_t)big::BM * big::BN;  // exact path buffer per workgroup
+static_assert(2 * big::STAGE + big::BM * kRowCand * 8 + big::BM * 8 + 8 <= 160 * 1024, "LM-head workgroup LDS");
+static_assert(big::NT * kScrStride * 4 <= 2 * big::STAGE, "register-scan scratch over the stage buffers");
+static_assert(big::NT * kCandStride * 8 <= big::STAGE, "exact-path buffers over one stage buffer");
 
 // (row tile, slab) of workgroup `bid`: the workgroups of one XCD (bid % 8)
 // take a block of up to 4 row tiles x consecutive slabs, so they share the
@@ -308,7 +306,6 @@ __device__ __forceinline__ void big_tile_of(int bid, int G, int n_mt, int n_slab
     mt = (L / (Mx * n_slabs)) * Mx + L % Mx;
     slab = (L / Mx) % n_slabs;
 }
-
 
 // A row's partial list: KL keys in descending order (0 = empty slot).
 template <int KL>
@@ -338,19 +335,42 @@ __device__ __forceinline__ void store_list(const uint64_t (&L)[KL], uint64_t *ds
             big::u32x4{(uint32_t)L[j], (uint32_t)(L[j] >> 32), (uint32_t)L[j + 1], (uint32_t)(L[j + 1] >> 32)};
 }
 
-// Register scan of one finished tile: each lane compares its accumulators
-// with the thresholds of their rows (kept in LDS) and appends every logit at
-// or above it to that row's LDS candidate slots.  A 16-value group with a hit
-// in any lane is first copied to the wave's LDS scratch so the lane can walk
-// its hits with a runtime index.  A row with more than kRowCand hits sets
-// the tile's overflow flag; the tile is then scanned from staged logits.
+// The accumulators stay in AGPRs: every use outside the MFMAs goes through
+// these, whose operands are AGPRs (left to itself the compiler moves all 256
+// to VGPRs for the compares and spills everything else).
+__device__ __forceinline__ float agpr_read(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ void agpr_store_global(float *p, float a) {
+    asm volatile("global_store_dword %0, %1, off offset:%2" ::"v"(p), "a"(a), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void agpr_store_lds4(float *p, f32x4 a) {
+    asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"((uint32_t)(size_t)(__attribute__((address_space(3))) float *)p),
+                 "a"(a), "i"(OFF)
+                 : "memory");
+}
+
+// Register scan of one finished tile (every column real).  For each of its
+// four 32-row groups a lane forms, in vector registers only, the mask of its
+// 64 accumulators at or above their rows' thresholds (kept in LDS).  A group
+// with a hit in any lane is copied to the wave's LDS scratch, and each lane
+// walks its own hits: value by index from the scratch, a slot of the row
+// claimed with an LDS atomic (a row's hits come from two waves), the key
+// written there.  A row with more than kRowCand hits sets *ovf.
 __device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], const float *thr, uint32_t *cnt,
-                                              uint64_t *slots, uint32_t *ovf, float *scr, int v0, int V) {
+                                              uint64_t *slots, uint32_t *ovf, float *scr, int v0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-    const int hl = lane >> 5;
-    bool col_ok[4];
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) col_ok[tn] = v0 + wn * 128 + tn * 32 + (lane & 31) < V;
+    // an opaque zero: the addresses below are formed where they are used
+    // instead of being hoisted out of the tile loop (and spilled)
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    const int hl = (lane >> 5) + zero;
+    const uint32_t col0 = (uint32_t)(v0 + wn * 128 + (lane & 31));
+    float *sc = scr + (wave * 64 + lane) * kScrStride;  // the lane's 64 values
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
         const int rbase = wm * 128 + tm * 32 + 4 * hl;  // rows of acc[tm][*][i]: rbase + 8 (i / 4) + i % 4
@@ -363,207 +383,206 @@ __device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], co
             th[4 * g + 2] = t4.z;
             th[4 * g + 3] = t4.w;
         }
+        uint64_t bits = 0;  // bit 16 tn + i: acc[tm][tn][i] is a hit
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
             uint32_t hb = 0;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) hb |= (acc[tm][tn][i] >= th[i] ? 1u : 0u) << i;
-            if (!col_ok[tn]) hb = 0;
-            if (__ballot(hb != 0)) {
-                float *sc = scr + lane * 16;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<float4 *>(sc + 4 * q) =
-                        make_float4(acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
-                                    acc[tm][tn][4 * q + 3]);
-                const uint32_t col = (uint32_t)(v0 + wn * 128 + tn * 32 + (lane & 31));
-                while (hb) {
-                    const int i = __builtin_ctz(hb);
-                    hb &= hb - 1;
-                    const int r = rbase + 8 * (i >> 2) + (i & 3);
-                    const uint32_t slot = atomicAdd(cnt + r, 1u);
-                    if (slot < (uint32_t)kRowCand) slots[r * kRowCand + slot] = make_key(sc[i], col);
-                    else *ovf = 1u;
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 16; ++i) hb |= agpr_read(acc[tm][tn][i]) >= th[i] ? (1u << i) : 0u;
+            bits |= (uint64_t)hb << (16 * tn);
         }
+        if (__ballot(bits != 0)) {
+#define DF2_SCR(TN, Q)                                                                                        \
+    agpr_store_lds4<(16 * TN + 4 * Q) * 4>(                                                                   \
+        sc, __builtin_shufflevector(acc[tm][TN], acc[tm][TN], 4 * Q, 4 * Q + 1, 4 * Q + 2, 4 * Q + 3))
+            DF2_SCR(0, 0); DF2_SCR(0, 1); DF2_SCR(0, 2); DF2_SCR(0, 3);
+            DF2_SCR(1, 0); DF2_SCR(1, 1); DF2_SCR(1, 2); DF2_SCR(1, 3);
+            DF2_SCR(2, 0); DF2_SCR(2, 1); DF2_SCR(2, 2); DF2_SCR(2, 3);
+            DF2_SCR(3, 0); DF2_SCR(3, 1); DF2_SCR(3, 2); DF2_SCR(3, 3);
+#undef DF2_SCR
+            while (bits) {
+                const int j = __builtin_ctzll(bits);
+                bits &= bits - 1;
+                const int tn = j >> 4, i = j & 15;
+                const int r = rbase + 8 * (i >> 2) + (i & 3);
+                const uint32_t sl = atomicAdd(cnt + r, 1u);
+                if (sl < (uint32_t)kRowCand) slots[r * kRowCand + sl] = make_key(sc[j], col0 + 32 * tn);
+                else *ovf = 1u;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Exact path, one owner thread per row over the tile's logits in `row`
+// (256 floats, nvalid of them real columns).  Pass 1: a lower bound of the
+// row's KL-th largest logit in the tile, the KL-th largest of the maxima of
+// its 64 runs of 4 (KL distinct logits reach it), by a branch-free max / min
+// network.  Pass 2: logits at or above max(threshold, bound) go to the
+// thread's LDS buffer, 16 at a time; a buffer past kCandPerThread is merged
+// into the list and the threshold raised.
+// (Not inlined: it runs on rare tiles, and inlined its registers would crowd
+// the accumulators of the common path.)
+template <int KL>
+__device__ __attribute__((noinline)) void exact_row_scan(const float *__restrict__ row, int nvalid, int v0,
+                                                         bool fresh, uint64_t *list, float *thr_out, uint64_t *buf) {
+    const float4 *row4 = reinterpret_cast<const float4 *>(row);
+    float top[KL];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) top[j] = -__builtin_inff();
+    for (int q0 = 0; q0 < big::BN / 4; q0 += 8) {
+        float4 v4[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v4[u] = row4[q0 + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = 4 * (q0 + u);
+            float m = fmaxf(fmaxf(v4[u].x, c + 1 < nvalid ? v4[u].y : -__builtin_inff()),
+                            fmaxf(c + 2 < nvalid ? v4[u].z : -__builtin_inff(),
+                                  c + 3 < nvalid ? v4[u].w : -__builtin_inff()));
+            if (c >= nvalid) m = -__builtin_inff();
+#pragma unroll
+            for (int j = 0; j < KL; ++j) {
+                const float hi = fmaxf(top[j], m);
+                m = fminf(top[j], m);
+                top[j] = hi;
+            }
+        }
+    }
+    float th = fmaxf(*thr_out, top[KL - 1]);
+    bool loaded = false, changed = false;
+    uint64_t L[KL];
+    int n = 0;
+    auto flush = [&]() {
+        if (!loaded) {
+            if (fresh) {
+#pragma unroll
+                for (int j = 0; j < KL; ++j) L[j] = 0ull;
+            } else {
+                load_list<KL>(L, list);
+            }
+            loaded = true;
+        }
+        for (int i = 0; i < n; ++i) list_insert<KL>(L, buf[i]);
+        if (L[KL - 1]) th = fmaxf(th, key_val(L[KL - 1]));
+        changed = true;
+        n = 0;
+    };
+    for (int q0 = 0; q0 < big::BN / 4; q0 += 4) {
+        float4 v4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v4[u] = row4[q0 + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float vv[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 4 * (q0 + u) + e;
+                if (vv[e] >= th && c < nvalid) buf[n++] = make_key(vv[e], (uint32_t)(v0 + c));
+            }
+        }
+        if (n > kCandPerThread) flush();
+    }
+    if (n) flush();
+    if (changed) {
+        store_list<KL>(L, list);
+        *thr_out = th;
     }
 }
 
 template <int KL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_big_kernel(
-    const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int n_mt,
-    int n_slabs, int n_vt, uint64_t *__restrict__ partial, uint32_t *__restrict__ status) {
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int n_mt, int n_slabs,
+    int n_vt, uint64_t *__restrict__ partial, float *__restrict__ tiles, uint32_t *__restrict__ status) {
     using namespace big;
-    __shared__ __align__(16) uint8_t st0[kStageArr];
-    __shared__ __align__(16) uint8_t st1[kStageArr];
-    __shared__ __align__(16) uint64_t cand[kCandRegion];
-    __shared__ __align__(16) float thr[BM];  // per tile row: value of its K-th key (+inf: not a row)
+    __shared__ __align__(16) uint8_t st0[STAGE];
+    __shared__ __align__(16) uint8_t st1[STAGE];
+    __shared__ __align__(16) uint64_t slots[BM * kRowCand];
+    __shared__ __align__(16) float thr[BM];  // per tile row: value of its KL-th key (+inf: not a row)
     __shared__ uint32_t cnt[BM];             // per tile row: register-scan hits this tile
     __shared__ uint32_t ovf[2];              // per tile parity: some row overflowed its slots
-    // staged row rr (0 <= rr < 128) of the current half
-    auto ct_row = [&](int rr) -> float * {
-        return reinterpret_cast<float *>(rr < kCtRows ? st0 : st1) + (rr & (kCtRows - 1)) * kCtStride;
-    };
-    uint64_t *wscr = cand;  // long lists' staged scan: wave_topk scratch [4 waves][128]
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
     int mt, slab;
     big_tile_of(blockIdx.x, gridDim.x, n_mt, n_slabs, mt, slab);
     const int m0 = mt * BM;
     if (blockIdx.x == 0 && t == 0 && status) *status = 0u;
     const int vt0 = (int)((long long)slab * n_vt / n_slabs), vt1 = (int)((long long)(slab + 1) * n_vt / n_slabs);
-    // thread t owns tile row t (staged in half t / 128 as staged row t % 128)
-    const int my_half = t >> 7, my_rr = t & 127;
     const bool my_ok = m0 + t < M;
     uint64_t *my_list = partial + ((size_t)(my_ok ? m0 + t : 0) * n_slabs + slab) * KL;
+    float *tile = tiles + (size_t)blockIdx.x * kBigTileFloats;  // exact path: [256 rows][256 cols]
     thr[t] = my_ok ? -__builtin_inff() : __builtin_inff();
     cnt[t] = 0u;
     if (t < 2) ovf[t] = 0u;
     // (the mainloop's barriers order these before their first use)
-    for (int vt = vt0; vt < vt1; ++vt) {
-        const int v0 = vt * BN, par = vt & 1;
+    // A tile is kept in the workspace buffer ("stored") when it is the slab's
+    // first or follows a tile that overflowed; an overflow in a tile that was
+    // not stored drops its slots and forms the tile again, stored.  So no
+    // accumulator is live past the register scan.
+    bool store = true;
+    int pass = 0;  // parity of the overflow flag: per pass, a tile formed twice takes two
+    for (int vt = vt0; vt < vt1; ++pass) {
+        const int v0 = vt * BN, par = pass & 1;
+        const bool fresh = vt == vt0;
+        // the tile with the vocabulary's tail takes the exact path too (the
+        // register scan assumes every column real)
+        const bool scan = !fresh && v0 + BN <= V;
+        store = store || !scan;
         f32x16 acc[4][4];
         mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H);
-        bool staged = vt == vt0;  // a slab's first tile fills the lists from staged logits
-        if (!staged) {
-            // the stage buffers are idle here: the wave's scratch goes over the second one
-            register_scan(acc, thr, cnt, cand, &ovf[par], reinterpret_cast<float *>(st1) + wave * 1024,
-                                v0, V);
+        if (store) {
+            // straight from the accumulators, one base address per 4-row group
+            // (an opaque zero keeps the compiler from hoisting all sixteen out of the loop)
+            int zero;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+            float *tile_z = tile + zero;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float *b = tile_z + acc_row(wm, tm, 4 * g, lane) * BN + wn * 128 + (lane & 31);
+#define DF2_ST(E, TN) agpr_store_global<(E * BN + TN * 32) * 4>(b, acc[tm][TN][4 * g + E])
+                    DF2_ST(0, 0); DF2_ST(0, 1); DF2_ST(0, 2); DF2_ST(0, 3);
+                    DF2_ST(1, 0); DF2_ST(1, 1); DF2_ST(1, 2); DF2_ST(1, 3);
+                    DF2_ST(2, 0); DF2_ST(2, 1); DF2_ST(2, 2); DF2_ST(2, 3);
+                    DF2_ST(3, 0); DF2_ST(3, 1); DF2_ST(3, 2); DF2_ST(3, 3);
+#undef DF2_ST
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+        bool over = true;
+        if (scan) {
+            // the idle stage buffers hold the scan's scratch
+            register_scan(acc, thr, cnt, slots, &ovf[par], reinterpret_cast<float *>(st0), v0);
             __syncthreads();
-            staged = ovf[par] != 0u;
-            if (t == 0) ovf[par ^ 1] = 0u;  // last read a tile ago; next written a tile from now
+            over = ovf[par] != 0u;
+            if (t == 0) ovf[par ^ 1] = 0u;  // last read a pass ago; next written a pass from now
             const uint32_t n = cnt[t];
             cnt[t] = 0u;
-            if (!staged) {
-                // the row's hits go into its list (no accumulator is live from here on)
-                if (n) {
-                    uint64_t L[KL];
-                    load_list<KL>(L, my_list);
-                    for (uint32_t i = 0; i < n; ++i) list_insert<KL>(L, cand[t * kRowCand + i]);
-                    store_list<KL>(L, my_list);
-                    thr[t] = L[KL - 1] ? key_val(L[KL - 1]) : -__builtin_inff();
-                }
-                continue;
-            }
-            // overflow: every candidate is found again below; the slots are dropped
-        }
-        for (int half = 0; half < 2; ++half) {
-            if (wm == half) {
-#pragma unroll
-                for (int tm = 0; tm < 4; ++tm) {
-                    float *Ct = reinterpret_cast<float *>(tm < 2 ? st0 : st1);
-#pragma unroll
-                    for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            Ct[acc_row(0, tm & 1, i, lane) * kCtStride + wn * 128 + tn * 32 + (lane & 31)] =
-                                acc[tm][tn][i];
-                }
-            }
-            __syncthreads();
-            if constexpr (KL > 16) {
-                // long lists: one wave per row, the list one key per lane; this
-                // wave's 32 rows 16 at a time, the batch's lists fetched together
-                const bool fresh = vt == vt0;
-                for (int j0 = 0; j0 < 32; j0 += 16) {
-                    uint64_t lk[16];
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int row = min(half * 128 + wave + 4 * (j0 + j), M - 1 - m0);
-                        lk[j] = (!fresh && lane < KL) ? partial[((size_t)(m0 + row) * n_slabs + slab) * KL + lane] : 0ull;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int rr = wave + 4 * (j0 + j), row = half * 128 + rr;
-                        if (m0 + row >= M) break;
-                        const float4 v4 = *reinterpret_cast<const float4 *>(ct_row(rr) + 4 * lane);
-                        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-                        const float th = thr[row];
-                        uint64_t k[5];
-                        unsigned long long anym = 0;
-                        int npass = 0;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int col = v0 + 4 * lane + e;
-                            const bool p = col < V && vv[e] >= th;
-                            k[e] = p ? make_key(vv[e], (uint32_t)col) : 0ull;
-                            const unsigned long long m = __ballot(p);
-                            anym |= m;
-                            npass += __popcll(m);
-                        }
-                        if (!anym) continue;
-                        uint64_t top;
-                        if (npass <= 8 && !fresh) {  // a few candidates: insert one by one
-                            uint64_t cur = lk[j];
-                            uint64_t thk = readlane_u64(cur, KL - 1);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                unsigned long long m = __ballot(k[e] > thk);
-                                while (m) {
-                                    const int src = __builtin_ctzll(m);
-                                    m &= m - 1;
-                                    const uint64_t x = readlane_u64(k[e], src);
-                                    if (x > thk) {
-                                        cur = sorted_insert(cur, x, KL);
-                                        thk = readlane_u64(cur, KL - 1);
-                                    }
-                                }
-                            }
-                            top = cur;
-                        } else {
-                            k[4] = lk[j];
-                            top = wave_topk<5>(k, KL, wscr + wave * 128);
-                        }
-                        if (lane < KL) partial[((size_t)(m0 + row) * n_slabs + slab) * KL + lane] = top;
-                        const uint64_t kth = readlane_u64(top, KL - 1);
-                        if (lane == 0) thr[row] = kth ? key_val(kth) : -__builtin_inff();
-                    }
-                }
-            } else if (my_half == half && my_ok) {
-                // scan the row from position q0 on; candidates go to the thread's
-                // buffer; a full buffer is merged, the threshold raised and the
-                // scan resumed where it stopped (no logit is inserted twice)
-                const float *row = ct_row(my_rr);
-                uint64_t *buf = cand + my_rr * (kCandPerThread + 4);
-                const bool fresh = vt == vt0;
-                float my_thr = thr[t];
-                bool loaded = false, changed = false;
+            if (!over && n) {
+                // the row's hits go into its list
                 uint64_t L[KL];
-                int q0 = 0;
-                while (q0 < BN / 4) {
-                    int n = 0, q = q0;
-                    for (; q < BN / 4 && n < kCandPerThread; ++q) {
-                        const float4 v4 = *reinterpret_cast<const float4 *>(row + 4 * q);
-                        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int col = v0 + 4 * q + e;
-                            if (vv[e] >= my_thr && col < V) buf[n++] = make_key(vv[e], (uint32_t)col);
-                        }
-                    }
-                    q0 = q;
-                    if (n == 0) break;
-                    if (!loaded) {
-                        if (fresh) {
-#pragma unroll
-                            for (int j = 0; j < KL; ++j) L[j] = 0ull;
-                        } else {
-                            load_list<KL>(L, my_list);
-                        }
-                        loaded = true;
-                    }
-                    for (int i = 0; i < n; ++i) list_insert<KL>(L, buf[i]);
-                    my_thr = L[KL - 1] ? key_val(L[KL - 1]) : -__builtin_inff();
-                    changed = true;
-                }
-                if (changed) {
-                    store_list<KL>(L, my_list);
-                    thr[t] = my_thr;
-                }
+                load_list<KL>(L, my_list);
+                for (uint32_t i = 0; i < n; ++i) list_insert<KL>(L, slots[t * kRowCand + i]);
+                store_list<KL>(L, my_list);
+                thr[t] = L[KL - 1] ? key_val(L[KL - 1]) : -__builtin_inff();
             }
-            __syncthreads();
+        } else {
+            __syncthreads();  // the stored tile is visible to the workgroup
         }
+        if (!over) {
+            store = false;
+            ++vt;
+            continue;
+        }
+        if (store) {
+            // exact path over the stored tile (the slots, if any, are dropped)
+            if (my_ok)
+                exact_row_scan<KL>(tile + t * BN, V - v0, v0, fresh, my_list, &thr[t],
+                                   reinterpret_cast<uint64_t *>(st0) + t * kCandStride);
+            __syncthreads();  // the buffers in st0 are the next mainloop's first stage
+            ++vt;
+        }
+        store = true;  // next: this tile again if it was not stored, else the next tile, stored
     }
 }
 
@@ -722,6 +741,11 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
     p.merge_rows = 1;
     p.merge_lds = (size_t)2 * first * 8 + 8 * 128 * 8;
     p.partial_bytes = (size_t)M * p.n_lists * p.list_len * 8;
+    if (p.big) {  // then the exact-path tile buffers, one per workgroup
+        p.partial_bytes = (p.partial_bytes + 255) / 256 * 256;
+        p.tiles_offset = p.partial_bytes;
+        p.partial_bytes += (size_t)p.grid_x * kBigTileFloats * 4;
+    }
     return p;
 }
 
@@ -765,8 +789,10 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
                         : p.list_len == 16 ? lmhead_big_kernel<16>
                         : p.list_len == 32 ? lmhead_big_kernel<32>
                                            : lmhead_big_kernel<64>;
+            float *tiles = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(partial) + p.tiles_offset);
             hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(big::NT), p.lds, stream, (const uint16_t *)h,
-                               (const uint16_t *)w, (int)M, H, V, p.n_mt, p.n_lists, p.n_tiles, partial, status);
+                               (const uint16_t *)w, (int)M, H, V, p.n_mt, p.n_lists, p.n_tiles, partial, tiles,
+                               status);
             e = hipGetLastError();
         } else {
             return hipErrorInvalidValue;
