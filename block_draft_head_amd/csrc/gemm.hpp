@@ -289,8 +289,17 @@ struct Pipe {
 // copy has landed and all waves have passed a barrier after their last
 // fragment read that matters; the caller may reuse st0 and st1 after one more
 // barrier (the last fragment reads are of a spare slice and unused).
+//
+// prefilled: the caller has already issued this wave's copies of k-slice 0
+// into st0 (prefill below, same operands), so the first stage only waits.
+__device__ __forceinline__ void prefill(uint8_t *st0, const uint16_t *A, int a_rows, const uint16_t *B, int b_rows,
+                                        int H) {
+    Pipe P;
+    P.init(A, a_rows, B, b_rows, H);
+    P.fill(st0, 0);
+}
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *st0, uint8_t *st1, const uint16_t *A,
-                                         int a_rows, const uint16_t *B, int b_rows, int H) {
+                                         int a_rows, const uint16_t *B, int b_rows, int H, bool prefilled = false) {
     Pipe P;
     P.init(A, a_rows, B, b_rows, H);
 #pragma unroll
@@ -299,7 +308,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *st0, uint
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-    P.fill(st0, 0);
+    if (!prefilled) P.fill(st0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     u32x4 fa[2][4], fb[2][4];

@@ -430,12 +430,12 @@ __device__ __attribute__((noinline)) void exact_row_scan(const float *__restrict
     float top[KL];
 #pragma unroll
     for (int j = 0; j < KL; ++j) top[j] = -__builtin_inff();
-    for (int q0 = 0; q0 < big::BN / 4; q0 += 8) {
-        float4 v4[8];
+    for (int q0 = 0; q0 < big::BN / 4; q0 += 16) {  // 16 loads in flight per round trip
+        float4 v4[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v4[u] = row4[q0 + u];
+        for (int u = 0; u < 16; ++u) v4[u] = row4[q0 + u];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
             const int c = 4 * (q0 + u);
             float m = fmaxf(fmaxf(v4[u].x, c + 1 < nvalid ? v4[u].y : -__builtin_inff()),
                             fmaxf(c + 2 < nvalid ? v4[u].z : -__builtin_inff(),
@@ -468,20 +468,23 @@ __device__ __attribute__((noinline)) void exact_row_scan(const float *__restrict
         changed = true;
         n = 0;
     };
-    for (int q0 = 0; q0 < big::BN / 4; q0 += 4) {
-        float4 v4[4];
+    for (int q0 = 0; q0 < big::BN / 4; q0 += 16) {
+        float4 v4[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v4[u] = row4[q0 + u];
+        for (int u = 0; u < 16; ++u) v4[u] = row4[q0 + u];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float vv[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
+        for (int s4 = 0; s4 < 4; ++s4) {  // 16 values per step, then the buffer check
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = 4 * (q0 + u) + e;
-                if (vv[e] >= th && c < nvalid) buf[n++] = make_key(vv[e], (uint32_t)(v0 + c));
+            for (int u = 4 * s4; u < 4 * s4 + 4; ++u) {
+                const float vv[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 4 * (q0 + u) + e;
+                    if (vv[e] >= th && c < nvalid) buf[n++] = make_key(vv[e], (uint32_t)(v0 + c));
+                }
             }
+            if (n > kCandPerThread) flush();
         }
-        if (n > kCandPerThread) flush();
     }
     if (n) flush();
     if (changed) {
@@ -520,6 +523,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // accumulator is live past the register scan.
     bool store = true;
     int pass = 0;  // parity of the overflow flag: per pass, a tile formed twice takes two
+    // short lists live in their owner's registers between tiles (written to
+    // the workspace around exact-path tiles and at the end)
+    constexpr bool kRegList = KL <= 16;
+    uint64_t RL[kRegList ? KL : 1];
+#pragma unroll
+    for (int j = 0; j < (kRegList ? KL : 1); ++j) RL[j] = 0ull;
+    bool prefilled = false;
     for (int vt = vt0; vt < vt1; ++pass) {
         const int v0 = vt * BN, par = pass & 1;
         const bool fresh = vt == vt0;
@@ -528,7 +538,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool scan = !fresh && v0 + BN <= V;
         store = store || !scan;
         f32x16 acc[4][4];
-        mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H);
+        mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H, prefilled);
+        prefilled = false;
         if (store) {
             // straight from the accumulators, one base address per 4-row group
             // (an opaque zero keeps the compiler from hoisting all sixteen out of the loop)
@@ -558,13 +569,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (t == 0) ovf[par ^ 1] = 0u;  // last read a pass ago; next written a pass from now
             const uint32_t n = cnt[t];
             cnt[t] = 0u;
+            if (!over && vt + 1 < vt1) {
+                // the next tile's first k-slice loads under the list insertion (the
+                // barrier above ended the scan's use of st0)
+                const int v1 = v0 + BN;
+                prefill(st0, h + (size_t)m0 * H, M - m0, w + (size_t)v1 * H, V - v1, H);
+                prefilled = true;
+            }
             if (!over && n) {
                 // the row's hits go into its list
-                uint64_t L[KL];
-                load_list<KL>(L, my_list);
-                for (uint32_t i = 0; i < n; ++i) list_insert<KL>(L, slots[t * kRowCand + i]);
-                store_list<KL>(L, my_list);
-                thr[t] = L[KL - 1] ? key_val(L[KL - 1]) : -__builtin_inff();
+                if constexpr (kRegList) {
+                    for (uint32_t i = 0; i < n; ++i) list_insert<KL>(RL, slots[t * kRowCand + i]);
+                    thr[t] = RL[KL - 1] ? key_val(RL[KL - 1]) : -__builtin_inff();
+                } else {
+                    uint64_t L[KL];
+                    load_list<KL>(L, my_list);
+                    for (uint32_t i = 0; i < n; ++i) list_insert<KL>(L, slots[t * kRowCand + i]);
+                    store_list<KL>(L, my_list);
+                    thr[t] = L[KL - 1] ? key_val(L[KL - 1]) : -__builtin_inff();
+                }
             }
         } else {
             __syncthreads();  // the stored tile is visible to the workgroup
@@ -576,13 +599,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         if (store) {
             // exact path over the stored tile (the slots, if any, are dropped)
-            if (my_ok)
+            if (my_ok) {
+                if constexpr (kRegList) {
+                    if (!fresh) store_list<KL>(RL, my_list);
+                }
                 exact_row_scan<KL>(tile + t * BN, V - v0, v0, fresh, my_list, &thr[t],
                                    reinterpret_cast<uint64_t *>(st0) + t * kCandStride);
+                if constexpr (kRegList) load_list<KL>(RL, my_list);
+            }
             __syncthreads();  // the buffers in st0 are the next mainloop's first stage
             ++vt;
         }
         store = true;  // next: this tile again if it was not stored, else the next tile, stored
+    }
+    if constexpr (kRegList) {
+        if (my_ok) store_list<KL>(RL, my_list);
     }
 }
 
