@@ -253,6 +253,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(w, w.name)
     roof["kernel"] = ("lmhead_stream_kernel + topk_merge_kernel" if N <= 8 else
+                      "lmhead_big_kernel + topk_merge_kernel" if w.dtype == "bf16" else
                       "lmhead_tiled_kernel + topk_merge_kernel")
     roof["algorithmic_bytes"] = lm_bytes
     roof["avg_ms"] = lm_ms
