@@ -287,13 +287,12 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
 // logits go to a per-workgroup buffer in the workspace and each owner scans
 // its whole row there.  Insertion keeps the exact top-KL under the key order,
 // so the result does not depend on the tiling or on which path a tile took.
-constexpr int kRowCand = 14;        // candidate slots per tile row
-constexpr int kScrStride = 68;      // register scan: a lane's 64 values in LDS, padded against bank conflicts
+constexpr int kRowCand = 32;        // candidate slots per tile row (over the second stage buffer)
 constexpr int kCandPerThread = 8;   // exact path: buffer merged past this many (16 more land per step)
 constexpr int kCandStride = kCandPerThread + 16;
 constexpr size_t kBigTileFloats = (size_t)big::BM * big::BN;  // exact path buffer per workgroup
-static_assert(2 * big::STAGE + big::BM * kRowCand * 8 + big::BM * 8 + 8 <= 160 * 1024, "LM-head workgroup LDS");
-static_assert(big::NT * kScrStride * 4 <= 2 * big::STAGE, "register-scan scratch over the stage buffers");
+static_assert(big::BM * kRowCand * 8 <= big::STAGE, "candidate slots over one stage buffer");
+static_assert(big::NT * 64 * 4 <= big::STAGE, "register-scan scratch over one stage buffer");
 static_assert(big::NT * kCandStride * 8 <= big::STAGE, "exact-path buffers over one stage buffer");
 
 // (row tile, slab) of workgroup `bid`: the workgroups of one XCD (bid % 8)
@@ -370,7 +369,10 @@ __device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], co
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
     const int hl = (lane >> 5) + zero;
     const uint32_t col0 = (uint32_t)(v0 + wn * 128 + (lane & 31));
-    float *sc = scr + (wave * 64 + lane) * kScrStride;  // the lane's 64 values
+    // the lane's 64 values: 16-byte chunk q at (q ^ lane % 16), so each 16 lanes
+    // writing one chunk hit 16 different bank groups
+    float *sc = scr + (wave * 64 + lane) * 64;
+    const int swz = lane & 15;
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
         const int rbase = wm * 128 + tm * 32 + 4 * hl;  // rows of acc[tm][*][i]: rbase + 8 (i / 4) + i % 4
@@ -393,8 +395,8 @@ __device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], co
         }
         if (__ballot(bits != 0)) {
 #define DF2_SCR(TN, Q)                                                                                        \
-    agpr_store_lds4<(16 * TN + 4 * Q) * 4>(                                                                   \
-        sc, __builtin_shufflevector(acc[tm][TN], acc[tm][TN], 4 * Q, 4 * Q + 1, 4 * Q + 2, 4 * Q + 3))
+    agpr_store_lds4<0>(sc + 4 * ((4 * TN + Q) ^ swz),                                                         \
+                       __builtin_shufflevector(acc[tm][TN], acc[tm][TN], 4 * Q, 4 * Q + 1, 4 * Q + 2, 4 * Q + 3))
             DF2_SCR(0, 0); DF2_SCR(0, 1); DF2_SCR(0, 2); DF2_SCR(0, 3);
             DF2_SCR(1, 0); DF2_SCR(1, 1); DF2_SCR(1, 2); DF2_SCR(1, 3);
             DF2_SCR(2, 0); DF2_SCR(2, 1); DF2_SCR(2, 2); DF2_SCR(2, 3);
@@ -406,7 +408,8 @@ __device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], co
                 const int tn = j >> 4, i = j & 15;
                 const int r = rbase + 8 * (i >> 2) + (i & 3);
                 const uint32_t sl = atomicAdd(cnt + r, 1u);
-                if (sl < (uint32_t)kRowCand) slots[r * kRowCand + sl] = make_key(sc[j], col0 + 32 * tn);
+                if (sl < (uint32_t)kRowCand)
+                    slots[r * kRowCand + sl] = make_key(sc[4 * ((j >> 2) ^ swz) + (j & 3)], col0 + 32 * tn);
                 else *ovf = 1u;
             }
         }
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     using namespace big;
     __shared__ __align__(16) uint8_t st0[STAGE];
     __shared__ __align__(16) uint8_t st1[STAGE];
-    __shared__ __align__(16) uint64_t slots[BM * kRowCand];
+    uint64_t *slots = reinterpret_cast<uint64_t *>(st1);  // register-scan hits, [BM][kRowCand]
     __shared__ __align__(16) float thr[BM];  // per tile row: value of its KL-th key (+inf: not a row)
     __shared__ uint32_t cnt[BM];             // per tile row: register-scan hits this tile
     __shared__ uint32_t ovf[2];              // per tile parity: some row overflowed its slots
