@@ -426,15 +426,20 @@ __device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], co
 // into the list and the threshold raised.
 // (Not inlined: it runs on rare tiles, and inlined its registers would crowd
 // the accumulators of the common path.)
+// (Out of line, so its pointers carry their address spaces explicitly: as
+// generic pointers every access would be a flat access with full waits.)
+typedef __attribute__((address_space(1))) const f32x4 gfloat4;
+typedef __attribute__((address_space(1))) uint64_t gu64;
+typedef __attribute__((address_space(3))) uint64_t lu64;
+typedef __attribute__((address_space(3))) float lfloat;
 template <int KL>
-__device__ __attribute__((noinline)) void exact_row_scan(const float *__restrict__ row, int nvalid, int v0,
-                                                         bool fresh, uint64_t *list, float *thr_out, uint64_t *buf) {
-    const float4 *row4 = reinterpret_cast<const float4 *>(row);
+__device__ __attribute__((noinline)) void exact_row_scan(gfloat4 *__restrict__ row4, int nvalid, int v0, bool fresh,
+                                                         gu64 *list, lfloat *thr_out, lu64 *buf) {
     float top[KL];
 #pragma unroll
     for (int j = 0; j < KL; ++j) top[j] = -__builtin_inff();
     for (int q0 = 0; q0 < big::BN / 4; q0 += 16) {  // 16 loads in flight per round trip
-        float4 v4[16];
+        f32x4 v4[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) v4[u] = row4[q0 + u];
 #pragma unroll
@@ -462,7 +467,8 @@ __device__ __attribute__((noinline)) void exact_row_scan(const float *__restrict
 #pragma unroll
                 for (int j = 0; j < KL; ++j) L[j] = 0ull;
             } else {
-                load_list<KL>(L, list);
+#pragma unroll
+                for (int j = 0; j < KL; ++j) L[j] = list[j];
             }
             loaded = true;
         }
@@ -472,7 +478,7 @@ __device__ __attribute__((noinline)) void exact_row_scan(const float *__restrict
         n = 0;
     };
     for (int q0 = 0; q0 < big::BN / 4; q0 += 16) {
-        float4 v4[16];
+        f32x4 v4[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) v4[u] = row4[q0 + u];
 #pragma unroll
@@ -491,7 +497,8 @@ __device__ __attribute__((noinline)) void exact_row_scan(const float *__restrict
     }
     if (n) flush();
     if (changed) {
-        store_list<KL>(L, list);
+#pragma unroll
+        for (int j = 0; j < KL; ++j) list[j] = L[j];
         *thr_out = th;
     }
 }
@@ -606,8 +613,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if constexpr (kRegList) {
                     if (!fresh) store_list<KL>(RL, my_list);
                 }
-                exact_row_scan<KL>(tile + t * BN, V - v0, v0, fresh, my_list, &thr[t],
-                                   reinterpret_cast<uint64_t *>(st0) + t * kCandStride);
+                exact_row_scan<KL>((gfloat4 *)(tile + t * BN), V - v0, v0, fresh, (gu64 *)my_list,
+                                   (lfloat *)&thr[t], (lu64 *)(reinterpret_cast<uint64_t *>(st0) + t * kCandStride));
                 if constexpr (kRegList) load_list<KL>(RL, my_list);
             }
             __syncthreads();  // the buffers in st0 are the next mainloop's first stage
