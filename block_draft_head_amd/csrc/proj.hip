@@ -141,10 +141,14 @@ struct EpiConv {
 };
 
 // ------------------------------------------------------------ tiled
+// 64 x 64 tiles: the projections have few output columns (2·T·G or r), so
+// larger tiles would leave most CUs idle.
+constexpr int kProjTile = 64;
+
 template <typename T, class Epi>
 __global__ __launch_bounds__(256) void proj_tiled_kernel(const T *__restrict__ A, const T *__restrict__ W,
                                                          int M, int H, Epi epi) {
-    using Cfg = TiledCfg<T, 128, 128>;
+    using Cfg = TiledCfg<T, kProjTile, kProjTile>;
     extern __shared__ __align__(16) uint8_t smem[];
     const int ct = blockIdx.x, m0 = blockIdx.y * Cfg::BM;
     f32x4 acc[Cfg::TM][Cfg::TN];
@@ -165,13 +169,13 @@ __global__ __launch_bounds__(256) void proj_tiled_kernel(const T *__restrict__ A
 template <typename T, class Epi>
 static hipError_t run_proj_tiled(int64_t M, int H, int n_col_tiles, const void *A, const void *W, const Epi &epi,
                                  hipStream_t stream) {
-    using Cfg = TiledCfg<T, 128, 128>;
+    using Cfg = TiledCfg<T, kProjTile, kProjTile>;
     const size_t lds = Cfg::STAGE_BYTES > Cfg::CTILE_BYTES ? Cfg::STAGE_BYTES : Cfg::CTILE_BYTES;
     auto kern = proj_tiled_kernel<T, Epi>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(n_col_tiles, (unsigned)((M + 127) / 128)), dim3(256), lds, stream,
+    hipLaunchKernelGGL(kern, dim3(n_col_tiles, (unsigned)((M + kProjTile - 1) / kProjTile)), dim3(256), lds, stream,
                        (const T *)A, (const T *)W, (int)M, H, epi);
     return hipGetLastError();
 }
@@ -195,7 +199,7 @@ static hipError_t run_conv_prepare(int64_t N, int bs, int H, int taps, int gs, c
         return hipGetLastError();
     }
     EpiConv<T> epi{(const T *)x, (const T *)base, (T *)x_out, k_post, (int)N, H, bs, taps, gs, G, 0};
-    epi.Gw = 128 / (2 * taps);
+    epi.Gw = kProjTile / (2 * taps);
     const int n_ct = (G + epi.Gw - 1) / epi.Gw;
     return run_proj_tiled<T>(N, H, n_ct, x, w_proj, epi, stream);
 }
@@ -216,7 +220,7 @@ static hipError_t run_context_proj(int64_t N, int H, int r, const void *h, const
         return hipGetLastError();
     }
     EpiStore epi{g, (int)N, r, status};
-    return run_proj_tiled<T>(N, H, (r + 127) / 128, h, w_h, epi, stream);
+    return run_proj_tiled<T>(N, H, (r + kProjTile - 1) / kProjTile, h, w_h, epi, stream);
 }
 
 hipError_t launch_context_proj(int dtype, int64_t N, int H, int r, const void *h, const void *w_h,
