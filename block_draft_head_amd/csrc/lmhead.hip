@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
 // its whole row there.  Insertion keeps the exact top-KL under the key order,
 // so the result does not depend on the tiling or on which path a tile took.
 constexpr int kRowCand = 32;        // candidate slots per tile row (over the second stage buffer)
-constexpr int kCandPerThread = 8;   // exact path: buffer merged past this many (16 more land per step)
+constexpr int kCandPerThread = 16;  // exact path: buffers merged once one holds more (16 more land per step)
 constexpr int kCandStride = kCandPerThread + 16;
 constexpr size_t kBigTileFloats = (size_t)big::BM * big::BN;  // exact path buffer per workgroup
 static_assert(big::BM * kRowCand * 8 <= big::STAGE, "candidate slots over one stage buffer");
@@ -492,7 +492,9 @@ __device__ __attribute__((noinline)) void exact_row_scan(gfloat4 *__restrict__ r
                     if (vv[e] >= th && c < nvalid) buf[n++] = make_key(vv[e], (uint32_t)(v0 + c));
                 }
             }
-            if (n > kCandPerThread) flush();
+            // all lanes merge together once any buffer is past the mark (a merge
+            // per lane at its own step would run the wave through every one)
+            if (__any(n > kCandPerThread)) flush();
         }
     }
     if (n) flush();
