@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from block_draft_head_amd.inputs import Workload, make_inputs
+from block_draft_head_amd.inputs import Workload, make_inputs, to_storage
 from oracle import dflash2_oracle as O
 from tests.helpers import (act_ok, close, compare_tf, compare_topk, compare_walk, conv_term_scale, to_dev,
                            to_np)
@@ -135,6 +135,47 @@ def test_unary_topk_exact_ties_take_the_lower_id(D, N):
     want = torch.sort(tied).values.int()
     assert torch.equal(ids[:, :8], want.expand(N, 8))
     assert torch.equal(vals[:, :8], vals[:, :1].expand(N, 8))
+
+
+@pytest.mark.parametrize("N,V,K", [(40, 6000, 8), (300, 6001, 16), (260, 5000, 64), (16, 777, 7)])
+def test_unary_topk_rising_logits_take_every_fallback(D, N, V, K):
+    """Weight rows whose norm grows with the id: every vocabulary tile beats
+    the thresholds the earlier tiles set, so in the many-row kernel rows
+    overflow their candidate slots on nearly every tile and the tiles are
+    formed again and scanned exactly."""
+    log(f"rising topk N={N} V={V} K={K}")
+    H = 256
+    w = wl(n_blocks=N, block_size=1, hidden=H, vocab=V, top_k=K)
+    inp = make_inputs(w, seed=11, fields=["h", "gold"])
+    rng = np.random.default_rng(11)
+    scale = (1.0 + 3.0 * np.arange(V) / V).astype(np.float32)[:, None]
+    w_lm = to_storage(torch.from_numpy((rng.standard_normal((V, H)) / np.sqrt(H)).astype(np.float32) * scale), "bf16")
+    ids, vals, gl = D.unary_topk(to_dev(inp["h"]), to_dev(w_lm), K, gold_ids=to_dev(inp["gold"]))
+    U = O.lm_logits(inp["h"], w_lm, "bf16")
+    fails, flags, msgs = compare_topk(to_np(ids), to_np(vals), U, K)
+    log(f"  fails={fails} flags={flags}")
+    assert fails == 0, msgs[:5]
+    assert flags <= max(1, N // 50)
+    assert close(to_np(gl), U[np.arange(N), inp["gold"]]).all()
+
+
+@pytest.mark.parametrize("N,K", [(24, 16), (300, 8), (40, 64)])
+def test_unary_topk_repeated_rows_tie_everywhere(D, N, K):
+    """Five distinct weight rows repeated over the vocabulary: every tile
+    holds exact ties at the thresholds, and the K best must be the lowest ids
+    of the best value(s)."""
+    H, V = 256, 3001
+    w = wl(n_blocks=N, block_size=1, hidden=H, vocab=V, top_k=K)
+    inp = make_inputs(w, seed=12, fields=["h", "w_lm"])
+    w_lm = inp["w_lm"][np.arange(V) % 5].copy()
+    ids, vals, _ = D.unary_topk(to_dev(inp["h"]), to_dev(w_lm), K)
+    U = O.lm_logits(inp["h"], w_lm, "bf16")
+    fails, flags, msgs = compare_topk(to_np(ids), to_np(vals), U, K)
+    assert fails == 0, msgs[:5]
+    # with only 5 distinct values per row the K best are fixed exactly (no
+    # near-tie is possible between distinct values of this size)
+    order = np.lexsort((np.broadcast_to(np.arange(V), U.shape), -U), axis=1)[:, :K]
+    assert np.array_equal(to_np(ids), order.astype(np.int32))
 
 
 def test_unary_topk_is_deterministic(D):
