@@ -17,6 +17,7 @@ constexpr uint32_t kStatusIdRange = 1u;
 
 struct LmheadPlan {
     bool streaming, big;  // big: 256 x 256 bf16 MFMA tiles (many rows)
+    bool dma;             // streaming, weights copied into LDS (bf16, at most 8 rows)
     int n_mt;
     int nw, prefetch, n_tiles;
     int grid_x, grid_y, n_lists;

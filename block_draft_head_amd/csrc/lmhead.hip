@@ -6,6 +6,8 @@
 // vocabulary, and topk_merge_kernel merges the slices.  A key orders
 // candidates by value, then by lower id (see make_key), so the result does not
 // depend on how the vocabulary was split.
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemm.hpp"
 #include "launch.hpp"
@@ -197,6 +199,214 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
         if (lane < K) partial[((size_t)row * gridDim.x + blockIdx.x) * K + lane] = top;
     }
 
+}
+
+// ---------------------------------------------------------------- streaming through LDS (bf16)
+//
+// The same work split and epilogue as lmhead_stream_kernel, but the weight
+// rows reach the MFMAs through LDS: each wave copies 2 KB blocks (16
+// vocabulary rows x 64 k) from HBM straight into a private ring of kDmaRing
+// LDS blocks with non-temporal global_load_lds_dwordx4 (each instruction
+// reads 8 whole 128-byte lines), and reads its B fragments from there.
+// Streaming a weight this way reads HBM about 12% faster than loading it
+// into registers (the register loads read 64 bytes of 16 rows each, which
+// the non-temporal policy cannot serve well).  A wave waits only for its own
+// copies, so the stream needs no barrier.  Row r of a block holds 16-byte
+// chunk c at position c ^ (r & 7): the 8 lanes of a fragment read hit 8
+// different bank groups.
+constexpr int kDmaWaves = 4;
+constexpr int kDmaRing = 6;        // 2 KB blocks per wave
+constexpr int kDmaCandCap = 128;   // candidate slots per wave and row
+
+inline size_t dma_lds_bytes(int H) {
+    return (size_t)H * 16 + (size_t)kDmaWaves * kDmaRing * 2048 + (size_t)kDmaWaves * 8 * kDmaCandCap * 8 +
+           (size_t)kDmaWaves * 128 * 8 + (size_t)kDmaWaves * 8 * 4 + 16;
+}
+
+__global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K, int n_tiles,
+    const int32_t *__restrict__ gold, float *__restrict__ gold_logit, uint64_t *__restrict__ partial,
+    uint32_t *__restrict__ status) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int NW = kDmaWaves, NB = kDmaRing, CAP = kDmaCandCap;
+    const int NBLK = H / 64;  // 2 KB blocks per tile
+    uint4 *afrag = reinterpret_cast<uint4 *>(smem);
+    uint8_t *rings = smem + (size_t)H * 16;                                         // [NW][NB][2048]
+    uint64_t *bufs = reinterpret_cast<uint64_t *>(rings + (size_t)NW * NB * 2048);  // [NW][8][CAP]
+    uint64_t *scratch = bufs + NW * 8 * CAP;                                        // [NW][128]
+    int *cnts = reinterpret_cast<int *>(scratch + NW * 128);                        // [NW][8]
+    (void)n_tiles;
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && status) *status = 0u;
+
+    load_afrag<uint16_t>(afrag, h, M, H);
+    __syncthreads();
+
+    // every wave of the grid streams an equal contiguous range of vocabulary
+    // rows (the weight stream is the whole cost, so equal bytes finish
+    // together); its 16-row tiles start at r0, the last one partial
+    const long long nw_all = (long long)gridDim.x * NW, gw = (long long)blockIdx.x * NW + wave;
+    const int r0 = (int)(gw * V / nw_all), r1 = (int)((gw + 1) * V / nw_all);
+    const int ntile = (r1 - r0 + 15) / 16;
+    uint64_t *mybuf = bufs + wave * 8 * CAP;
+    const int n = lane & 15, q = lane >> 4;
+    int grow[4];
+    uint64_t thr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = 4 * q + e;
+        grow[e] = (gold && row < M) ? gold[row] : -1;
+        thr[e] = 0ull;
+    }
+    int cnt[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) cnt[r] = 0;
+    uint64_t *myscratch = scratch + wave * 128;
+    auto compact = [&](int r) {
+        uint64_t *B = mybuf + r * CAP;
+        uint64_t k[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) k[i] = lane + 64 * i < cnt[r] ? B[lane + 64 * i] : 0ull;
+        const uint64_t top = wave_topk<2>(k, K, myscratch);
+        const int kept = cnt[r] < K ? cnt[r] : K;
+        if (lane < K) B[lane] = top;
+        cnt[r] = kept;
+        const uint64_t kth = readlane_u64(top, K - 1);
+        if (q == (r >> 2)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e == (r & 3)) thr[e] = kth;
+        }
+    };
+
+    // copies: lane L of copy j of a block fills row 8 j + L / 8, position L % 8,
+    // with the row's chunk (L % 8) ^ (row & 7).  Rows past the range read row 0
+    // instead (a few lines per partial tile; every copy is still issued, so the
+    // counted waits stay exact).
+    uint8_t *ring = rings + (size_t)wave * NB * 2048;
+    const uint32_t ring_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)ring;
+    const int crow = lane >> 3, cpos = lane & 7;
+    uint32_t roff[2];  // byte offset of this lane's chunk of its two copy rows, block 0
+    auto set_rows = [&](int tile) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 8 * j + crow, vrow = r0 + tile * 16 + row;
+            roff[j] = (uint32_t)((cpos ^ (row & 7)) * 16) + (vrow < r1 ? (uint32_t)vrow * (uint32_t)H * 2u : 0u);
+        }
+    };
+    auto copy_block = [&](const uint32_t (&ro)[2], int blk, int slot) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(ro[j] + (uint32_t)blk * 128u), "s"(w),
+                         "{m0}"(ring_lds + (uint32_t)slot * 2048u + (uint32_t)j * 1024u)
+                         : "memory");
+    };
+    // fragments of the block in `slot`: B from the ring, A from afrag (rows 8..15
+    // of A only reach output rows 8..15, which are never read)
+    const uint32_t bq0 = (uint32_t)(n * 128 + (((0 + q) ^ (n & 7)) << 4));
+    const uint32_t bq1 = (uint32_t)(n * 128 + (((4 + q) ^ (n & 7)) << 4));
+    const uint4 *arow = afrag + q * 8 + (n & 7);
+    auto frags = [&](int slot, int blk, uint4 (&fb)[2], uint4 (&fa)[2]) {
+        fb[0] = *reinterpret_cast<const uint4 *>(ring + slot * 2048 + bq0);
+        fb[1] = *reinterpret_cast<const uint4 *>(ring + slot * 2048 + bq1);
+        fa[0] = arow[(2 * blk) * 32];
+        fa[1] = arow[(2 * blk + 1) * 32];
+    };
+
+    int t = 0;
+    if (ntile > 0) {
+        // The wave's stream of blocks: the ring holds NB consecutive positions.
+        // Position p + b + NB - 1 is copied while block b is in use; block b + 1
+        // is waited for (at most NB - 2 later blocks in flight) and its
+        // fragments read before block b's MFMAs.  Past the last tile the copies
+        // re-read blocks of the last tile into free slots.
+        uint32_t cur[2], nxt[2];
+        set_rows(0);
+        cur[0] = roff[0];
+        cur[1] = roff[1];
+        set_rows(ntile > 1 ? 1 : 0);
+        nxt[0] = roff[0];
+        nxt[1] = roff[1];
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i) copy_block(cur, min(i, NBLK - 1), i);
+        int slot = 0;             // ring slot of the block in use
+        int cslot = NB - 1;       // ring slot of the next copy
+        uint4 fb[2][2], fa[2][2];
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NB - 2)) : "memory");  // block 0 has landed
+        frags(0, 0, fb[0], fa[0]);
+        while (true) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            // one block: copy ahead, wait for block b + 1, read its fragments
+            // into half CB ^ 1, multiply block b from half CB (NBLK is even, so
+            // the halves alternate with a fixed pattern and the next tile
+            // starts from half 0)
+            auto step = [&](int b, auto cbc) {
+                constexpr int CB = decltype(cbc)::value;
+                const int ahead = b + NB - 1;
+                if (ahead < NBLK) copy_block(cur, ahead, cslot);
+                else copy_block(nxt, min(ahead - NBLK, NBLK - 1), cslot);
+                cslot = cslot + 1 == NB ? 0 : cslot + 1;
+                const int nslot = slot + 1 == NB ? 0 : slot + 1;
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NB - 2)) : "memory");
+                frags(nslot, b + 1 < NBLK ? b + 1 : 0, fb[CB ^ 1], fa[CB ^ 1]);
+                mma16<uint16_t>(acc, fa[CB][0], fb[CB][0]);
+                mma16<uint16_t>(acc, fa[CB][1], fb[CB][1]);
+                slot = nslot;
+            };
+            for (int b = 0; b < NBLK; b += 2) {
+                step(b, std::integral_constant<int, 0>{});
+                step(b + 1, std::integral_constant<int, 1>{});
+            }
+            const int v = r0 + t * 16 + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 4 * q + e;
+                const bool ok = row < M && v < r1;
+                const uint64_t key = ok ? make_key(acc[e], (uint32_t)v) : 0ull;
+                if (ok && grow[e] == v) gold_logit[row] = acc[e];
+                const bool pass = key > thr[e];
+                const unsigned long long mask = __ballot(pass);
+                const int c0 = __popcll(mask & 0xffffull), c1 = __popcll(mask & 0xffff0000ull);
+                if (pass) {
+                    const int pos = lanes_below(mask) - (q ? c0 : 0);
+                    mybuf[row * CAP + (q ? cnt[4 + e] : cnt[e]) + pos] = key;
+                }
+                cnt[e] += c0;
+                cnt[4 + e] += c1;
+            }
+            // (a gold store is a vector-memory op too: let it drain so the ring's
+            // counted waits above stay exact)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NB - 2)) : "memory");
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (cnt[r] > CAP - 16) compact(r);
+            if (t + 1 >= ntile) break;
+            ++t;
+            cur[0] = nxt[0];
+            cur[1] = nxt[1];
+            set_rows(t + 1 < ntile ? t + 1 : t);
+            nxt[0] = roff[0];
+            nxt[1] = roff[1];
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if (lane < 8) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (lane == r) cnts[wave * 8 + r] = cnt[r];
+    }
+    __syncthreads();
+    for (int row = wave; row < M; row += NW) {
+        constexpr int R = 2 * NW;
+        uint64_t k[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int ww = i >> 1, slot = lane + 64 * (i & 1);
+            k[i] = slot < cnts[ww * 8 + row] ? bufs[(ww * 8 + row) * CAP + slot] : 0ull;
+        }
+        const uint64_t top = wave_topk<R>(k, K, myscratch);
+        if (lane < K) partial[((size_t)row * gridDim.x + blockIdx.x) * K + lane] = top;
+    }
 }
 
 // ---------------------------------------------------------------- tiled
@@ -741,7 +951,17 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
     const int nw = 8;
     size_t stream_lds = (size_t)S * 32 * 16 + (size_t)nw * (8 * kCandCap + 128) * 8 + (size_t)nw * 8 * 4 + 16;
     if (stream_lds < (size_t)kStreamMinLds) stream_lds = kStreamMinLds;
-    if (M <= kStreamMaxRows && stream_lds <= 160 * 1024) {
+    if (dtype != 0 && M <= kStreamMaxRows && H % 128 == 0 && H / 64 >= kDmaRing - 1 && dma_lds_bytes(H) <= 160 * 1024 &&
+        (uint64_t)V * H * 2 < (1ull << 32)) {
+        // weights through LDS (the ring's look-ahead stays within the next tile)
+        p.streaming = true;
+        p.dma = true;
+        p.n_tiles = (V + 15) / 16;
+        p.grid_x = p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs;
+        p.grid_y = 1;
+        p.n_lists = p.grid_x;
+        p.lds = dma_lds_bytes(H);
+    } else if (M <= kStreamMaxRows && stream_lds <= 160 * 1024) {
         p.streaming = true;
         p.nw = nw;
         p.n_tiles = (V + 15) / 16;
@@ -816,7 +1036,17 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
                              float *gold_logit, uint64_t *partial, uint32_t *status,
                              hipStream_t stream) {
     hipError_t e;
-    if (p.streaming) {
+    if (p.dma) {
+        if constexpr (sizeof(T) == 2) {
+            if ((e = set_lds(lmhead_dma_kernel, p.lds)) != hipSuccess) return e;
+            hipLaunchKernelGGL(lmhead_dma_kernel, dim3(p.grid_x), dim3(64 * kDmaWaves), p.lds, stream,
+                               (const uint16_t *)h, (const uint16_t *)w, (int)M, H, V, K, p.n_tiles, gold, gold_logit,
+                               partial, status);
+            e = hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (p.streaming) {
 #define DF2_STREAM(PP) launch_stream<T, PP>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream)
         switch (p.prefetch) {
             case 16: e = DF2_STREAM(16); break;
