@@ -7,6 +7,7 @@
 // candidates by value, then by lower id (see make_key), so the result does not
 // depend on how the vocabulary was split.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "gemm.hpp"
@@ -64,11 +65,55 @@ __device__ __forceinline__ void insert_survivors(uint64_t &cur, uint64_t &thr, u
 // filtered.  Lane (n = l % 16, q = l / 16) holds the logits of vocabulary row
 // tile*16 + n for rows 4q .. 4q+3.  Each wave appends the logits above its
 // per-row threshold to an LDS candidate buffer (ballot compaction, no sort)
-// and shrinks a buffer to its top K only when it fills; the workgroup
-// reduces its waves' lists at the end.
+// and shrinks a buffer only when it fills; the workgroup reduces its waves'
+// lists at the end.
 constexpr int kStreamWGs = 256;       // one per CU of an MI355X
 constexpr int kStreamMinLds = 81 * 1024;  // > half the CU's LDS: one workgroup per CU
 constexpr int kCandCap = 128;             // candidate slots per wave and row
+
+// Shrinks a wave's candidate buffer B (n keys, K < n <= 128) in place and
+// returns the row's new filter threshold (a key passes when it is greater).
+// The buffer need not hold a sorted top K, only every key that can still be
+// among the row's K best: a bit search over the keys' high words (the order
+// image of the value) takes the first cut that keeps between K and about 2K
+// of them (at most 64), and since at least K keys reach the cut, no key below
+// it can be among the K best.  That costs a handful of ballots; only keys
+// tied in their high word past 64 fall back to the exact selection.
+__device__ __forceinline__ uint64_t shrink_candidates(uint64_t *B, int &n, int K, uint64_t *scratch) {
+    const int lane = lane_id();
+    uint64_t k[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) k[i] = lane + 64 * i < n ? B[lane + 64 * i] : 0ull;
+    // empty slots have high word 0, below every cut
+    const uint32_t h0 = (uint32_t)(k[0] >> 32), h1 = (uint32_t)(k[1] >> 32);
+    const int lim = K <= 16 ? 32 : K <= 32 ? 2 * K : 64;
+    uint32_t v = 0;
+    int c = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t t = v | (1u << b);
+        const int ct = __popcll(__ballot(h0 >= t)) + __popcll(__ballot(h1 >= t));
+        if (ct >= K) {
+            v = t;
+            c = ct;
+            if (ct <= lim) break;
+        }
+    }
+    if (c >= K && c <= 64) {
+        const bool p0 = h0 >= v, p1 = h1 >= v;
+        const unsigned long long m0 = __ballot(p0), m1 = __ballot(p1);
+        const int c0 = __popcll(m0);
+        wave_lds_fence();
+        if (p0) B[lanes_below(m0)] = k[0];
+        if (p1) B[c0 + lanes_below(m1)] = k[1];
+        wave_lds_fence();
+        n = c;
+        return ((uint64_t)v << 32) - 1ull;
+    }
+    const uint64_t top = wave_topk<2>(k, K, scratch);
+    if (lane < K) B[lane] = top;
+    n = K;
+    return readlane_u64(top, K - 1);
+}
 
 template <typename T, int NW, int P>
 __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
@@ -112,21 +157,13 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
 #pragma unroll
     for (int r = 0; r < 8; ++r) cnt[r] = 0;
     uint64_t *myscratch = scratch + wave * 128;
-    // Shrink row r's candidates to its top K and raise its threshold.
+    // Shrink row r's candidates and raise its threshold.
     auto compact = [&](int r) {
-        uint64_t *B = mybuf + r * kCandCap;
-        uint64_t k[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) k[i] = lane + 64 * i < cnt[r] ? B[lane + 64 * i] : 0ull;
-        const uint64_t top = wave_topk<2>(k, K, myscratch);
-        const int kept = cnt[r] < K ? cnt[r] : K;
-        if (lane < K) B[lane] = top;
-        cnt[r] = kept;
-        const uint64_t kth = readlane_u64(top, K - 1);
+        const uint64_t nt = shrink_candidates(mybuf + r * kCandCap, cnt[r], K, myscratch);
         if (q == (r >> 2)) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (e == (r & 3)) thr[e] = kth;
+                if (e == (r & 3)) thr[e] = nt;
         }
     };
     auto row_ptr = [&](int t) -> const T * {
@@ -214,13 +251,31 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
 // copies, so the stream needs no barrier.  Row r of a block holds 16-byte
 // chunk c at position c ^ (r & 7): the 8 lanes of a fragment read hit 8
 // different bank groups.
+//
+// One wave runs per SIMD, so every instruction of the block loop is issue
+// time that the copies cannot hide behind another wave: the loop is unrolled
+// over one turn of the ring (kDmaRing blocks, a tile holds a whole number of
+// turns) so that ring slots, fragment registers and block offsets are all
+// compile-time immediates, and fragments are read two blocks ahead of their
+// MFMAs so that LDS latency is not on the path either.
 constexpr int kDmaWaves = 4;
-constexpr int kDmaRing = 6;        // 2 KB blocks per wave
-constexpr int kDmaCandCap = 128;   // candidate slots per wave and row
+constexpr int kDmaRing = 8;        // 2 KB blocks per wave; H / 64 is a multiple of it
+constexpr int kDmaCandCap = 96;    // candidate slots per wave and row (>= top-K limit + 16)
 
 inline size_t dma_lds_bytes(int H) {
-    return (size_t)H * 16 + (size_t)kDmaWaves * kDmaRing * 2048 + (size_t)kDmaWaves * 8 * kDmaCandCap * 8 +
-           (size_t)kDmaWaves * 128 * 8 + (size_t)kDmaWaves * 8 * 4 + 16;
+    // A fragments (plus a copy of the first two blocks, read ahead across a
+    // tile boundary), rings, candidate buffers, merge scratch, counts
+    return (size_t)(H + 128) * 16 + (size_t)kDmaWaves * kDmaRing * 2048 +
+           (size_t)kDmaWaves * 8 * kDmaCandCap * 8 + (size_t)kDmaWaves * 128 * 8 + (size_t)kDmaWaves * 8 * 4 + 16;
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>) in order
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
@@ -229,9 +284,10 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     uint32_t *__restrict__ status) {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int NW = kDmaWaves, NB = kDmaRing, CAP = kDmaCandCap;
-    const int NBLK = H / 64;  // 2 KB blocks per tile
+    static_assert(NB == 8, "the block loop's waits assume an 8-block ring");
+    const int NBLK = H / 64;  // 2 KB blocks per tile, a multiple of NB
     uint4 *afrag = reinterpret_cast<uint4 *>(smem);
-    uint8_t *rings = smem + (size_t)H * 16;                                         // [NW][NB][2048]
+    uint8_t *rings = smem + (size_t)(H + 128) * 16;                                 // [NW][NB][2048]
     uint64_t *bufs = reinterpret_cast<uint64_t *>(rings + (size_t)NW * NB * 2048);  // [NW][8][CAP]
     uint64_t *scratch = bufs + NW * 8 * CAP;                                        // [NW][128]
     int *cnts = reinterpret_cast<int *>(scratch + NW * 128);                        // [NW][8]
@@ -240,6 +296,8 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     if (blockIdx.x == 0 && threadIdx.x == 0 && status) *status = 0u;
 
     load_afrag<uint16_t>(afrag, h, M, H);
+    __syncthreads();
+    if (threadIdx.x < 128) afrag[H + threadIdx.x] = afrag[threadIdx.x];  // blocks 0, 1 again
     __syncthreads();
 
     // every wave of the grid streams an equal contiguous range of vocabulary
@@ -252,110 +310,125 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     const int n = lane & 15, q = lane >> 4;
     int grow[4];
     uint64_t thr[4];
+    float gval[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int row = 4 * q + e;
         grow[e] = (gold && row < M) ? gold[row] : -1;
         thr[e] = 0ull;
+        gval[e] = 0.f;
     }
+    bool ghit[4] = {false, false, false, false};
     int cnt[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) cnt[r] = 0;
     uint64_t *myscratch = scratch + wave * 128;
     auto compact = [&](int r) {
-        uint64_t *B = mybuf + r * CAP;
-        uint64_t k[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) k[i] = lane + 64 * i < cnt[r] ? B[lane + 64 * i] : 0ull;
-        const uint64_t top = wave_topk<2>(k, K, myscratch);
-        const int kept = cnt[r] < K ? cnt[r] : K;
-        if (lane < K) B[lane] = top;
-        cnt[r] = kept;
-        const uint64_t kth = readlane_u64(top, K - 1);
+        const uint64_t nt = shrink_candidates(mybuf + r * CAP, cnt[r], K, myscratch);
         if (q == (r >> 2)) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (e == (r & 3)) thr[e] = kth;
+                if (e == (r & 3)) thr[e] = nt;
         }
     };
 
     // copies: lane L of copy j of a block fills row 8 j + L / 8, position L % 8,
     // with the row's chunk (L % 8) ^ (row & 7).  Rows past the range read row 0
-    // instead (a few lines per partial tile; every copy is still issued, so the
-    // counted waits stay exact).
+    // instead (a few lines per partial tile).
     uint8_t *ring = rings + (size_t)wave * NB * 2048;
     const uint32_t ring_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)ring;
     const int crow = lane >> 3, cpos = lane & 7;
-    uint32_t roff[2];  // byte offset of this lane's chunk of its two copy rows, block 0
-    auto set_rows = [&](int tile) {
+    // byte offsets of this lane's chunk of its two copy rows of `tile`, block 0
+    auto tile_rows = [&](int tile, uint32_t (&ro)[2]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = 8 * j + crow, vrow = r0 + tile * 16 + row;
-            roff[j] = (uint32_t)((cpos ^ (row & 7)) * 16) + (vrow < r1 ? (uint32_t)vrow * (uint32_t)H * 2u : 0u);
+            ro[j] = (uint32_t)((cpos ^ (row & 7)) * 16) + (vrow < r1 ? (uint32_t)vrow * (uint32_t)H * 2u : 0u);
         }
     };
-    auto copy_block = [&](const uint32_t (&ro)[2], int blk, int slot) {
+    // block `src` + I of the rows `ro` into ring slot I.  The instruction's
+    // immediate offset moves the LDS destination as well as the global
+    // address, so M0 is set that much lower.  `held` are the B fragments last
+    // read from the slot: naming them as inputs makes the compiler wait for
+    // those reads before the copy overwrites it.
+    auto copy_block = [&](const uint32_t (&ro)[2], const uint16_t *src, auto slotc, const uint4 (&held)[2]) {
+        constexpr int I = decltype(slotc)::value;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(ro[j] + (uint32_t)blk * 128u), "s"(w),
-                         "{m0}"(ring_lds + (uint32_t)slot * 2048u + (uint32_t)j * 1024u)
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t dst = ring_lds + (uint32_t)(I * (2048 - 128) + j * 1024);
+            asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2 nt" ::"v"(ro[j]), "s"(src), "n"(I * 128),
+                         "{m0}"(dst), "v"(__builtin_bit_cast(big::u32x4, held[0])),
+                         "v"(__builtin_bit_cast(big::u32x4, held[1]))
                          : "memory");
+        }
     };
-    // fragments of the block in `slot`: B from the ring, A from afrag (rows 8..15
-    // of A only reach output rows 8..15, which are never read)
+    // fragments: B from ring slot I, A from the block that `ablk` points at
+    // (rows 8..15 of A only reach output rows 8..15, which are never read)
     const uint32_t bq0 = (uint32_t)(n * 128 + (((0 + q) ^ (n & 7)) << 4));
     const uint32_t bq1 = (uint32_t)(n * 128 + (((4 + q) ^ (n & 7)) << 4));
     const uint4 *arow = afrag + q * 8 + (n & 7);
-    auto frags = [&](int slot, int blk, uint4 (&fb)[2], uint4 (&fa)[2]) {
-        fb[0] = *reinterpret_cast<const uint4 *>(ring + slot * 2048 + bq0);
-        fb[1] = *reinterpret_cast<const uint4 *>(ring + slot * 2048 + bq1);
-        fa[0] = arow[(2 * blk) * 32];
-        fa[1] = arow[(2 * blk + 1) * 32];
+    auto frags = [&](auto slotc, const uint4 *ablk, uint4 (&fb)[2], uint4 (&fa)[2]) {
+        constexpr int I = decltype(slotc)::value;
+        fb[0] = *reinterpret_cast<const uint4 *>(ring + I * 2048 + bq0);
+        fb[1] = *reinterpret_cast<const uint4 *>(ring + I * 2048 + bq1);
+        fa[0] = ablk[0];
+        fa[1] = ablk[32];
     };
 
-    int t = 0;
     if (ntile > 0) {
-        // The wave's stream of blocks: the ring holds NB consecutive positions.
-        // Position p + b + NB - 1 is copied while block b is in use; block b + 1
-        // is waited for (at most NB - 2 later blocks in flight) and its
-        // fragments read before block b's MFMAs.  Past the last tile the copies
-        // re-read blocks of the last tile into free slots.
+        // Stream position P (tile P / NBLK, block P % NBLK) lives in ring slot
+        // P % NB.  Step I of the turn starting at block g: wait for block
+        // g + I + 2 (the copies of up to five later blocks stay in flight),
+        // read its fragments into buffer (I + 2) % 4, multiply block g + I
+        // from buffer I % 4, then refill slot I (whose fragments are in
+        // registers by then) with block g + I + NB.
         uint32_t cur[2], nxt[2];
-        set_rows(0);
-        cur[0] = roff[0];
-        cur[1] = roff[1];
-        set_rows(ntile > 1 ? 1 : 0);
-        nxt[0] = roff[0];
-        nxt[1] = roff[1];
-#pragma unroll
-        for (int i = 0; i < NB - 1; ++i) copy_block(cur, min(i, NBLK - 1), i);
-        int slot = 0;             // ring slot of the block in use
-        int cslot = NB - 1;       // ring slot of the next copy
-        uint4 fb[2][2], fa[2][2];
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NB - 2)) : "memory");  // block 0 has landed
-        frags(0, 0, fb[0], fa[0]);
-        while (true) {
+        tile_rows(0, cur);
+        tile_rows(ntile > 1 ? 1 : 0, nxt);
+        uint4 fb[4][2], fa[4][2];
+        const uint4 none[2] = {};
+        static_for<NB>([&](auto ic) { copy_block(cur, w, ic, none); });
+        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // blocks 0 and 1 have landed
+        frags(std::integral_constant<int, 0>{}, arow, fb[0], fa[0]);
+        frags(std::integral_constant<int, 1>{}, arow + 64, fb[1], fa[1]);
+        for (int t = 0;; ++t) {
+            const bool last = t + 1 >= ntile;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            // one block: copy ahead, wait for block b + 1, read its fragments
-            // into half CB ^ 1, multiply block b from half CB (NBLK is even, so
-            // the halves alternate with a fixed pattern and the next tile
-            // starts from half 0)
-            auto step = [&](int b, auto cbc) {
-                constexpr int CB = decltype(cbc)::value;
-                const int ahead = b + NB - 1;
-                if (ahead < NBLK) copy_block(cur, ahead, cslot);
-                else copy_block(nxt, min(ahead - NBLK, NBLK - 1), cslot);
-                cslot = cslot + 1 == NB ? 0 : cslot + 1;
-                const int nslot = slot + 1 == NB ? 0 : slot + 1;
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NB - 2)) : "memory");
-                frags(nslot, b + 1 < NBLK ? b + 1 : 0, fb[CB ^ 1], fa[CB ^ 1]);
-                mma16<uint16_t>(acc, fa[CB][0], fb[CB][0]);
-                mma16<uint16_t>(acc, fa[CB][1], fb[CB][1]);
-                slot = nslot;
-            };
-            for (int b = 0; b < NBLK; b += 2) {
-                step(b, std::integral_constant<int, 0>{});
-                step(b + 1, std::integral_constant<int, 1>{});
+            for (int g = 0; g < NBLK; g += NB) {
+                const bool refill_cur = g + NB < NBLK;
+                // the next turn's blocks: this tile's, else the next tile's
+                // first turn, else none (the stream ends with this turn)
+                const uint32_t(&src_ro)[2] = refill_cur ? cur : nxt;
+                const uint16_t *src = w + (refill_cur ? (size_t)(g + NB) * 64 : 0);
+                const uint4 *ablk = arow + (size_t)(g + 2) * 64;
+                if (refill_cur || !last) {
+                    static_for<NB>([&](auto ic) {
+                        constexpr int I = decltype(ic)::value;
+                        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+                        frags(std::integral_constant<int, (I + 2) % NB>{}, ablk + I * 64, fb[(I + 2) % 4],
+                              fa[(I + 2) % 4]);
+                        mma16<uint16_t>(acc, fa[I % 4][0], fb[I % 4][0]);
+                        mma16<uint16_t>(acc, fa[I % 4][1], fb[I % 4][1]);
+                        copy_block(src_ro, src, ic, fb[I % 4]);
+                        // keep each step's instructions together: the scheduler
+                        // would otherwise pull every MFMA up to the reads of
+                        // its own fragments
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                } else {
+                    // final turn: no refills, so fewer copies trail each wait
+                    static_for<NB>([&](auto ic) {
+                        constexpr int I = decltype(ic)::value;
+                        if constexpr (I < 6) {
+                            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (5 - I)) : "memory");
+                            frags(std::integral_constant<int, (I + 2) % NB>{}, ablk + I * 64, fb[(I + 2) % 4],
+                                  fa[(I + 2) % 4]);
+                        }
+                        mma16<uint16_t>(acc, fa[I % 4][0], fb[I % 4][0]);
+                        mma16<uint16_t>(acc, fa[I % 4][1], fb[I % 4][1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                }
             }
             const int v = r0 + t * 16 + n;
 #pragma unroll
@@ -363,7 +436,10 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
                 const int row = 4 * q + e;
                 const bool ok = row < M && v < r1;
                 const uint64_t key = ok ? make_key(acc[e], (uint32_t)v) : 0ull;
-                if (ok && grow[e] == v) gold_logit[row] = acc[e];
+                if (ok && grow[e] == v) {
+                    gval[e] = acc[e];
+                    ghit[e] = true;
+                }
                 const bool pass = key > thr[e];
                 const unsigned long long mask = __ballot(pass);
                 const int c0 = __popcll(mask & 0xffffull), c1 = __popcll(mask & 0xffff0000ull);
@@ -374,22 +450,19 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
                 cnt[e] += c0;
                 cnt[4 + e] += c1;
             }
-            // (a gold store is a vector-memory op too: let it drain so the ring's
-            // counted waits above stay exact)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NB - 2)) : "memory");
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 if (cnt[r] > CAP - 16) compact(r);
-            if (t + 1 >= ntile) break;
-            ++t;
+            if (last) break;
             cur[0] = nxt[0];
             cur[1] = nxt[1];
-            set_rows(t + 1 < ntile ? t + 1 : t);
-            nxt[0] = roff[0];
-            nxt[1] = roff[1];
+            tile_rows(t + 2 < ntile ? t + 2 : t + 1, nxt);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (ghit[e]) gold_logit[4 * q + e] = gval[e];
     if (lane < 8) {
 #pragma unroll
         for (int r = 0; r < 8; ++r)
@@ -951,9 +1024,9 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
     const int nw = 8;
     size_t stream_lds = (size_t)S * 32 * 16 + (size_t)nw * (8 * kCandCap + 128) * 8 + (size_t)nw * 8 * 4 + 16;
     if (stream_lds < (size_t)kStreamMinLds) stream_lds = kStreamMinLds;
-    if (dtype != 0 && M <= kStreamMaxRows && H % 128 == 0 && H / 64 >= kDmaRing - 1 && dma_lds_bytes(H) <= 160 * 1024 &&
+    if (dtype != 0 && M <= kStreamMaxRows && H % (64 * kDmaRing) == 0 && dma_lds_bytes(H) <= 160 * 1024 &&
         (uint64_t)V * H * 2 < (1ull << 32)) {
-        // weights through LDS (the ring's look-ahead stays within the next tile)
+        // weights through LDS
         p.streaming = true;
         p.dma = true;
         p.n_tiles = (V + 15) / 16;

@@ -105,6 +105,9 @@ TOPK_CASES = [
     (8, 256, 4096, 1, "f32"), (3, 256, 2000, 16, "f32"), (8, 1024, 20000, 16, "bf16"),
     (9, 256, 3000, 16, "bf16"), (128, 256, 4096, 16, "f32"), (300, 256, 5000, 64, "bf16"),
     (130, 512, 2999, 7, "bf16"), (64, 256, 16, 16, "bf16"),
+    # bf16, N <= 8, H a multiple of 512: weights streamed through LDS; several
+    # ring turns per tile and several tiles per wave, ragged per-wave ranges
+    (8, 4096, 30011, 16, "bf16"), (1, 4096, 5003, 64, "bf16"), (3, 2048, 70001, 5, "bf16"),
 ]
 
 
