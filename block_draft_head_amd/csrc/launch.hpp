@@ -18,6 +18,7 @@ constexpr uint32_t kStatusIdRange = 1u;
 struct LmheadPlan {
     bool streaming, big;  // big: 256 x 256 bf16 MFMA tiles (many rows)
     bool dma;             // streaming, weights copied into LDS (bf16, at most 8 rows)
+    int ksplit;           // dma: waves sharing each tile (each multiplies 1 / ksplit of H)
     int n_mt;
     int nw, prefetch, n_tiles;
     int grid_x, grid_y, n_lists;

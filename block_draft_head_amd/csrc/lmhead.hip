@@ -240,33 +240,51 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
 
 // ---------------------------------------------------------------- streaming through LDS (bf16)
 //
-// The same work split and epilogue as lmhead_stream_kernel, but the weight
-// rows reach the MFMAs through LDS: each wave copies 2 KB blocks (16
-// vocabulary rows x 64 k) from HBM straight into a private ring of kDmaRing
-// LDS blocks with non-temporal global_load_lds_dwordx4 (each instruction
-// reads 8 whole 128-byte lines), and reads its B fragments from there.
-// Streaming a weight this way reads HBM about 12% faster than loading it
-// into registers (the register loads read 64 bytes of 16 rows each, which
-// the non-temporal policy cannot serve well).  A wave waits only for its own
-// copies, so the stream needs no barrier.  Row r of a block holds 16-byte
-// chunk c at position c ^ (r & 7): the 8 lanes of a fragment read hit 8
-// different bank groups.
+// The same job as lmhead_stream_kernel, with the weight rows reaching the
+// MFMAs through LDS: each wave copies 2 KB blocks (16 vocabulary rows x 64 k)
+// from HBM straight into a private ring of kDmaRing LDS blocks with
+// non-temporal global_load_lds_dwordx4 (each instruction reads 8 whole
+// 128-byte lines) and reads its B fragments from there.  Streaming a weight
+// this way reads HBM about 12% faster than loading it into registers (the
+// register loads read 64 bytes of 16 rows each, which the non-temporal
+// policy cannot serve well).  Row r of a block holds 16-byte chunk c at
+// position c ^ (r & 7): the 8 lanes of a fragment read hit 8 bank groups.
+//
+// Work split: workgroup b owns an equal contiguous range of vocabulary rows,
+// cut into 16-row tiles.  Its waves form groups of KS that share a tile, wave
+// p of a group multiplying k-blocks [p Q, p Q + Q) (Q = H / 64 / KS): the
+// workgroup then reads its rows close together, which streams HBM a few
+// percent faster than one 16-row tile per wave.  A group sums its partial
+// tiles through LDS (one barrier per tile) and each wave filters the logits
+// of the rows 4 q + e with e % KS == p into its own candidate buffers.
 //
 // One wave runs per SIMD, so every instruction of the block loop is issue
 // time that the copies cannot hide behind another wave: the loop is unrolled
-// over one turn of the ring (kDmaRing blocks, a tile holds a whole number of
-// turns) so that ring slots, fragment registers and block offsets are all
-// compile-time immediates, and fragments are read two blocks ahead of their
-// MFMAs so that LDS latency is not on the path either.
+// over one turn of the ring (a wave's share of a tile holds whole turns) so
+// that ring slots, fragment registers and block offsets are compile-time
+// immediates, and fragments are read ahead of their MFMAs so that LDS
+// latency is not on the path either.  A wave waits only for its own copies
+// (counted waits), and the group barrier waits for LDS alone, so the copy
+// stream never drains inside the kernel.
 constexpr int kDmaWaves = 4;
-constexpr int kDmaRing = 8;        // 2 KB blocks per wave; H / 64 is a multiple of it
+constexpr int kDmaRing = 8;        // 2 KB blocks per wave
 constexpr int kDmaCandCap = 96;    // candidate slots per wave and row (>= top-K limit + 16)
+constexpr int kDmaAhead = 2;       // fragments are read this many blocks before their MFMAs
+constexpr int kDmaLead = 8;        // a block is copied this many blocks before its MFMAs
 
-inline size_t dma_lds_bytes(int H) {
-    // A fragments (plus a copy of the first two blocks, read ahead across a
-    // tile boundary), rings, candidate buffers, merge scratch, counts
-    return (size_t)(H + 128) * 16 + (size_t)kDmaWaves * kDmaRing * 2048 +
-           (size_t)kDmaWaves * 8 * kDmaCandCap * 8 + (size_t)kDmaWaves * 128 * 8 + (size_t)kDmaWaves * 8 * 4 + 16;
+// K split of a tile among the waves that share it: the largest of 4, 2, 1
+// whose share of H holds whole ring turns (0: none does)
+inline int dma_ksplit(int H) {
+    return H % (64 * kDmaRing * 4) == 0 ? 4 : H % (64 * kDmaRing * 2) == 0 ? 2 : H % (64 * kDmaRing) == 0 ? 1 : 0;
+}
+
+inline size_t dma_lds_bytes(int H, int KS) {
+    // A fragments (each K share followed by its first two blocks again, read
+    // ahead across a tile boundary), rings, candidate buffers, two sets of
+    // partial tiles (K split only), merge scratch, counts
+    return (size_t)(H / 64 + 2 * KS) * 1024 + (size_t)kDmaWaves * kDmaRing * 2048 +
+           (size_t)kDmaWaves * (8 / KS) * kDmaCandCap * 8 + (KS > 1 ? (size_t)2 * kDmaWaves * 1024 : 0) +
+           (size_t)kDmaWaves * 128 * 8 + (size_t)kDmaWaves * 8 * 4 + 16;
 }
 
 template <typename F, int... I>
@@ -278,72 +296,92 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// A fragments of h (bf16, at most 8 rows) in load_afrag's order, except that
+// 64-k block b of share p = b / Q sits at block p (Q + 2) + b % Q, and each
+// share is followed by its first two blocks again.
+__device__ void load_afrag_shares(uint4 *afrag, const uint16_t *__restrict__ A, int M, int H, int Q) {
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+        const int m = i & 7, q = (i >> 3) & 3, s = i >> 5;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (m < M) v = *reinterpret_cast<const uint4 *>(A + (size_t)m * H + (size_t)(4 * s + q) * 8);
+        const int b = i >> 6, bl = b % Q;
+        const int dst = ((b / Q) * (Q + 2) + bl) * 64 + (i & 63);
+        afrag[dst] = v;
+        if (bl < 2) afrag[dst + Q * 64] = v;
+    }
+}
+
+template <int KS>
 __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
-    const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K, int n_tiles,
+    const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K,
     const int32_t *__restrict__ gold, float *__restrict__ gold_logit, uint64_t *__restrict__ partial,
     uint32_t *__restrict__ status) {
     extern __shared__ __align__(16) uint8_t smem[];
-    constexpr int NW = kDmaWaves, NB = kDmaRing, CAP = kDmaCandCap;
-    static_assert(NB == 8, "the block loop's waits assume an 8-block ring");
-    const int NBLK = H / 64;  // 2 KB blocks per tile, a multiple of NB
+    constexpr int NW = kDmaWaves, NB = kDmaRing, CAP = kDmaCandCap, AH = kDmaAhead, LD = kDmaLead;
+    constexpr int G = NW / KS;   // wave groups
+    constexpr int OWN = 8 / KS;  // rows whose candidates one wave keeps
+    static_assert(NW % KS == 0 && 4 % KS == 0, "a K split divides the waves and the rows of a lane");
+    static_assert(AH >= 1 && AH <= 2 && AH < LD && LD <= NB && NB % 4 == 0,
+                  "at most two tile-wrapping fragment reads, copies ahead of them, four fragment buffers");
+    const int Q = H / 64 / KS;  // blocks of one K share, a multiple of NB
     uint4 *afrag = reinterpret_cast<uint4 *>(smem);
-    uint8_t *rings = smem + (size_t)(H + 128) * 16;                                 // [NW][NB][2048]
-    uint64_t *bufs = reinterpret_cast<uint64_t *>(rings + (size_t)NW * NB * 2048);  // [NW][8][CAP]
-    uint64_t *scratch = bufs + NW * 8 * CAP;                                        // [NW][128]
-    int *cnts = reinterpret_cast<int *>(scratch + NW * 128);                        // [NW][8]
-    (void)n_tiles;
+    uint8_t *rings = smem + (size_t)(H / 64 + 2 * KS) * 1024;                        // [NW][NB][2048]
+    uint64_t *bufs = reinterpret_cast<uint64_t *>(rings + (size_t)NW * NB * 2048);   // [NW][OWN][CAP]
+    f32x4 *parts = reinterpret_cast<f32x4 *>(bufs + NW * OWN * CAP);                // [2][NW][64]
+    uint64_t *scratch = reinterpret_cast<uint64_t *>(parts + (KS > 1 ? 2 * NW * 64 : 0));  // [NW][128]
+    int *cnts = reinterpret_cast<int *>(scratch + NW * 128);                         // [NW][OWN]
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gi = wave / KS, kp = wave % KS;
     if (blockIdx.x == 0 && threadIdx.x == 0 && status) *status = 0u;
 
-    load_afrag<uint16_t>(afrag, h, M, H);
-    __syncthreads();
-    if (threadIdx.x < 128) afrag[H + threadIdx.x] = afrag[threadIdx.x];  // blocks 0, 1 again
+    load_afrag_shares(afrag, h, M, H, Q);
     __syncthreads();
 
-    // every wave of the grid streams an equal contiguous range of vocabulary
-    // rows (the weight stream is the whole cost, so equal bytes finish
-    // together); its 16-row tiles start at r0, the last one partial
-    const long long nw_all = (long long)gridDim.x * NW, gw = (long long)blockIdx.x * NW + wave;
-    const int r0 = (int)(gw * V / nw_all), r1 = (int)((gw + 1) * V / nw_all);
+    const int r0 = (int)((long long)blockIdx.x * V / gridDim.x);
+    const int r1 = (int)((long long)(blockIdx.x + 1) * V / gridDim.x);
     const int ntile = (r1 - r0 + 15) / 16;
-    uint64_t *mybuf = bufs + wave * 8 * CAP;
+    // group gi takes tiles gi, gi + G, ...; with a K split every wave runs the
+    // same number of iterations (they meet at barriers), a group with one
+    // tile fewer repeating its last tile with no row valid
+    const int nit = KS == 1 ? (ntile - gi + G - 1) / G : (ntile + G - 1) / G;
+    uint64_t *mybuf = bufs + wave * OWN * CAP;
     const int n = lane & 15, q = lane >> 4;
     int grow[4];
     uint64_t thr[4];
     float gval[4];
+    bool ghit[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int row = 4 * q + e;
         grow[e] = (gold && row < M) ? gold[row] : -1;
         thr[e] = 0ull;
         gval[e] = 0.f;
+        ghit[e] = false;
     }
-    bool ghit[4] = {false, false, false, false};
-    int cnt[8];
+    // take the gold ids now: the compiler, which does not count the copies,
+    // would otherwise wait for every load in flight at their first use
 #pragma unroll
-    for (int r = 0; r < 8; ++r) cnt[r] = 0;
+    for (int e = 0; e < 4; ++e) asm volatile("" ::"v"(grow[e]));
+    int cnt[OWN];
+#pragma unroll
+    for (int r = 0; r < OWN; ++r) cnt[r] = 0;
     uint64_t *myscratch = scratch + wave * 128;
-    auto compact = [&](int r) {
-        const uint64_t nt = shrink_candidates(mybuf + r * CAP, cnt[r], K, myscratch);
-        if (q == (r >> 2)) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (e == (r & 3)) thr[e] = nt;
-        }
-    };
 
     // copies: lane L of copy j of a block fills row 8 j + L / 8, position L % 8,
     // with the row's chunk (L % 8) ^ (row & 7).  Rows past the range read row 0
-    // instead (a few lines per partial tile).
+    // instead (a few lines per partial tile, L2 hits).
     uint8_t *ring = rings + (size_t)wave * NB * 2048;
     const uint32_t ring_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)ring;
     const int crow = lane >> 3, cpos = lane & 7;
-    // byte offsets of this lane's chunk of its two copy rows of `tile`, block 0
-    auto tile_rows = [&](int tile, uint32_t (&ro)[2]) {
+    // byte offsets of this lane's chunk of its two copy rows in the tile of
+    // iteration `it`, first block of the wave's K share
+    auto tile_rows = [&](int it, uint32_t (&ro)[2]) {
+        const int ti = min(it * G + gi, ntile - 1);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int row = 8 * j + crow, vrow = r0 + tile * 16 + row;
-            ro[j] = (uint32_t)((cpos ^ (row & 7)) * 16) + (vrow < r1 ? (uint32_t)vrow * (uint32_t)H * 2u : 0u);
+            const int row = 8 * j + crow, vrow = r0 + ti * 16 + row;
+            ro[j] = (uint32_t)((cpos ^ (row & 7)) * 16 + kp * Q * 128) +
+                    (vrow < r1 ? (uint32_t)vrow * (uint32_t)H * 2u : 0u);
         }
     };
     // block `src` + I of the rows `ro` into ring slot I.  The instruction's
@@ -366,7 +404,7 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     // (rows 8..15 of A only reach output rows 8..15, which are never read)
     const uint32_t bq0 = (uint32_t)(n * 128 + (((0 + q) ^ (n & 7)) << 4));
     const uint32_t bq1 = (uint32_t)(n * 128 + (((4 + q) ^ (n & 7)) << 4));
-    const uint4 *arow = afrag + q * 8 + (n & 7);
+    const uint4 *arow = afrag + (size_t)kp * (Q + 2) * 64 + q * 8 + (n & 7);
     auto frags = [&](auto slotc, const uint4 *ablk, uint4 (&fb)[2], uint4 (&fa)[2]) {
         constexpr int I = decltype(slotc)::value;
         fb[0] = *reinterpret_cast<const uint4 *>(ring + I * 2048 + bq0);
@@ -375,66 +413,83 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
         fa[1] = ablk[32];
     };
 
-    if (ntile > 0) {
-        // Stream position P (tile P / NBLK, block P % NBLK) lives in ring slot
-        // P % NB.  Step I of the turn starting at block g: wait for block
-        // g + I + 2 (the copies of up to five later blocks stay in flight),
-        // read its fragments into buffer (I + 2) % 4, multiply block g + I
-        // from buffer I % 4, then refill slot I (whose fragments are in
-        // registers by then) with block g + I + NB.
+    if (nit > 0) {
+        // Stream position P (iteration P / Q, block P % Q of the K share) lives
+        // in ring slot P % NB.  Step I of the turn starting at block g: wait
+        // for block g + I + AH (the copies of the LD - 1 - AH blocks after it
+        // may still be in flight), read its fragments into buffer
+        // (I + AH) % 4, multiply block g + I from buffer I % 4, then copy
+        // block g + I + LD into its slot, whose previous block has been
+        // multiplied by then.
         uint32_t cur[2], nxt[2];
         tile_rows(0, cur);
-        tile_rows(ntile > 1 ? 1 : 0, nxt);
+        tile_rows(nit > 1 ? 1 : 0, nxt);
         uint4 fb[4][2], fa[4][2];
         const uint4 none[2] = {};
-        static_for<NB>([&](auto ic) { copy_block(cur, w, ic, none); });
-        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // blocks 0 and 1 have landed
-        frags(std::integral_constant<int, 0>{}, arow, fb[0], fa[0]);
-        frags(std::integral_constant<int, 1>{}, arow + 64, fb[1], fa[1]);
-        for (int t = 0;; ++t) {
-            const bool last = t + 1 >= ntile;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int g = 0; g < NBLK; g += NB) {
-                const bool refill_cur = g + NB < NBLK;
-                // the next turn's blocks: this tile's, else the next tile's
-                // first turn, else none (the stream ends with this turn)
-                const uint32_t(&src_ro)[2] = refill_cur ? cur : nxt;
-                const uint16_t *src = w + (refill_cur ? (size_t)(g + NB) * 64 : 0);
-                const uint4 *ablk = arow + (size_t)(g + 2) * 64;
-                if (refill_cur || !last) {
-                    static_for<NB>([&](auto ic) {
-                        constexpr int I = decltype(ic)::value;
-                        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-                        frags(std::integral_constant<int, (I + 2) % NB>{}, ablk + I * 64, fb[(I + 2) % 4],
-                              fa[(I + 2) % 4]);
-                        mma16<uint16_t>(acc, fa[I % 4][0], fb[I % 4][0]);
-                        mma16<uint16_t>(acc, fa[I % 4][1], fb[I % 4][1]);
-                        copy_block(src_ro, src, ic, fb[I % 4]);
-                        // keep each step's instructions together: the scheduler
-                        // would otherwise pull every MFMA up to the reads of
-                        // its own fragments
-                        __builtin_amdgcn_sched_barrier(0);
-                    });
-                } else {
-                    // final turn: no refills, so fewer copies trail each wait
-                    static_for<NB>([&](auto ic) {
-                        constexpr int I = decltype(ic)::value;
-                        if constexpr (I < 6) {
-                            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (5 - I)) : "memory");
-                            frags(std::integral_constant<int, (I + 2) % NB>{}, ablk + I * 64, fb[(I + 2) % 4],
-                                  fa[(I + 2) % 4]);
-                        }
-                        mma16<uint16_t>(acc, fa[I % 4][0], fb[I % 4][0]);
-                        mma16<uint16_t>(acc, fa[I % 4][1], fb[I % 4][1]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    });
+        static_for<LD>([&](auto ic) { copy_block(cur, w, ic, none); });
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (LD - AH)) : "memory");  // blocks 0 .. AH-1 have landed
+        static_for<AH>([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            frags(ic, arow + I * 64, fb[I], fa[I]);
+        });
+        // One turn of the ring.  MODE 0: inside an iteration; 1: an
+        // iteration's last turn, whose copies past it take the next tile's
+        // first blocks; 2: the stream's last turn, which copies nothing past it.
+        auto turn = [&](int g, f32x4 &acc, auto modec) {
+            constexpr int MODE = decltype(modec)::value;
+            const uint4 *ablk = arow + (size_t)(g + AH) * 64;
+            static_for<NB>([&](auto ic) {
+                constexpr int I = decltype(ic)::value;
+                constexpr bool wrap = I + LD >= NB;  // the copy's block is in the next turn
+                constexpr int S = wrap ? I + LD - NB : I + LD;
+                // copies that may still be in flight once block g + I + AH has landed
+                constexpr int fly = MODE == 2 ? ((LD - 1 < NB - 1 - I) ? LD - 1 : NB - 1 - I) - AH : LD - 1 - AH;
+                if constexpr (MODE != 2 || I + AH < NB) {
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(fly > 0 ? 2 * fly : 0) : "memory");
+                    frags(std::integral_constant<int, (I + AH) % NB>{}, ablk + I * 64, fb[(I + AH) % 4],
+                          fa[(I + AH) % 4]);
                 }
+                mma16<uint16_t>(acc, fa[I % 4][0], fb[I % 4][0]);
+                mma16<uint16_t>(acc, fa[I % 4][1], fb[I % 4][1]);
+                if constexpr (MODE != 2 || !wrap) {
+                    constexpr bool next_tile = MODE == 1 && wrap;
+                    const uint16_t *src = w + (next_tile ? 0 : (size_t)(g + (wrap ? NB : 0)) * 64);
+                    // with LD == NB the slot is the one just multiplied from
+                    copy_block(next_tile ? nxt : cur, src, std::integral_constant<int, S>{},
+                               LD == NB ? fb[I % 4] : none);
+                }
+                // keep each step's instructions together: the scheduler would
+                // otherwise pull every MFMA up to the reads of its own fragments
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        for (int it = 0;; ++it) {
+            const bool last = it + 1 >= nit;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int g = 0; g < Q - NB; g += NB) turn(g, acc, std::integral_constant<int, 0>{});
+            if (!last) turn(Q - NB, acc, std::integral_constant<int, 1>{});
+            else turn(Q - NB, acc, std::integral_constant<int, 2>{});
+            if constexpr (KS > 1) {
+                // the group's partial tiles, summed in share order by each of
+                // its waves; two sets, so one barrier per tile keeps a set
+                // from being overwritten before every wave has read it.  The
+                // barrier waits for LDS only: the copies stay in flight.
+                f32x4 *set = parts + (it & 1) * NW * 64;
+                set[wave * 64 + lane] = acc;
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                acc = set[(gi * KS) * 64 + lane];
+#pragma unroll
+                for (int p = 1; p < KS; ++p) acc += set[(gi * KS + p) * 64 + lane];
             }
-            const int v = r0 + t * 16 + n;
+            const int ti = it * G + gi;
+            const int v = r0 + ti * 16 + n;
+            const bool vok = ti < ntile && v < r1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                if (e % KS != kp) continue;
                 const int row = 4 * q + e;
-                const bool ok = row < M && v < r1;
+                const int s0 = e / KS, s1 = 4 / KS + e / KS;  // buffers of rows e and 4 + e
+                const bool ok = vok && row < M;
                 const uint64_t key = ok ? make_key(acc[e], (uint32_t)v) : 0ull;
                 if (ok && grow[e] == v) {
                     gval[e] = acc[e];
@@ -445,37 +500,48 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
                 const int c0 = __popcll(mask & 0xffffull), c1 = __popcll(mask & 0xffff0000ull);
                 if (pass) {
                     const int pos = lanes_below(mask) - (q ? c0 : 0);
-                    mybuf[row * CAP + (q ? cnt[4 + e] : cnt[e]) + pos] = key;
+                    mybuf[(q ? s1 : s0) * CAP + (q ? cnt[s1] : cnt[s0]) + pos] = key;
                 }
-                cnt[e] += c0;
-                cnt[4 + e] += c1;
+                cnt[s0] += c0;
+                cnt[s1] += c1;
             }
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (cnt[r] > CAP - 16) compact(r);
+            for (int qq = 0; qq < 2; ++qq) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (e % KS != kp) continue;
+                    const int sl = qq * (4 / KS) + e / KS;
+                    if (cnt[sl] > CAP - 16) {
+                        const uint64_t nt = shrink_candidates(mybuf + sl * CAP, cnt[sl], K, myscratch);
+                        if (q == qq) thr[e] = nt;
+                    }
+                }
+            }
             if (last) break;
             cur[0] = nxt[0];
             cur[1] = nxt[1];
-            tile_rows(t + 2 < ntile ? t + 2 : t + 1, nxt);
+            tile_rows(it + 2 < nit ? it + 2 : it + 1, nxt);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (ghit[e]) gold_logit[4 * q + e] = gval[e];
-    if (lane < 8) {
+    if (lane == 0) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            if (lane == r) cnts[wave * 8 + r] = cnt[r];
+        for (int r = 0; r < OWN; ++r) cnts[wave * OWN + r] = cnt[r];
     }
     __syncthreads();
+    // row 4 q + e: candidates of wave e % KS of every group, buffer
+    // q (4 / KS) + e / KS
     for (int row = wave; row < M; row += NW) {
-        constexpr int R = 2 * NW;
+        constexpr int R = 2 * G;
+        const int e = row & 3, sl = (row >> 2) * (4 / KS) + e / KS;
         uint64_t k[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const int ww = i >> 1, slot = lane + 64 * (i & 1);
-            k[i] = slot < cnts[ww * 8 + row] ? bufs[(ww * 8 + row) * CAP + slot] : 0ull;
+            const int ww = (i >> 1) * KS + e % KS, slot = lane + 64 * (i & 1);
+            k[i] = slot < cnts[ww * OWN + sl] ? bufs[(ww * OWN + sl) * CAP + slot] : 0ull;
         }
         const uint64_t top = wave_topk<R>(k, K, myscratch);
         if (lane < K) partial[((size_t)row * gridDim.x + blockIdx.x) * K + lane] = top;
@@ -1024,16 +1090,18 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
     const int nw = 8;
     size_t stream_lds = (size_t)S * 32 * 16 + (size_t)nw * (8 * kCandCap + 128) * 8 + (size_t)nw * 8 * 4 + 16;
     if (stream_lds < (size_t)kStreamMinLds) stream_lds = kStreamMinLds;
-    if (dtype != 0 && M <= kStreamMaxRows && H % (64 * kDmaRing) == 0 && dma_lds_bytes(H) <= 160 * 1024 &&
+    const int ks = dma_ksplit(H);
+    if (dtype != 0 && M <= kStreamMaxRows && ks > 0 && dma_lds_bytes(H, ks) <= 160 * 1024 &&
         (uint64_t)V * H * 2 < (1ull << 32)) {
         // weights through LDS
         p.streaming = true;
         p.dma = true;
+        p.ksplit = ks;
         p.n_tiles = (V + 15) / 16;
         p.grid_x = p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs;
         p.grid_y = 1;
         p.n_lists = p.grid_x;
-        p.lds = dma_lds_bytes(H);
+        p.lds = dma_lds_bytes(H, ks);
     } else if (M <= kStreamMaxRows && stream_lds <= 160 * 1024) {
         p.streaming = true;
         p.nw = nw;
@@ -1111,11 +1179,16 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
     hipError_t e;
     if (p.dma) {
         if constexpr (sizeof(T) == 2) {
-            if ((e = set_lds(lmhead_dma_kernel, p.lds)) != hipSuccess) return e;
-            hipLaunchKernelGGL(lmhead_dma_kernel, dim3(p.grid_x), dim3(64 * kDmaWaves), p.lds, stream,
-                               (const uint16_t *)h, (const uint16_t *)w, (int)M, H, V, K, p.n_tiles, gold, gold_logit,
-                               partial, status);
-            e = hipGetLastError();
+            auto launch = [&](auto kern) -> hipError_t {
+                hipError_t err = set_lds(kern, p.lds);
+                if (err != hipSuccess) return err;
+                hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(64 * kDmaWaves), p.lds, stream, (const uint16_t *)h,
+                                   (const uint16_t *)w, (int)M, H, V, K, gold, gold_logit, partial, status);
+                return hipGetLastError();
+            };
+            e = p.ksplit == 4 ? launch(lmhead_dma_kernel<4>)
+                : p.ksplit == 2 ? launch(lmhead_dma_kernel<2>)
+                                : launch(lmhead_dma_kernel<1>);
         } else {
             return hipErrorInvalidValue;
         }
