@@ -269,8 +269,8 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
 constexpr int kDmaWaves = 4;
 constexpr int kDmaRing = 8;        // 2 KB blocks per wave
 constexpr int kDmaCandCap = 96;    // candidate slots per wave and row (>= top-K limit + 16)
-constexpr int kDmaAhead = 2;       // fragments are read this many blocks before their MFMAs
-constexpr int kDmaLead = 8;        // a block is copied this many blocks before its MFMAs
+constexpr int kDmaAhead = 1;       // fragments are read this many blocks before their MFMAs
+constexpr int kDmaLead = 5;        // a block is copied this many blocks before its MFMAs (a deeper lead streams slower)
 
 // K split of a tile among the waves that share it: the largest of 4, 2, 1
 // whose share of H holds whole ring turns (0: none does)

@@ -103,8 +103,8 @@ struct EpiStore {  // out[m][col] for col < ncol_total; clears the status word
 
 // Conv prepare.  Tile ct covers groups [ct*Gw, ct*Gw + Gw); tile column
 // c = (s*T + j)*Gw + gl holds c[n, s, j, ct*Gw + gl], i.e. projection row
-// (s*T + j)*G + ct*Gw + gl.
-template <typename T>
+// (s*T + j)*G + ct*Gw + gl.  TMAX bounds the taps at compile time.
+template <typename T, int TMAX>
 struct EpiConv {
     const T *x, *base;
     T *x_out;
@@ -125,6 +125,63 @@ struct EpiConv {
         }
         // input kernel applied block-locally
         const int nc = gn * gs;
+        if constexpr (sizeof(T) == 2) {
+            if (nc % 8 == 0 && (g0 * gs) % 8 == 0) {
+                // One item: 8 channels (a 16-byte chunk) of one row.  A thread
+                // loads every tap operand of IB items before any sum, so the
+                // loads overlap instead of each waiting out its latency; the
+                // sums keep the tap order of the scalar path below.
+                constexpr int IB = TMAX <= 2 ? 4 : TMAX <= 4 ? 2 : 1;
+                const int chunks = nc / 8, items = nrows * chunks, h0 = g0 * gs;
+                for (int i0 = threadIdx.x; i0 < items; i0 += IB * blockDim.x) {
+                    uint4 xv[IB][TMAX], bv[IB][TMAX];
+#pragma unroll
+                    for (int ib = 0; ib < IB; ++ib) {
+                        const int i = i0 + ib * blockDim.x, r = i / chunks, n = m0 + r;
+                        const int hh = h0 + (i % chunks) * 8;
+                        const bool live = i < items && n < M;
+                        const int jmax = live ? min(taps - 1, n % bs) : -1;
+#pragma unroll
+                        for (int j = 0; j < TMAX; ++j) {
+                            const bool ok = j <= jmax;
+                            xv[ib][j] = ok ? *reinterpret_cast<const uint4 *>(x + (size_t)(n - j) * H + hh)
+                                           : make_uint4(0u, 0u, 0u, 0u);
+                            bv[ib][j] = ok ? *reinterpret_cast<const uint4 *>(base + (size_t)j * H + hh)
+                                           : make_uint4(0u, 0u, 0u, 0u);
+                        }
+                    }
+#pragma unroll
+                    for (int ib = 0; ib < IB; ++ib) {
+                        const int i = i0 + ib * blockDim.x, r = i / chunks, n = m0 + r, ch = i % chunks;
+                        if (i >= items || n >= M) continue;
+                        const int jmax = min(taps - 1, n % bs);
+                        float acc[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+                        for (int j = 0; j < TMAX; ++j) {
+                            if (j > jmax) break;
+                            const uint32_t xw[4] = {xv[ib][j].x, xv[ib][j].y, xv[ib][j].z, xv[ib][j].w};
+                            const uint32_t bw[4] = {bv[ib][j].x, bv[ib][j].y, bv[ib][j].z, bv[ib][j].w};
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const float xf = bf16_to_f32((xw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                                const float bf = bf16_to_f32((bw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                                const int gl = (ch * 8 + e) / gs;
+                                acc[e] = fmaf(bf + C[r * cs + j * Gw + gl], xf, acc[e]);
+                            }
+                        }
+                        uint32_t ow[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            ow[e] = (uint32_t)f32_to_bf16(acc[2 * e]) | ((uint32_t)f32_to_bf16(acc[2 * e + 1]) << 16);
+                        *reinterpret_cast<uint4 *>(x_out + (size_t)n * H + h0 + ch * 8) =
+                            make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                    }
+                }
+                return;
+            }
+        }
         for (int i = threadIdx.x; i < nrows * nc; i += blockDim.x) {
             const int r = i / nc, hc = i % nc;
             const int n = m0 + r;
@@ -164,7 +221,145 @@ __global__ __launch_bounds__(256) void proj_tiled_kernel(const T *__restrict__ A
     epi(C, Cfg::CSTRIDE, m0, min(Cfg::BM, M - m0), ct, Cfg::BN);
 }
 
+// ------------------------------------------------------------ DMA-fed tiles (bf16)
+//
+// The same tiles for bf16 operands with a deep pipeline: the k loop walks
+// 64-element stages through a ring of NS LDS stages that global_load_lds
+// fills directly, NS - 1 stages ahead, so a workgroup's loads are not
+// serialised behind its MFMAs (the projections have few output tiles, and a
+// tile that waits out each load's latency leaves HBM idle).  Each wave waits
+// for its own copies (counted waits) and one barrier per stage publishes
+// them; the barrier waits for LDS only, so the later stages stay in flight.
+// Row r of a stage holds 16-byte chunk c at position c ^ (r & 7): the rows
+// one fragment read touches fall on distinct bank groups.
+template <int BM_, int BN_, int NS_>
+struct DmaTileCfg {
+    static constexpr int BM = BM_, BN = BN_, NS = NS_;
+    static constexpr int ROWS = BM + BN;
+    static constexpr int STAGE = ROWS * 128;     // bytes: 64 k of every row
+    static constexpr int CPW = ROWS / 32;        // 8-row copies per wave and stage
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int TM = WM / 16, TN = WN / 16;
+    static constexpr int CSTRIDE = BN + 4;
+    static constexpr int CTILE_BYTES = BM * CSTRIDE * 4;
+    static constexpr int LDS = NS * STAGE > CTILE_BYTES ? NS * STAGE : CTILE_BYTES;
+    static_assert(ROWS % 32 == 0 && TM >= 1 && TN >= 1 && NS >= 3, "tile shape");
+};
+
+// (row tile, column tile) of workgroup `bid` of n_rt * n_ct.  Workgroups are
+// dispatched to the 8 XCDs in turn; each XCD takes a contiguous range of
+// tiles, walked in bands of up to kProjBandRows row tiles, column by column,
+// so the workgroups that run together on an XCD share A rows and W rows in
+// its L2 instead of each XCD re-reading every row tile.
+constexpr int kProjBandRows = 4;
+__device__ __forceinline__ void proj_tile_of(int bid, int n_rt, int n_ct, int &rt, int &ct) {
+    const int n = n_rt * n_ct;
+    const int L = n % 8 == 0 ? (bid & 7) * (n >> 3) + (bid >> 3) : bid;
+    int SM = kProjBandRows;
+    while (n_rt % SM != 0) SM >>= 1;
+    const int band = L / (SM * n_ct), rem = L % (SM * n_ct);
+    ct = rem / SM;
+    rt = band * SM + rem % SM;
+}
+using DmaTileBig = DmaTileCfg<64, 64, 4>;
+using DmaTileSmall = DmaTileCfg<32, 32, 8>;
+
+template <class Cfg, class Epi>
+__global__ __launch_bounds__(256) void proj_dma_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
+                                                       int M, int H, int n_ct, Epi epi) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int NS = Cfg::NS, CPW = Cfg::CPW;
+    int rt, ct;
+    proj_tile_of(blockIdx.x, (M + Cfg::BM - 1) / Cfg::BM, n_ct, rt, ct);
+    const int m0 = rt * Cfg::BM;
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1, n = lane & 15, q = lane >> 4;
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)smem;
+    // this lane's chunk of each of its copies: stage row (wave CPW + c) 8 + L / 8
+    // (A rows, then W rows), chunk (L % 8) ^ (row % 8).  Rows past M or past
+    // the projection read row 0; their outputs are never used.
+    const uint8_t *src[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int row = (wave * CPW + c) * 8 + (lane >> 3);
+        const uint16_t *rp;
+        if (row < Cfg::BM) {
+            const int r = m0 + row;
+            rp = A + (size_t)(r < M ? r : 0) * H;
+        } else {
+            const int wr = epi.col_row(ct, row - Cfg::BM, Cfg::BN);
+            rp = W + (size_t)(wr >= 0 ? wr : 0) * H;
+        }
+        src[c] = reinterpret_cast<const uint8_t *>(rp) + (((lane & 7) ^ (row & 7)) << 4);
+    }
+    const int nk = H / 64;
+    // stage s (the last one again past the end) into slot s % NS
+    auto issue = [&](int s) {
+        const size_t kb = (size_t)(s < nk ? s : nk - 1) * 128;
+        const uint32_t base = lds0 + (uint32_t)((s % NS) * Cfg::STAGE + wave * CPW * 1024);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const uint8_t *p = src[c] + kb;
+            const uint32_t dst = base + (uint32_t)(c * 1024);
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(p), "{m0}"(dst) : "memory");
+        }
+    };
+    f32x4 acc[Cfg::TM][Cfg::TN];
+#pragma unroll
+    for (int a = 0; a < Cfg::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < NS - 1; ++s) issue(s);
+    for (int s = 0; s < nk; ++s) {
+        // stage s has landed (the NS - 2 after it may still fly) in every wave,
+        // and every wave has finished reading stage s - 1, whose slot is refilled
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(CPW * (NS - 2)) : "memory");
+        issue(s + NS - 1);
+        const uint8_t *st = smem + (s % NS) * Cfg::STAGE;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int pos = ((ks * 4 + q) ^ (n & 7)) << 4;
+            uint4 fa[Cfg::TM], fb[Cfg::TN];
+#pragma unroll
+            for (int a = 0; a < Cfg::TM; ++a)
+                fa[a] = *reinterpret_cast<const uint4 *>(st + (wm * Cfg::WM + a * 16 + n) * 128 + pos);
+#pragma unroll
+            for (int b = 0; b < Cfg::TN; ++b)
+                fb[b] = *reinterpret_cast<const uint4 *>(st + (Cfg::BM + wn * Cfg::WN + b * 16 + n) * 128 + pos);
+#pragma unroll
+            for (int a = 0; a < Cfg::TM; ++a)
+#pragma unroll
+                for (int b = 0; b < Cfg::TN; ++b) mma16<uint16_t>(acc[a][b], fa[a], fb[b]);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float *C = reinterpret_cast<float *>(smem);
+    tiled_store_c<Cfg>(C, acc);
+    __syncthreads();
+    epi(C, Cfg::CSTRIDE, m0, min(Cfg::BM, M - m0), ct, Cfg::BN);
+}
+
 // ------------------------------------------------------------ host side
+
+template <class Cfg, class Epi>
+static hipError_t run_proj_dma(int64_t M, int H, int n_col_tiles, const void *A, const void *W, const Epi &epi,
+                               hipStream_t stream) {
+    auto kern = proj_dma_kernel<Cfg, Epi>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+    if (e != hipSuccess) return e;
+    const int n_rt = (int)((M + Cfg::BM - 1) / Cfg::BM);
+    hipLaunchKernelGGL(kern, dim3(n_rt * n_col_tiles), dim3(256), Cfg::LDS, stream, (const uint16_t *)A,
+                       (const uint16_t *)W, (int)M, H, n_col_tiles, epi);
+    return hipGetLastError();
+}
+
+// The largest tile whose grid still fills the chip: larger tiles read fewer
+// bytes per MFMA, and a workgroup's stream rate is bounded by the bytes its
+// ring keeps in flight.
+template <class Cfg> static bool proj_fills(int64_t M, int n_col_tiles) {
+    return (M + Cfg::BM - 1) / Cfg::BM * n_col_tiles >= 256;
+}
 
 template <typename T, class Epi>
 static hipError_t run_proj_tiled(int64_t M, int H, int n_col_tiles, const void *A, const void *W, const Epi &epi,
@@ -178,6 +373,27 @@ static hipError_t run_proj_tiled(int64_t M, int H, int n_col_tiles, const void *
     hipLaunchKernelGGL(kern, dim3(n_col_tiles, (unsigned)((M + kProjTile - 1) / kProjTile)), dim3(256), lds, stream,
                        (const T *)A, (const T *)W, (int)M, H, epi);
     return hipGetLastError();
+}
+
+template <typename T, int TMAX>
+static hipError_t run_conv_tiles(int64_t N, int bs, int H, int taps, int gs, const void *x, const void *w_proj,
+                                 const void *base, void *x_out, float *k_post, hipStream_t stream) {
+    const int G = H / gs;
+    EpiConv<T, TMAX> epi{(const T *)x, (const T *)base, (T *)x_out, k_post, (int)N, H, bs, taps, gs, G, 0};
+    if constexpr (sizeof(T) == 2) {
+        // Gw groups per tile: the 2 T projection rows of each
+        auto run = [&](auto cfg) -> hipError_t {
+            using Cfg = decltype(cfg);
+            epi.Gw = Cfg::BN / (2 * taps);
+            return run_proj_dma<Cfg>(N, H, (G + epi.Gw - 1) / epi.Gw, x, w_proj, epi, stream);
+        };
+        auto n_ct = [&](int bn) { return (G + bn / (2 * taps) - 1) / (bn / (2 * taps)); };
+        if (proj_fills<DmaTileBig>(N, n_ct(DmaTileBig::BN))) return run(DmaTileBig{});
+        return run(DmaTileSmall{});
+    }
+    epi.Gw = kProjTile / (2 * taps);
+    const int n_ct = (G + epi.Gw - 1) / epi.Gw;
+    return run_proj_tiled<T>(N, H, n_ct, x, w_proj, epi, stream);
 }
 
 template <typename T>
@@ -198,10 +414,10 @@ static hipError_t run_conv_prepare(int64_t N, int bs, int H, int taps, int gs, c
                                (const T *)base, (T *)x_out, k_post, (int)N, H, bs, taps, gs);
         return hipGetLastError();
     }
-    EpiConv<T> epi{(const T *)x, (const T *)base, (T *)x_out, k_post, (int)N, H, bs, taps, gs, G, 0};
-    epi.Gw = kProjTile / (2 * taps);
-    const int n_ct = (G + epi.Gw - 1) / epi.Gw;
-    return run_proj_tiled<T>(N, H, n_ct, x, w_proj, epi, stream);
+    if (taps <= 2) return run_conv_tiles<T, 2>(N, bs, H, taps, gs, x, w_proj, base, x_out, k_post, stream);
+    if (taps <= 4) return run_conv_tiles<T, 4>(N, bs, H, taps, gs, x, w_proj, base, x_out, k_post, stream);
+    if (taps <= 8) return run_conv_tiles<T, 8>(N, bs, H, taps, gs, x, w_proj, base, x_out, k_post, stream);
+    return run_conv_tiles<T, 16>(N, bs, H, taps, gs, x, w_proj, base, x_out, k_post, stream);
 }
 
 hipError_t launch_conv_prepare(int dtype, int64_t N, int bs, int H, int taps, int gs, const void *x,
@@ -220,6 +436,14 @@ static hipError_t run_context_proj(int64_t N, int H, int r, const void *h, const
         return hipGetLastError();
     }
     EpiStore epi{g, (int)N, r, status};
+    if constexpr (sizeof(T) == 2) {
+        auto run = [&](auto cfg) -> hipError_t {
+            using Cfg = decltype(cfg);
+            return run_proj_dma<Cfg>(N, H, (r + Cfg::BN - 1) / Cfg::BN, h, w_h, epi, stream);
+        };
+        if (proj_fills<DmaTileBig>(N, (r + DmaTileBig::BN - 1) / DmaTileBig::BN)) return run(DmaTileBig{});
+        return run(DmaTileSmall{});
+    }
     return run_proj_tiled<T>(N, H, (r + kProjTile - 1) / kProjTile, h, w_h, epi, stream);
 }
 

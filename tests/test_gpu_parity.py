@@ -38,6 +38,8 @@ CONV_CASES = [
     (1, 4, 256, 1, 64, "bf16"), (1, 8, 256, 8, 32, "bf16"),
     (17, 8, 256, 2, 16, "bf16"), (17, 8, 256, 2, 16, "f32"), (9, 16, 384, 8, 32, "bf16"),
     (40, 4, 256, 3, 4, "bf16"), (5, 16, 256, 16, 16, "bf16"),
+    # bf16 grids of 64 x 64 tiles (at least 256 of them), tap bounds 2, 4, 8
+    (512, 8, 1024, 2, 8, "bf16"), (256, 16, 1024, 4, 8, "bf16"), (128, 16, 1024, 8, 32, "bf16"),
 ]
 
 
