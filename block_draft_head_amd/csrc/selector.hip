@@ -43,28 +43,37 @@ __device__ __forceinline__ void split_bf16x8(const float (&v)[8], uint4 &hi, uin
 // candidate cid (row l % 16) and predecessor pid (column l % 16); a negative
 // id is a zero row/column.  r is a multiple of 8; grow is the context row (r
 // floats, global memory or LDS).  The rank index is visited 32 at a time (8
-// per lane group); a batch of steps (256 ranks of bf16, 128 of float32) has
-// all of its gathers and context loads issued before its MFMAs.
+// per lane group).  pair_tiles forms NJ such tiles over the same
+// predecessors (tile j from candidates cid[j]): the predecessor rows and the
+// context are loaded and multiplied once for all of them, and a batch of
+// steps (as many as keep its operands within about 128 registers) has all of
+// its gathers and context loads issued before its MFMAs.
 //   bf16 codebooks: the B rows enter a bf16 MFMA exactly; A(a) * g is split
 //   into bf16 high and low parts (relative error below 2^-15), two 16x16x32
 //   MFMAs per step, summed in two accumulators.
 //   float32 codebooks: 16x16x4 float32 MFMAs, element e of a step feeding
 //   accumulator e % 4.
-// Every caller visits the same order, so equal inputs give bit-equal tiles.
-// acc[i] of lane l is P[4 * (l / 16) + i][l % 16].
-template <typename T>
-__device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__restrict__ B,
-                                           const float *grow, int pid, int cid, int r) {
-    constexpr int S = sizeof(T) == 2 ? 8 : 4;
+// A tile's MFMAs run in the same order whatever NJ and the batch size, so
+// equal inputs give bit-equal tiles in every caller.
+// P[j][i] of lane l is tile j's P[4 * (l / 16) + i][l % 16].
+template <typename T, int NJ>
+__device__ __forceinline__ void pair_tiles(const T *__restrict__ A, const T *__restrict__ B, const float *grow,
+                                           int pid, const int (&cid)[NJ], int r, f32x4 (&P)[NJ]) {
     constexpr int W = kWords8<T>;
+    constexpr int PER = 4 * W * (1 + NJ) + 8;  // registers of one step's operands
+    constexpr int S = 128 / PER >= 8 ? 8 : 128 / PER >= 4 ? 4 : 128 / PER >= 2 ? 2 : 1;
     const int q = lane_id() >> 4;
     const T *arow = pid >= 0 ? A + (size_t)pid * r : nullptr;
-    const T *brow = cid >= 0 ? B + (size_t)cid * r : nullptr;
-    f32x4 acc[4];
+    const T *brow[NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) brow[j] = cid[j] >= 0 ? B + (size_t)cid[j] * r : nullptr;
+    f32x4 acc[NJ][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int rho0 = 0; rho0 < r; rho0 += 32 * S) {
-        uint4 ra[S][W], rb[S][W];
+        uint4 ra[S][W], rb[S][NJ][W];
         float gg[S][8];
 #pragma unroll
         for (int u = 0; u < S; ++u) {
@@ -73,7 +82,10 @@ __device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__r
 #pragma unroll
             for (int i = 0; i < W; ++i) {
                 ra[u][i] = (in && arow) ? reinterpret_cast<const uint4 *>(arow + rho)[i] : make_uint4(0u, 0u, 0u, 0u);
-                rb[u][i] = (in && brow) ? reinterpret_cast<const uint4 *>(brow + rho)[i] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    rb[u][j][i] =
+                        (in && brow[j]) ? reinterpret_cast<const uint4 *>(brow[j] + rho)[i] : make_uint4(0u, 0u, 0u, 0u);
             }
             const float4 g0 = in ? reinterpret_cast<const float4 *>(grow + rho)[0] : make_float4(0.f, 0.f, 0.f, 0.f);
             const float4 g1 = in ? reinterpret_cast<const float4 *>(grow + rho)[1] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -89,17 +101,33 @@ __device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__r
             if constexpr (sizeof(T) == 2) {
                 uint4 hi, lo;
                 split_bf16x8(ag, hi, lo);
-                mma16<uint16_t>(acc[0], rb[u][0], hi);
-                mma16<uint16_t>(acc[1], rb[u][0], lo);
-            } else {
-                float b[8];
-                unpack_words8(rb[u], b);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) mma16_f32x1(acc[e & 3], b[e], ag[e]);
+                for (int j = 0; j < NJ; ++j) {
+                    mma16<uint16_t>(acc[j][0], rb[u][j][0], hi);
+                    mma16<uint16_t>(acc[j][1], rb[u][j][0], lo);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    float b[8];
+                    unpack_words8(rb[u][j], b);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mma16_f32x1(acc[j][e & 3], b[e], ag[e]);
+                }
             }
         }
     }
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) P[j] = (acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3]);
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__restrict__ B, const float *grow,
+                                           int pid, int cid, int r) {
+    const int c[1] = {cid};
+    f32x4 P[1];
+    pair_tiles<T, 1>(A, B, grow, pid, c, r, P);
+    return P[0];
 }
 
 // ------------------------------------------------------------------ walk
@@ -110,8 +138,8 @@ __device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__r
 // key (score, lowest slot on ties) in LDS.  Wave 0 then chases the pointers:
 // the keys of 8 positions at a time sit in its registers (lane = slot) and
 // each step is a register read-lane.
-// LDS (walk_lds_bytes): best [bs][K] u64, ids [bs][K] int.
-template <typename T>
+// LDS (walk_lds_bytes): best [bs][K] u64, ids [bs][K] int.  NJ = ceil(K / 16).
+template <typename T, int NJ>
 __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *__restrict__ g, const T *__restrict__ A,
                            const T *__restrict__ B, const int32_t *__restrict__ cand_ids,
                            const float *__restrict__ cand_vals, const int32_t *__restrict__ anchors, int bs,
@@ -121,7 +149,7 @@ __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *_
     int32_t *cids = reinterpret_cast<int32_t *>(best + bs * K);
     const int lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int q = lane >> 4, c = lane & 15;
-    const int n_it = (K + 15) / 16, n_jt = n_it;
+    const int n_it = NJ;
     const int n_items = bs >= 2 ? 1 + (bs - 2) * n_it : 0;
     const size_t row0 = (size_t)blk * bs;
     const int anchor = anchors[blk];
@@ -146,20 +174,39 @@ __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *_
                 if (pid < 0 || pid >= V) pid = -1;  // flagged when its own row is scored
             }
         }
-        uint64_t bestkey = 0;
-        for (int jt = 0; jt < n_jt; ++jt) {
+        // every successor tile at once: ids and unary values first, then one
+        // pass over the rank for all NJ tiles
+        int cid[NJ];
+        bool cok[NJ];
+        float uv[NJ][4];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
             const int j = jt * 16 + c;
-            int cid = j < K ? cand_ids[n * K + j] : -1;
-            bool cok = j < K && cid >= 0 && cid < V;
-            if (j < K && !cok) flag_status(status, kStatusIdRange);
-            if (!cok) cid = -1;
-            const f32x4 P = pair_tile<T>(A, B, g + n * r, pid, cid, r);
+            cid[jt] = j < K ? cand_ids[n * K + j] : -1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int jj = jt * 16 + 4 * q + i;
+                uv[jt][i] = jj < K ? cand_vals[n * K + jj] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            const int j = jt * 16 + c;
+            cok[jt] = j < K && cid[jt] >= 0 && cid[jt] < V;
+            if (j < K && !cok[jt]) flag_status(status, kStatusIdRange);
+            if (!cok[jt]) cid[jt] = -1;
+        }
+        f32x4 P[NJ];
+        pair_tiles<T, NJ>(A, B, g + n * r, pid, cid, r, P);
+        uint64_t bestkey = 0;
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
             uint64_t local = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int jj = jt * 16 + 4 * q + i;
-                const bool ok = __shfl((int)cok, 4 * q + i) != 0;
-                const float s = jj < K ? cand_vals[n * K + jj] + P[i] : 0.f;
+                const bool ok = __shfl((int)cok[jt], 4 * q + i) != 0;
+                const float s = jj < K ? uv[jt][i] + P[jt][i] : 0.f;
                 const uint64_t key = (ok && pid >= 0) ? make_key(s, (uint32_t)jj) : 0ull;
                 local = key > local ? key : local;
             }
@@ -203,14 +250,15 @@ __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *_
     }
 }
 
-template <typename T>
+template <typename T, int NJ>
 __global__ __launch_bounds__(512) void selector_walk_kernel(
     const float *__restrict__ g, const T *__restrict__ A, const T *__restrict__ B,
     const int32_t *__restrict__ cand_ids, const float *__restrict__ cand_vals,
     const int32_t *__restrict__ anchors, int bs, int V, int r, int K, int32_t *__restrict__ path,
     float *__restrict__ path_score, uint32_t *__restrict__ status) {
     extern __shared__ __align__(16) uint8_t wsm[];
-    walk_block<T>(blockIdx.x, wsm, g, A, B, cand_ids, cand_vals, anchors, bs, V, r, K, path, path_score, status);
+    walk_block<T, NJ>(blockIdx.x, wsm, g, A, B, cand_ids, cand_vals, anchors, bs, V, r, K, path, path_score,
+                      status);
 }
 
 // ------------------------------------------------------------------ teacher forcing
@@ -303,21 +351,27 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
     const int items = bs >= 2 ? 1 + (bs - 2) * n_it : 1;
     int waves = items < 8 ? items : 8;
     const dim3 block(64 * waves);
-    hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void *>(selector_walk_kernel<float>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipError_t b = hipFuncSetAttribute(reinterpret_cast<const void *>(selector_walk_kernel<uint16_t>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (a != hipSuccess) return a;
-    if (b != hipSuccess) return b;
-    if (dtype == 0)
-        hipLaunchKernelGGL(selector_walk_kernel<float>, dim3(n_blocks), block, lds, stream, g,
-                           (const float *)A, (const float *)B, cand_ids, cand_vals, anchors, bs, V, r,
-                           K, path, path_score, status);
-    else
-        hipLaunchKernelGGL(selector_walk_kernel<uint16_t>, dim3(n_blocks), block, lds, stream, g,
-                           (const uint16_t *)A, (const uint16_t *)B, cand_ids, cand_vals, anchors,
-                           bs, V, r, K, path, path_score, status);
-    return hipGetLastError();
+    auto launch = [&](auto kern, const auto *Ap, const auto *Bp) -> hipError_t {
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3(n_blocks), block, lds, stream, g, Ap, Bp, cand_ids, cand_vals, anchors, bs, V,
+                           r, K, path, path_score, status);
+        return hipGetLastError();
+    };
+    // one kernel per successor tile count (K <= 64)
+    if (dtype == 0) {
+        const float *Af = (const float *)A, *Bf = (const float *)B;
+        return n_it == 1 ? launch(selector_walk_kernel<float, 1>, Af, Bf)
+               : n_it == 2 ? launch(selector_walk_kernel<float, 2>, Af, Bf)
+               : n_it == 3 ? launch(selector_walk_kernel<float, 3>, Af, Bf)
+                           : launch(selector_walk_kernel<float, 4>, Af, Bf);
+    }
+    const uint16_t *Ah = (const uint16_t *)A, *Bh = (const uint16_t *)B;
+    return n_it == 1 ? launch(selector_walk_kernel<uint16_t, 1>, Ah, Bh)
+           : n_it == 2 ? launch(selector_walk_kernel<uint16_t, 2>, Ah, Bh)
+           : n_it == 3 ? launch(selector_walk_kernel<uint16_t, 3>, Ah, Bh)
+                       : launch(selector_walk_kernel<uint16_t, 4>, Ah, Bh);
 }
 
 hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
