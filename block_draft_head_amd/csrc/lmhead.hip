@@ -386,7 +386,9 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     };
     // block `src` + I of the rows `ro` into ring slot I.  The instruction's
     // immediate offset moves the LDS destination as well as the global
-    // address, so M0 is set that much lower.  `held` are the B fragments last
+    // address, so M0 is set that much lower.  s_nop 4: the wait states that
+    // an SGPR or M0 written just before needs (the compiler adds none to
+    // inline assembly).  `held` are the B fragments last
     // read from the slot: naming them as inputs makes the compiler wait for
     // those reads before the copy overwrites it.
     auto copy_block = [&](const uint32_t (&ro)[2], const uint16_t *src, auto slotc, const uint4 (&held)[2]) {
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t dst = ring_lds + (uint32_t)(I * (2048 - 128) + j * 1024);
-            asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2 nt" ::"v"(ro[j]), "s"(src), "n"(I * 128),
+            asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 offset:%2 nt" ::"v"(ro[j]), "s"(src), "n"(I * 128),
                          "{m0}"(dst), "v"(__builtin_bit_cast(big::u32x4, held[0])),
                          "v"(__builtin_bit_cast(big::u32x4, held[1]))
                          : "memory");

@@ -301,7 +301,9 @@ __global__ __launch_bounds__(256) void proj_dma_kernel(const uint16_t *__restric
         for (int c = 0; c < CPW; ++c) {
             const uint8_t *p = src[c] + kb;
             const uint32_t dst = base + (uint32_t)(c * 1024);
-            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(p), "{m0}"(dst) : "memory");
+            // (s_nop: the wait state M0 needs after the SALU write before it;
+            // the compiler adds none to inline assembly)
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "{m0}"(dst) : "memory");
         }
     };
     f32x4 acc[Cfg::TM][Cfg::TN];
