@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_1x8_h4096_v151936")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--selector", choices=("greedy", "sample"), default="greedy",
+                    help="walk workloads: greedy walk, or the path sampled from softmax of the same scores "
+                         "(temperature 1, a fixed generator key)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
@@ -165,6 +168,9 @@ def main():
         if tf_mode:
             return D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"],
                                        gold_ids=gold, force=dev["force"], gold_logit=gl, workspace=ws_sel)
+        if args.selector == "sample":
+            return D.selector_sample(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals,
+                                     dev["anchors"], bs, temperature=1.0, seed=0x5EED, workspace=ws_sel)
         return D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"],
                                bs, workspace=ws_sel)
 
@@ -231,7 +237,7 @@ def main():
     op_ms = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(names)}
     tf_ms = op_ms.pop("tf", None)
     replay_ok = None
-    if not tf_mode:
+    if not tf_mode and args.selector == "greedy":  # a sampled path is not the scores' argmax
         _, best, _, _ = op_tf(ids, vals)
         replay_ok = bool(torch.equal(best.view(w.n_blocks, bs)[:, 1:], res[0][:, 1:]))
 
@@ -273,7 +279,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "n_blocks": w.n_blocks, "block_size": bs, "hidden": H, "vocab": V,
-                   "taps": T, "group_size": gs, "rank": r, "top_k": K, "mode": w.mode},
+                   "taps": T, "group_size": gs, "rank": r, "top_k": K, "mode": w.mode,
+                   "selector": "teacher-forced" if tf_mode else args.selector},
         "roofline": roof,
         "ops_ms": op_ms,
         "selector_plus_conv_over_lmhead": (op_ms["conv"] + op_ms["selector"]) / lm_ms,

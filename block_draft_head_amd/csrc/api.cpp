@@ -2,6 +2,7 @@
 // launchers.  Every error the host can detect is returned before anything is
 // enqueued; nothing here allocates or synchronises (except
 // dflash2_read_device_status).
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -169,7 +170,35 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
         return DFLASH2_ERR_ALIAS;
     return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
                                          cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
-                                         out_path_score, workspace, (hipStream_t)stream));
+                                         out_path_score, workspace, (hipStream_t)stream, nullptr));
+}
+
+dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,
+                                       int32_t vocab, int32_t rank, int32_t top_k, const void *h,
+                                       const void *w_h, const void *cb_pred, const void *cb_succ,
+                                       const int32_t *cand_ids, const float *cand_vals,
+                                       const int32_t *anchor_ids, float temperature, uint64_t seed,
+                                       int32_t *out_path, float *out_path_score, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+    if (n_blocks < 1 || block_size < 1) return dtype_ok(dtype) ? DFLASH2_ERR_SHAPE : DFLASH2_ERR_DTYPE;
+    const int64_t N = (int64_t)n_blocks * block_size;
+    dflash2_status s = check_selector(dtype, N, hidden, vocab, rank, top_k);
+    if (s != DFLASH2_OK) return s;
+    if (!(temperature > 0.0f) || !std::isfinite(temperature)) return DFLASH2_ERR_SHAPE;
+    if (block_size > DFLASH2_MAX_BLOCK_SIZE) return DFLASH2_ERR_UNSUPPORTED;
+    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path || !workspace)
+        return DFLASH2_ERR_NULL;
+    if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))
+        return DFLASH2_ERR_WORKSPACE;
+    const size_t np = (size_t)N * 4;
+    if (overlaps(out_path, np, workspace, workspace_bytes) ||
+        (out_path_score && (overlaps(out_path_score, np, workspace, workspace_bytes) ||
+                            overlaps(out_path_score, np, out_path, np))))
+        return DFLASH2_ERR_ALIAS;
+    const SampleParams sp{temperature, seed};
+    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
+                                         cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
+                                         out_path_score, workspace, (hipStream_t)stream, &sp));
 }
 
 dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,

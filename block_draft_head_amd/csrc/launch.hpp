@@ -29,8 +29,15 @@ struct LmheadPlan {
 };
 LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
 
-// LDS of one walk workgroup: the block's best-successor keys and candidate ids.
-inline size_t walk_lds_bytes(int bs, int K) { return (size_t)bs * K * (8 + 4); }
+// LDS of one walk workgroup: the block's best-successor keys, their scores,
+// the candidate ids and (sampling) the noise.
+inline size_t walk_lds_bytes(int bs, int K) { return (size_t)bs * K * (8 + 4 + 4 + 4); }
+
+// Sampling walk: temperature and the generator's 64-bit key.
+struct SampleParams {
+    float temperature;
+    uint64_t seed;
+};
 
 hipError_t launch_conv_prepare(int dtype, int64_t N, int bs, int H, int taps, int gs, const void *x,
                                const void *w_proj, const void *base, void *x_out, float *k_post,
@@ -46,7 +53,7 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
                                 const void *h, const void *w_h, const void *A, const void *B,
                                 const int32_t *cand_ids, const float *cand_vals,
                                 const int32_t *anchors, int32_t *path, float *path_score,
-                                void *workspace, hipStream_t stream);
+                                void *workspace, hipStream_t stream, const SampleParams *sample);
 hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
                               const void *w_h, const void *A, const void *B, const int32_t *cand_ids,
                               const float *cand_vals, const int32_t *pred_ids,

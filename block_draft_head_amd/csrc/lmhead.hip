@@ -896,9 +896,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int vt = vt0; vt < vt1; ++pass) {
         const int v0 = vt * BN, par = pass & 1;
         const bool fresh = vt == vt0;
-        // the tile with the vocabulary's tail takes the exact path too (the
-        // register scan assumes every column real)
-        const bool scan = !fresh && v0 + BN <= V;
+        // The tile with the vocabulary's tail takes the exact path too (the
+        // register scan assumes every column real), and so do a slab's first
+        // KL / 16 tiles: after j tiles a row expects about KL / j hits in the
+        // next, and a tile in which any of its 256 rows overflows the 32
+        // slots would be formed twice, so the register scan starts once
+        // that expectation is down to 16.
+        const bool scan = !fresh && v0 + BN <= V && (vt - vt0) * 16 >= KL;
         store = store || !scan;
         f32x16 acc[4][4];
         mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H, prefilled);

@@ -8,6 +8,8 @@
 // only the final pointer chase is sequential.  Teacher forcing places its one
 // predecessor in column 0 of the same routine, so replaying a walk's own
 // predecessors reproduces the walk's scores bit for bit.
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemv.hpp"
 #include "launch.hpp"
@@ -138,15 +140,51 @@ __device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__r
 // key (score, lowest slot on ties) in LDS.  Wave 0 then chases the pointers:
 // the keys of 8 positions at a time sit in its registers (lane = slot) and
 // each step is a register read-lane.
-// LDS (walk_lds_bytes): best [bs][K] u64, ids [bs][K] int.  NJ = ceil(K / 16).
-template <typename T, int NJ>
+// LDS (walk_lds_bytes): best [bs][K] u64, ids [bs][K] int, best_s [bs][K]
+// float, noise [bs][K] float (sampling).  NJ = ceil(K / 16).
+//
+// SAMPLE: the pick maximises S / temperature + G instead of S, G standard
+// Gumbel noise drawn per (block, position, slot) from Philox4x32-10 (the key
+// order then ranks the noisy scores; the clean S of each predecessor's pick
+// is kept beside its key for the path score).
+//
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds of
+// (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+// lo(M0 c0)), the key advanced by the Weyl increments between rounds; the
+// first output word.
+__device__ __forceinline__ uint32_t philox_first_word(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                     uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c0;
+}
+// Standard Gumbel noise of slot j at position t of block b: -log(-log(u)),
+// u the centred top 24 bits of the first Philox word at counter (j, t, b, 0).
+__device__ __forceinline__ float walk_gumbel(int j, int t, int b, uint32_t k0, uint32_t k1) {
+    const uint32_t x = philox_first_word((uint32_t)j, (uint32_t)t, (uint32_t)b, 0u, k0, k1);
+    const float u = ((float)(x >> 8) + 0.5f) * 0x1p-24f;
+    return -logf(-logf(u));
+}
+
+template <typename T, int NJ, bool SAMPLE>
 __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *__restrict__ g, const T *__restrict__ A,
                            const T *__restrict__ B, const int32_t *__restrict__ cand_ids,
                            const float *__restrict__ cand_vals, const int32_t *__restrict__ anchors, int bs,
                            int V, int r, int K, int32_t *__restrict__ path, float *__restrict__ path_score,
-                           uint32_t *__restrict__ status) {
+                           uint32_t *__restrict__ status, float temperature, uint32_t k0, uint32_t k1) {
     uint64_t *best = reinterpret_cast<uint64_t *>(wsm);
     int32_t *cids = reinterpret_cast<int32_t *>(best + bs * K);
+    float *best_s = reinterpret_cast<float *>(cids + bs * K);
+    float *noise = best_s + bs * K;
     const int lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int q = lane >> 4, c = lane & 15;
     const int n_it = NJ;
@@ -156,6 +194,12 @@ __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *_
     const bool anchor_ok = anchor >= 0 && anchor < V;
     if (!anchor_ok && threadIdx.x == 0) flag_status(status, kStatusIdRange);
     for (int i = threadIdx.x; i < bs * K; i += blockDim.x) cids[i] = cand_ids[row0 * K + i];  // for the chase
+    if constexpr (SAMPLE) {
+        // the block's noise, once per (position, slot): every predecessor of a
+        // position sees the same draws
+        for (int i = threadIdx.x; i < bs * K; i += blockDim.x) noise[i] = walk_gumbel(i % K, i / K, blk, k0, k1);
+        __syncthreads();
+    }
 
     for (int item = wave; item < n_items; item += nwaves) {
         const int t = item == 0 ? 1 : 2 + (item - 1) / n_it;
@@ -198,25 +242,58 @@ __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *_
         }
         f32x4 P[NJ];
         pair_tiles<T, NJ>(A, B, g + n * r, pid, cid, r, P);
+        // noise of this lane's slots
+        float gn[NJ][4];
+        if constexpr (SAMPLE) {
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int jj = jt * 16 + 4 * q + i;
+                    gn[jt][i] = jj < K ? noise[t * K + jj] : 0.f;
+                }
+        }
         uint64_t bestkey = 0;
+        float bests = 0.f;  // S of the best key's slot (sampling)
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
             uint64_t local = 0;
+            float locs = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int jj = jt * 16 + 4 * q + i;
                 const bool ok = __shfl((int)cok[jt], 4 * q + i) != 0;
                 const float s = jj < K ? uv[jt][i] + P[jt][i] : 0.f;
-                const uint64_t key = (ok && pid >= 0) ? make_key(s, (uint32_t)jj) : 0ull;
-                local = key > local ? key : local;
+                float z = s;
+                if constexpr (SAMPLE) z = s / temperature + gn[jt][i];
+                const uint64_t key = (ok && pid >= 0) ? make_key(z, (uint32_t)jj) : 0ull;
+                if (key > local) {
+                    local = key;
+                    locs = s;
+                }
             }
             uint64_t o = shfl_xor_u64(local, 16);
-            local = o > local ? o : local;
+            float os = __shfl_xor(locs, 16);
+            if (o > local) {
+                local = o;
+                locs = os;
+            }
             o = shfl_xor_u64(local, 32);
-            local = o > local ? o : local;
-            bestkey = local > bestkey ? local : bestkey;
+            os = __shfl_xor(locs, 32);
+            if (o > local) {
+                local = o;
+                locs = os;
+            }
+            if (local > bestkey) {
+                bestkey = local;
+                bests = locs;
+            }
         }
-        if (q == 0 && col_used) best[t * K + (t == 1 ? 0 : it * 16 + c)] = bestkey;
+        if (q == 0 && col_used) {
+            const int e = t * K + (t == 1 ? 0 : it * 16 + c);
+            best[e] = bestkey;
+            best_s[e] = bests;
+        }
     }
     __syncthreads();
     if (wave == 0) {
@@ -229,36 +306,39 @@ __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *_
         int slot = 0;  // wave-uniform
         for (int t0 = 1; t0 < bs; t0 += 8) {
             uint64_t kk[8];
+            float ks[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int t = t0 + u;
                 kk[u] = (t < bs && lane < K) ? best[t * K + lane] : 0ull;
+                ks[u] = (t < bs && lane < K) ? best_s[t * K + lane] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int t = t0 + u;
                 if (t >= bs) break;
                 const uint64_t key = alive ? readlane_u64(kk[u], slot) : 0ull;
+                const float sc = __shfl(ks[u], slot);  // S of the pick (the key holds the noisy score when sampling)
                 if (key == 0) alive = false;
                 else slot = (int)key_id(key);
                 if (lane == 0) {
                     path[p0 + t] = alive ? cids[t * K + slot] : -1;
-                    if (path_score) path_score[p0 + t] = alive ? key_val(key) : __builtin_nanf("");
+                    if (path_score) path_score[p0 + t] = alive ? (SAMPLE ? sc : key_val(key)) : __builtin_nanf("");
                 }
             }
         }
     }
 }
 
-template <typename T, int NJ>
+template <typename T, int NJ, bool SAMPLE>
 __global__ __launch_bounds__(512) void selector_walk_kernel(
     const float *__restrict__ g, const T *__restrict__ A, const T *__restrict__ B,
     const int32_t *__restrict__ cand_ids, const float *__restrict__ cand_vals,
     const int32_t *__restrict__ anchors, int bs, int V, int r, int K, int32_t *__restrict__ path,
-    float *__restrict__ path_score, uint32_t *__restrict__ status) {
+    float *__restrict__ path_score, uint32_t *__restrict__ status, float temperature, uint32_t k0, uint32_t k1) {
     extern __shared__ __align__(16) uint8_t wsm[];
-    walk_block<T, NJ>(blockIdx.x, wsm, g, A, B, cand_ids, cand_vals, anchors, bs, V, r, K, path, path_score,
-                      status);
+    walk_block<T, NJ, SAMPLE>(blockIdx.x, wsm, g, A, B, cand_ids, cand_vals, anchors, bs, V, r, K, path,
+                              path_score, status, temperature, k0, k1);
 }
 
 // ------------------------------------------------------------------ teacher forcing
@@ -340,7 +420,7 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
                                 const void *h, const void *w_h, const void *A, const void *B,
                                 const int32_t *cand_ids, const float *cand_vals,
                                 const int32_t *anchors, int32_t *path, float *path_score,
-                                void *workspace, hipStream_t stream) {
+                                void *workspace, hipStream_t stream, const SampleParams *sample) {
     uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
     float *g = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
     const int64_t N = (int64_t)n_blocks * bs;
@@ -351,27 +431,30 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
     const int items = bs >= 2 ? 1 + (bs - 2) * n_it : 1;
     int waves = items < 8 ? items : 8;
     const dim3 block(64 * waves);
+    const float temp = sample ? sample->temperature : 1.f;
+    const uint32_t k0 = sample ? (uint32_t)sample->seed : 0u, k1 = sample ? (uint32_t)(sample->seed >> 32) : 0u;
     auto launch = [&](auto kern, const auto *Ap, const auto *Bp) -> hipError_t {
         hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(kern, dim3(n_blocks), block, lds, stream, g, Ap, Bp, cand_ids, cand_vals, anchors, bs, V,
-                           r, K, path, path_score, status);
+                           r, K, path, path_score, status, temp, k0, k1);
         return hipGetLastError();
     };
-    // one kernel per successor tile count (K <= 64)
-    if (dtype == 0) {
-        const float *Af = (const float *)A, *Bf = (const float *)B;
-        return n_it == 1 ? launch(selector_walk_kernel<float, 1>, Af, Bf)
-               : n_it == 2 ? launch(selector_walk_kernel<float, 2>, Af, Bf)
-               : n_it == 3 ? launch(selector_walk_kernel<float, 3>, Af, Bf)
-                           : launch(selector_walk_kernel<float, 4>, Af, Bf);
-    }
-    const uint16_t *Ah = (const uint16_t *)A, *Bh = (const uint16_t *)B;
-    return n_it == 1 ? launch(selector_walk_kernel<uint16_t, 1>, Ah, Bh)
-           : n_it == 2 ? launch(selector_walk_kernel<uint16_t, 2>, Ah, Bh)
-           : n_it == 3 ? launch(selector_walk_kernel<uint16_t, 3>, Ah, Bh)
-                       : launch(selector_walk_kernel<uint16_t, 4>, Ah, Bh);
+    // one kernel per successor tile count (K <= 64) and mode
+    auto pick = [&](const auto *Ap, const auto *Bp, auto samplec) -> hipError_t {
+        using T = std::remove_cv_t<std::remove_pointer_t<decltype(Ap)>>;
+        constexpr bool S = decltype(samplec)::value;
+        return n_it == 1 ? launch(selector_walk_kernel<T, 1, S>, Ap, Bp)
+               : n_it == 2 ? launch(selector_walk_kernel<T, 2, S>, Ap, Bp)
+               : n_it == 3 ? launch(selector_walk_kernel<T, 3, S>, Ap, Bp)
+                           : launch(selector_walk_kernel<T, 4, S>, Ap, Bp);
+    };
+    auto mode = [&](const auto *Ap, const auto *Bp) -> hipError_t {
+        return sample ? pick(Ap, Bp, std::true_type{}) : pick(Ap, Bp, std::false_type{});
+    };
+    if (dtype == 0) return mode((const float *)A, (const float *)B);
+    return mode((const uint16_t *)A, (const uint16_t *)B);
 }
 
 hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,

@@ -26,7 +26,7 @@ F32, BF16 = 0, 1
 MAX_TOP_K, MAX_TAPS, MAX_BLOCK_SIZE, MAX_RANK = 64, 16, 64, 4096
 
 EXPORTS = ["dflash2_conv_prepare", "dflash2_conv_finish", "dflash2_unary_topk",
-           "dflash2_selector_walk", "dflash2_selector_score_tf", "dflash2_workspace_bytes",
+           "dflash2_selector_walk", "dflash2_selector_sample", "dflash2_selector_score_tf", "dflash2_workspace_bytes",
            "dflash2_status_str", "dflash2_read_device_status", "dflash2_version"]
 
 
@@ -46,6 +46,8 @@ def _load() -> ctypes.CDLL:
         "dflash2_conv_finish": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P],
         "dflash2_unary_topk": [ctypes.c_int, I64, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
         "dflash2_selector_walk": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "dflash2_selector_sample": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P,
+                                    ctypes.c_float, ctypes.c_uint64, P, P, P, SZ, P],
         "dflash2_selector_score_tf": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "dflash2_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "dflash2_status_str": [ctypes.c_int],
@@ -199,6 +201,31 @@ def selector_walk(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, blo
                                     _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals), _ptr(anchor_ids), _ptr(path),
                                     _ptr(ps), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "dflash2_selector_walk")
+    return path, ps
+
+
+def selector_sample(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, block_size: int,
+                    temperature: float = 1.0, seed: int = 0, workspace: Optional[torch.Tensor] = None,
+                    want_scores: bool = True):
+    """-> (path [n_blocks, bs] int32, path_score [n_blocks, bs] float32 or None), the
+    path drawn from softmax(S / temperature) with the counter-based generator keyed by seed."""
+    _same_dtype(h, w_h, cb_pred, cb_succ)
+    _ids(cand_ids, "cand_ids")
+    _ids(anchor_ids, "anchor_ids")
+    N, H = h.shape
+    V, r = cb_pred.shape
+    K = cand_ids.shape[1]
+    nb = anchor_ids.shape[0]
+    dev = h.device
+    path = torch.empty((nb, block_size), dtype=torch.int32, device=dev)
+    ps = torch.empty((nb, block_size), dtype=torch.float32, device=dev) if want_scores else None
+    if workspace is None:
+        workspace = make_workspace(OP_SELECTOR_WALK, nb * block_size, H, V, r, K, dev)
+    st = _lib.dflash2_selector_sample(_dtype_code(h), nb, block_size, H, V, r, K, _ptr(h), _ptr(w_h), _ptr(cb_pred),
+                                      _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals), _ptr(anchor_ids),
+                                      float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(path), _ptr(ps),
+                                      _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "dflash2_selector_sample")
     return path, ps
 
 

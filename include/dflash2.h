@@ -7,7 +7,8 @@
  *   2. full-vocabulary unary LM-head logits with a per-position top-K
  *      (dflash2_unary_topk);
  *   3. the candidate selector S_t(a,b) = U_t(b) + <A(a) * H(h_t), B(b)>,
- *      walked greedily from the anchor (dflash2_selector_walk) or scored in one
+ *      walked greedily from the anchor (dflash2_selector_walk), sampled from
+ *      the same scores (dflash2_selector_sample), or scored in one
  *      shot with teacher-forced predecessors (dflash2_selector_score_tf).
  *
  * Sources, cited by page title and section:
@@ -171,6 +172,31 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
                                      const float *cand_vals, const int32_t *anchor_ids,
                                      int32_t *out_path, float *out_path_score, void *workspace,
                                      size_t workspace_bytes, void *stream);
+
+/*
+ * Sampled selector walk per anchor block ([Explainer] "Problem 1", the
+ * paragraph after the selector equation: the walk may sample from the same
+ * scores instead of following the best successor; "Draft-Verify Cycle"
+ * flowchart, the walk node).  Same inputs, scores and outputs as
+ * dflash2_selector_walk, except that the pick at t is the first argmax over
+ * the slots j of
+ *   S_t(path[blk, t-1], c_{t,j}) / temperature + G[blk, t, j],
+ * G[blk, t, j] = -log(-log(u)), u = ((x >> 8) + 1/2) / 2^24 with x the first
+ * word of Philox4x32-10 at counter (j, t, blk, 0) under the key (seed & 0xffffffff,
+ * seed >> 32): a draw from softmax(S_t / temperature) over the candidates
+ * (Gumbel-max), reproducible from (seed, blk, t).  out_path_score holds the
+ * picked candidate's S_t, without the noise.
+ *   temperature > 0 and finite (DFLASH2_ERR_SHAPE otherwise); the workspace
+ *   is that of DFLASH2_OP_SELECTOR_WALK.
+ */
+dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t block_size,
+                                       int32_t hidden, int32_t vocab, int32_t rank, int32_t top_k,
+                                       const void *h, const void *w_h, const void *cb_pred,
+                                       const void *cb_succ, const int32_t *cand_ids,
+                                       const float *cand_vals, const int32_t *anchor_ids,
+                                       float temperature, uint64_t seed, int32_t *out_path,
+                                       float *out_path_score, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /*
  * Teacher-forced selector scoring of every row at once ([verl PR] "Selector

@@ -385,3 +385,100 @@ def selector_score_tf(g, cb_pred, cb_succ, cand_ids, cand_u, pred_ids,
         ce[n] = lse - s2[kg]
         valid[n] = 1
     return scores, best, ce, valid
+
+
+# --------------------------------------------------------------------------
+# sampling walk
+# --------------------------------------------------------------------------
+#
+# [Explainer] "Problem 1 - Independent picks are incoherent" (the paragraph
+# after the selector equation) and the "Draft-Verify Cycle" flowchart (the
+# walk node): besides the greedy walk, the path may be sampled from the same
+# scores.  The pages fix no distribution or generator.  READINGS:
+#   * a_t is drawn from softmax over the candidates of row t of
+#     S_t(a_{t-1}, .) / temperature (temperature 1: the scores as they are);
+#   * the draw is the Gumbel-max form: the first argmax over j of
+#     S_t(a_{t-1}, c_{t,j}) / temperature + G[b, t, j], with G standard
+#     Gumbel noise (Gumbel-max: this argmax is distributed exactly as the
+#     softmax draw), so, as in the greedy walk, every predecessor's pick is
+#     defined before the path is known;
+#   * G[b, t, j] = -log(-log(u)) with u = (x / 256 + 1/2) / 2^24, x the first
+#     word of Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random
+#     numbers: as easy as 1, 2, 3", SC 2011) at counter (j, t, b, 0) under the
+#     key (seed mod 2^32, seed / 2^32): one counter-based generator, defined
+#     by its publication and implemented separately on each side.
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # key schedule (Weyl) increments
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32 with 10 rounds (the SC 2011 definition): each round takes
+    (c0, c1, c2, c3) to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+    lo(M0 c0)) and the key advances by the Weyl constants between rounds.
+    counter: uint array [..., 4]; key: uint array [..., 2] (broadcast).
+    Returns uint32 [..., 4]."""
+    c = np.asarray(counter, dtype=np.uint64) & 0xFFFFFFFF
+    k = np.asarray(key, dtype=np.uint64) & 0xFFFFFFFF
+    c0, c1, c2, c3 = (c[..., i] for i in range(4))
+    k0, k1 = k[..., 0], k[..., 1]
+    mask = np.uint64(0xFFFFFFFF)
+    for r in range(10):
+        p0 = np.uint64(_PHILOX_M[0]) * c0   # exact: a 32 x 32-bit product fits 64 bits
+        p1 = np.uint64(_PHILOX_M[1]) * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & mask
+        hi1, lo1 = p1 >> np.uint64(32), p1 & mask
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+        k0 = (k0 + np.uint64(_PHILOX_W[0])) & mask
+        k1 = (k1 + np.uint64(_PHILOX_W[1])) & mask
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+def walk_uniform(block: int, t: int, slots, seed: int) -> np.ndarray:
+    """u[j] in (0, 1) for the given slots of position t of anchor block
+    `block` (READING above): 24 bits of the first Philox word, centred."""
+    slots = np.asarray(slots, dtype=np.uint64)
+    ctr = np.stack([slots, np.full_like(slots, t), np.full_like(slots, block), np.zeros_like(slots)], axis=-1)
+    key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], dtype=np.uint64)
+    x = philox4x32_10(ctr, key)[..., 0].astype(np.float64)
+    return (np.floor(x / 256.0) + 0.5) / 2.0 ** 24
+
+
+def gumbel_noise(block: int, t: int, slots, seed: int) -> np.ndarray:
+    """Standard Gumbel noise -log(-log(u)) for the given slots."""
+    return -np.log(-np.log(walk_uniform(block, t, slots, seed)))
+
+
+def selector_sample(g, cb_pred, cb_succ, cand_ids, cand_u, anchors, block_size: int,
+                    dtype: str, temperature: float, seed: int, return_scores: bool = False):
+    """Sampled path per anchor block: as selector_walk, with the pick at t the
+    first argmax of S_t(a_{t-1}, .) / temperature + G[b, t, .] (READINGS above).
+    path_score holds the picked candidate's S (without the noise).
+
+    Returns (path int32 [n_b, bs], path_score float64 [n_b, bs][, z float64
+    [n_b, bs, K]: the noisy scores the picks maximise])."""
+    if not temperature > 0:
+        raise ValueError("temperature must be positive")
+    cand_ids = np.asarray(cand_ids)
+    N, K = cand_ids.shape
+    nb = _check_blocked(N, block_size)
+    anchors = np.asarray(anchors)
+    _need_shape("anchors", anchors, (nb,))
+    path = np.zeros((nb, block_size), dtype=np.int32)
+    pscore = np.zeros((nb, block_size), dtype=np.float64)
+    allz = np.zeros((nb, block_size, K), dtype=np.float64)
+    for b in range(nb):
+        a = int(anchors[b])
+        path[b, 0] = a
+        for t in range(1, block_size):
+            n = b * block_size + t
+            s = transition_scores(g[n], cb_pred, cb_succ, a, cand_ids[n], cand_u[n], dtype)
+            z = s / temperature + gumbel_noise(b, t, np.arange(K), seed)
+            j = first_argmax(z)
+            a = int(cand_ids[n, j])
+            path[b, t] = a
+            pscore[b, t] = s[j]
+            allz[b, t] = z
+    if return_scores:
+        return path, pscore, allz
+    return path, pscore

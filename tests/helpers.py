@@ -168,6 +168,42 @@ def compare_walk(gpu_path, gpu_ps, g64, A, B, cand_ids, cand_u, anchors, bs, dty
     return fails, flags, teeth, msgs
 
 
+def compare_sample(gpu_path, gpu_ps, g64, A, B, cand_ids, cand_u, anchors, bs, dtype, temperature, seed):
+    """Replays a sampled GPU path through the oracle: at each step the oracle's
+    scores S for the GPU's predecessor, the noisy scores z = S / temperature +
+    G (float64 Gumbel noise from the same generator), and the GPU's pick must
+    be the first argmax of z, or within TIE / temperature + 1e-4 of it (the
+    kernel forms S and the noise in float32: flagged, not failed).
+    Returns (fails, flags, messages)."""
+    fails = flags = 0
+    msgs = []
+    for b in range(gpu_path.shape[0]):
+        if gpu_path[b, 0] != anchors[b]:
+            fails += 1
+            msgs.append(f"block {b}: position 0 {gpu_path[b, 0]} != anchor {anchors[b]}")
+            continue
+        for t in range(1, bs):
+            n = b * bs + t
+            s = O.transition_scores(g64[n], A, B, int(gpu_path[b, t - 1]), cand_ids[n], cand_u[n], dtype)
+            z = s / temperature + O.gumbel_noise(b, t, np.arange(len(s)), seed)
+            hits = np.flatnonzero(cand_ids[n] == gpu_path[b, t])
+            if hits.size == 0:
+                fails += 1
+                msgs.append(f"block {b} t {t}: picked {gpu_path[b, t]} is not a candidate")
+                continue
+            jg, jo = int(hits[0]), O.first_argmax(z)
+            if jg != jo:
+                if z[jo] - z[jg] <= TIE / temperature + 1e-4:
+                    flags += 1
+                else:
+                    fails += 1
+                    msgs.append(f"block {b} t {t}: slot {jg} (z {z[jg]}) vs oracle slot {jo} ({z[jo]})")
+            if gpu_ps is not None and not close(gpu_ps[b, t], s[jg]):
+                fails += 1
+                msgs.append(f"block {b} t {t}: path score {gpu_ps[b, t]} vs {s[jg]}")
+    return fails, flags, msgs
+
+
 def compare_tf(gpu, ref, cand_ids):
     """gpu/ref = (scores, best_ids, ce, valid) of the same rows."""
     gs, gb, gce, gv = gpu

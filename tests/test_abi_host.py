@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert sorted(D.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -121,6 +121,26 @@ def test_selector_walk_rules():
     assert walk(path=None) == NULL and walk(anchors=None) == NULL and walk(ws=None) == NULL
     assert walk(wsb=100) == WS
     assert walk(ps=fake(7)) == ALIAS
+
+
+def sample(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, temp=1.0, path=fake(10), ps=None, anchors=fake(6),
+           ws=fake(12), wsb=None):
+    if wsb is None:
+        wsb = D.workspace_bytes(D.OP_SELECTOR_WALK, max(nb * bs, 1), h, v, r, k) if nb > 0 else 1 << 20
+    return L.dflash2_selector_sample(dtype, nb, bs, h, v, r, k, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+                                     anchors, temp, 0x1234, path, ps, ws, wsb, None)
+
+
+@no_gpu
+def test_selector_sample_rules():
+    # the walk's rules, plus a positive, finite temperature
+    assert sample(k=0) == SHAPE and sample(nb=0) == SHAPE and sample(k=65) == UNSUP and sample(r=12) == UNSUP
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert sample(temp=bad) == SHAPE
+    assert sample(dtype=5) == DTYPE
+    assert sample(path=None) == NULL and sample(anchors=None) == NULL and sample(ws=None) == NULL
+    assert sample(wsb=100) == WS
+    assert sample(ps=fake(10)) == ALIAS
 
 
 def tf(dtype=1, n=16, h=256, v=1000, r=32, k=16, gold=None, force=None, gl=None, ce=None, valid=None, ws=fake(12),

@@ -8,7 +8,8 @@ import torch
 
 from block_draft_head_amd.inputs import Workload, make_inputs, to_storage
 from oracle import dflash2_oracle as O
-from tests.helpers import (act_ok, close, compare_tf, compare_topk, compare_walk, conv_term_scale, to_dev,
+from tests.helpers import (act_ok, close, compare_sample, compare_tf, compare_topk, compare_walk, conv_term_scale,
+                           to_dev,
                            to_np)
 
 pytestmark = pytest.mark.gpu
@@ -276,6 +277,85 @@ def test_selector_walk_and_tf(D, nb, bs, H, V, r, K, dtype):
     best, sc = to_np(best).reshape(nb, bs), to_np(sc).reshape(nb, bs, K)
     assert np.array_equal(best[:, 1:], P[:, 1:])
     assert np.array_equal(sc.max(axis=2)[:, 1:], to_np(ps)[:, 1:])  # bit-exact replay
+
+
+SAMPLE_CASES = [
+    # (n_blocks, bs, H, V, r, K, dtype, temperature)
+    (3, 8, 256, 1000, 256, 16, "bf16", 1.0), (16, 8, 256, 4096, 32, 16, "f32", 0.5),
+    (4, 16, 512, 5000, 512, 64, "bf16", 2.0), (2, 3, 256, 800, 256, 33, "bf16", 1.0),
+    (64, 8, 256, 2000, 256, 16, "bf16", 1.0),
+]
+
+
+@pytest.mark.parametrize("nb,bs,H,V,r,K,dtype,temp", SAMPLE_CASES)
+def test_selector_sample(D, nb, bs, H, V, r, K, dtype, temp):
+    log(f"sample nb={nb} bs={bs} H={H} V={V} r={r} K={K} {dtype} T={temp}")
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, vocab=V, rank=r, top_k=K, dtype=dtype)
+    inp = make_inputs(w, seed=19, fields=["h", "w_h", "cb_pred", "cb_succ", "anchors"])
+    if dtype == "f32":
+        inp["cb_pred"] *= np.float32(6)
+        inp["cb_succ"] *= np.float32(6)
+    rng = np.random.default_rng(nb * 1000 + K + 7)
+    ids, vals = rand_cands(rng, nb * bs, V, K)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    seed = 0x9E3779B97F4A7C15 ^ (nb * 131 + K)
+    path, ps = D.selector_sample(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids), to_dev(vals),
+                                 dev["anchors"], bs, temperature=temp, seed=seed)
+    g64 = O.context_projection(inp["h"], inp["w_h"], dtype)
+    u64 = vals.astype(np.float64)
+    fails, flags, msgs = compare_sample(to_np(path), to_np(ps), g64, inp["cb_pred"], inp["cb_succ"], ids, u64,
+                                        inp["anchors"], bs, dtype, temp, seed)
+    log(f"  sample fails={fails} flags={flags}")
+    assert fails == 0, msgs[:5]
+    if flags == 0:
+        ref, _ = O.selector_sample(g64, inp["cb_pred"], inp["cb_succ"], ids, u64, inp["anchors"], bs, dtype, temp,
+                                   seed)
+        assert np.array_equal(to_np(path), ref)
+    # the same seed draws the same path; another seed another one
+    path2, _ = D.selector_sample(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids), to_dev(vals),
+                                 dev["anchors"], bs, temperature=temp, seed=seed)
+    assert torch.equal(path, path2)
+    if nb * (bs - 1) >= 16:
+        path3, _ = D.selector_sample(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids),
+                                     to_dev(vals), dev["anchors"], bs, temperature=temp, seed=seed + 1)
+        assert not torch.equal(path, path3)
+
+
+def test_sampling_at_vanishing_temperature_follows_the_greedy_walk(D):
+    nb, bs, H, V, r, K = 32, 8, 256, 2000, 256, 16
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, vocab=V, rank=r, top_k=K)
+    inp = make_inputs(w, seed=21, fields=["h", "w_h", "cb_pred", "cb_succ", "anchors"])
+    rng = np.random.default_rng(5)
+    ids, vals = rand_cands(rng, nb * bs, V, K)
+    args = [to_dev(inp[k]) for k in ("h", "w_h", "cb_pred", "cb_succ")] + [to_dev(ids), to_dev(vals),
+                                                                           to_dev(inp["anchors"]), bs]
+    gp, gps = D.selector_walk(*args)
+    sp, sps = D.selector_sample(*args, temperature=1e-6, seed=3)
+    same = (to_np(gp) == to_np(sp)).all(axis=1)
+    # a block may part only where two of the greedy scores lie within the noise's reach
+    assert same.mean() > 0.9, same.mean()
+    assert np.array_equal(to_np(gps)[same], to_np(sps)[same])
+
+
+def test_gpu_draws_follow_the_softmax_of_the_scores(D):
+    # Zero successor codebook: every position scores the same three unary
+    # values log(1, 2, 5); each (block, position) is one draw.
+    nb, bs, H, V, r, K = 2048, 8, 256, 64, 32, 3
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, vocab=V, rank=r, top_k=K)
+    inp = make_inputs(w, seed=22, fields=["h", "w_h", "cb_pred", "anchors"])
+    N = nb * bs
+    ids = np.tile(np.array([5, 9, 17], np.int32), (N, 1))
+    vals = np.tile(np.log([1.0, 2.0, 5.0]).astype(np.float32), (N, 1))
+    zero_b = torch.zeros((V, r), dtype=torch.bfloat16, device="cuda")
+    for temp, p in ((1.0, np.array([1, 2, 5]) / 8), (2.0, np.sqrt([1, 2, 5]) / np.sqrt([1, 2, 5]).sum())):
+        path, _ = D.selector_sample(to_dev(inp["h"]), to_dev(inp["w_h"]), to_dev(inp["cb_pred"]), zero_b,
+                                    to_dev(ids), to_dev(vals), to_dev(inp["anchors"]), bs, temperature=temp,
+                                    seed=11)
+        picks = to_np(path)[:, 1:].ravel()
+        freq = np.array([(picks == i).mean() for i in (5, 9, 17)])
+        sd = np.sqrt(p * (1 - p) / picks.size)
+        log(f"  T={temp} freq={freq} want={p}")
+        assert np.all(np.abs(freq - p) < 4 * sd), (temp, freq, p)
 
 
 def test_zero_successor_codebook_walks_the_unary_argmax(D):

@@ -31,6 +31,12 @@ MUTANTS = {
     "CE sign flipped": ("ce[n] = lse - s2[kg]", "ce[n] = s2[kg] - lse"),
     "gold outside the set always kept": ("elif force is not None and force[n]:", "elif True:"),
     "context projection transposed": ("return widen(h, dtype) @ widen(w_h, dtype).T", "return widen(h, dtype) @ widen(w_h, dtype).T[::-1]"),
+    "Philox round multipliers swapped": ("p0 = np.uint64(_PHILOX_M[0]) * c0", "p0 = np.uint64(_PHILOX_M[1]) * c0"),
+    "Philox key not advanced": ("k0 = (k0 + np.uint64(_PHILOX_W[0])) & mask", "k0 = k0"),
+    "Gumbel noise with the wrong sign": ("return -np.log(-np.log(walk_uniform(", "return np.log(-np.log(walk_uniform("),
+    "temperature multiplies the scores": ("z = s / temperature + gumbel_noise(", "z = s * temperature + gumbel_noise("),
+    "sampled score reported with its noise": ("pscore[b, t] = s[j]\n            allz[b, t] = z", "pscore[b, t] = z[j]\n            allz[b, t] = z"),
+    "noise shared by every slot": ("gumbel_noise(b, t, np.arange(K), seed)", "gumbel_noise(b, t, np.zeros(K, np.int64), seed)"),
 }
 
 

@@ -454,3 +454,77 @@ def test_forced_gold_takes_the_weakest_slot_and_coverage_follows():
     assert abs(ce[n] - (m + math.log(np.exp(s2 - m).sum()) - s2[K - 1])) < 1e-12
     # excluded rows contribute no CE
     assert np.all(ce[valid == 0] == 0)
+
+
+# ---------------------------------------------------------------- sampling walk
+
+def test_philox4x32_10_reproduces_the_published_known_answers():
+    # Known-answer vectors of Philox4x32-10 (Salmon et al., SC 2011, as
+    # distributed with the authors' Random123 library): counter, key -> output.
+    kat = [
+        ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+         (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+        ((0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF), (0xFFFFFFFF, 0xFFFFFFFF),
+         (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+        ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+         (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+    ]
+    for ctr, key, want in kat:
+        got = O.philox4x32_10(np.array(ctr, np.uint64), np.array(key, np.uint64))
+        assert tuple(int(v) for v in got) == want
+
+
+def test_walk_uniforms_are_open_24_bit_grid_points():
+    u = O.walk_uniform(3, 5, np.arange(4096), 0xDEADBEEF12345678)
+    assert u.min() > 0 and u.max() < 1
+    assert np.all(((u * 2 ** 24) - 0.5) == np.floor(u * 2 ** 24))
+    # distinct counters give distinct draws; the same counter the same draw
+    assert len(np.unique(u)) > 4000
+    assert np.array_equal(u, O.walk_uniform(3, 5, np.arange(4096), 0xDEADBEEF12345678))
+    assert not np.array_equal(u, O.walk_uniform(3, 6, np.arange(4096), 0xDEADBEEF12345678))
+    assert not np.array_equal(u, O.walk_uniform(3, 5, np.arange(4096), 0xDEADBEEF12345679))
+
+
+def test_sampling_at_vanishing_temperature_is_the_greedy_walk():
+    rng = np.random.default_rng(41)
+    V, r, K, bs, nb = 200, 16, 8, 8, 12
+    A, B, g, ids, U = _rand_selector(rng, nb * bs, V, r, K)
+    anchors = rng.integers(0, V, nb)
+    path, ps = O.selector_walk(g, A, B, ids, U, anchors, bs, "f32")
+    spath, sps = O.selector_sample(g, A, B, ids, U, anchors, bs, "f32", 1e-9, 7)
+    assert np.array_equal(path, spath) and np.array_equal(ps, sps)
+    # at temperature 1 the draws depart from the greedy path
+    spath1, _ = O.selector_sample(g, A, B, ids, U, anchors, bs, "f32", 1.0, 7)
+    assert not np.array_equal(path, spath1)
+
+
+def test_sampled_picks_follow_the_softmax_of_the_scores():
+    # Gumbel-max: the first argmax of S / temperature + Gumbel noise is
+    # distributed as softmax(S / temperature).  Zero successor codebook: S is
+    # the unary row, the same at every position, so every (block, position)
+    # is an independent draw from one known distribution.
+    rng = np.random.default_rng(42)
+    V, r, K, bs, nb = 64, 4, 3, 8, 2000
+    N = nb * bs
+    A, B, g, _, _ = _rand_selector(rng, N, V, r, K)
+    ids = np.tile(np.array([5, 9, 17], np.int32), (N, 1))
+    U = np.tile(np.log([1.0, 2.0, 5.0]), (N, 1))
+    for temp, p in ((1.0, np.array([1, 2, 5]) / 8), (2.0, np.sqrt([1, 2, 5]) / np.sqrt([1, 2, 5]).sum())):
+        path, ps = O.selector_sample(g, A, np.zeros_like(B), ids, U, rng.integers(0, V, nb), bs, "f32", temp, 99)
+        picks = path[:, 1:].ravel()
+        freq = np.array([(picks == i).mean() for i in (5, 9, 17)])
+        sd = np.sqrt(p * (1 - p) / picks.size)
+        assert np.all(np.abs(freq - p) < 4 * sd), (temp, freq, p)
+        # the reported score is the picked candidate's S, noise excluded
+        assert np.allclose(ps[:, 1:].ravel(), np.log([1.0, 2.0, 5.0])[np.searchsorted([5, 9, 17], picks)])
+
+
+def test_temperature_divides_the_scores_not_the_noise():
+    rng = np.random.default_rng(43)
+    V, r, K, bs, nb = 100, 8, 6, 8, 10
+    A, B, g, ids, U = _rand_selector(rng, nb * bs, V, r, K)
+    anchors = rng.integers(0, V, nb)
+    # scores doubled at temperature 2 give the same draws as the scores at 1
+    p1, s1 = O.selector_sample(g, A, np.zeros_like(B), ids, U, anchors, bs, "f32", 1.0, 5)
+    p2, s2 = O.selector_sample(g, A, np.zeros_like(B), ids, 2.0 * U, anchors, bs, "f32", 2.0, 5)
+    assert np.array_equal(p1, p2) and np.allclose(2.0 * s1, s2)
