@@ -482,3 +482,62 @@ def selector_sample(g, cb_pred, cb_succ, cand_ids, cand_u, anchors, block_size: 
     if return_scores:
         return path, pscore, allz
     return path, pscore
+
+
+# --------------------------------------------------------------------------
+# selector CE backward
+# --------------------------------------------------------------------------
+#
+# [verl PR] "Selector training objective": the selector's inputs are
+# detached, so its CE trains only its own parameters; [SpecForge] "Selector
+# objective and schedule" (the stop-gradient switch detaches both inputs,
+# the unary logits and the hidden states).  With L = sum_n w[n] CE[n] over the
+# rows that carry a CE (w the upstream gradient dL/dCE[n]) and d[n, k] =
+# w[n] (softmax(S'[n])_k - [k = k_gold]) on the forced set C' of
+# selector_score_tf:
+#   dL/dB[c'_k]   += d[n, k] (A[p_n] * g[n])
+#   dL/dA[p_n]    += g[n] * v[n],          v[n] = sum_k d[n, k] B[c'_k]
+#   dL/dg[n]       = A[p_n] * v[n]
+#   dL/dW_H        = sum_n dL/dg[n] (outer) h[n]      (g = W_H h)
+# READING: h and U (the forced gold's logit included) are constants.
+
+def selector_ce_backward(h, w_h, cb_pred, cb_succ, cand_ids, cand_u, pred_ids, dtype: str,
+                         gold_ids, force, gold_logit, grad_ce):
+    """Gradients of sum_n grad_ce[n] CE[n] (the CE of selector_score_tf) with
+    respect to the predecessor codebook A, the successor codebook B and the
+    context projection W_H.  Returns (dA [V, r], dB [V, r], dW_H [r, H],
+    dg [N, r], valid [N]) in float64."""
+    cand_ids = np.asarray(cand_ids)
+    N, K = cand_ids.shape
+    g = context_projection(h, w_h, dtype)
+    A, B = widen(cb_pred, dtype), widen(cb_succ, dtype)
+    dA, dB = np.zeros_like(A), np.zeros_like(B)
+    dg = np.zeros_like(g)
+    valid = np.zeros(N, dtype=np.uint8)
+    for n in range(N):
+        p = int(pred_ids[n])
+        ids = cand_ids[n].astype(np.int64).copy()
+        u = np.asarray(cand_u[n], dtype=np.float64).copy()
+        gold = int(gold_ids[n])
+        hits = np.flatnonzero(ids == gold)
+        if hits.size:
+            kg = int(hits[0])
+        elif force is not None and force[n]:
+            kg = K - 1
+            ids[kg] = gold
+            u[kg] = float(gold_logit[n])
+        else:
+            continue
+        valid[n] = 1
+        ag = A[p] * g[n]
+        s = u + B[ids] @ ag
+        e = np.exp(s - s.max())
+        d = e / e.sum()
+        d[kg] -= 1.0
+        d *= float(grad_ce[n])
+        v = d @ B[ids]
+        dg[n] = A[p] * v
+        dA[p] += g[n] * v
+        np.add.at(dB, ids, d[:, None] * ag[None, :])
+    dW = dg.T @ widen(h, dtype)
+    return dA, dB, dW, dg, valid

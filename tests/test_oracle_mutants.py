@@ -37,6 +37,13 @@ MUTANTS = {
     "temperature multiplies the scores": ("z = s / temperature + gumbel_noise(", "z = s * temperature + gumbel_noise("),
     "sampled score reported with its noise": ("pscore[b, t] = s[j]\n            allz[b, t] = z", "pscore[b, t] = z[j]\n            allz[b, t] = z"),
     "noise shared by every slot": ("gumbel_noise(b, t, np.arange(K), seed)", "gumbel_noise(b, t, np.zeros(K, np.int64), seed)"),
+    "backward drops the gold one-hot": ("d[kg] -= 1.0", "d[kg] -= 0.0"),
+    "backward ignores the forced gold": ("ids[kg] = gold\n            u[kg] = float(", "ids[kg] = ids[kg]\n            u[kg] = float("),
+    "backward ignores the upstream gradient": ("d *= float(grad_ce[n])", "d *= 1.0"),
+    "predecessor gradient without the context": ("dA[p] += g[n] * v", "dA[p] += v"),
+    "successor gradient sent to the predecessor row": ("np.add.at(dB, ids, d[:, None]", "np.add.at(dB, np.full_like(ids, p), d[:, None]"),
+    "projection gradient against the wrong factor": ("dg[n] = A[p] * v", "dg[n] = g[n] * v"),
+    "backward keeps rows the forward excludes": ("        else:\n            continue\n        valid[n] = 1\n        ag", "        else:\n            pass\n        valid[n] = 1\n        ag"),
 }
 
 

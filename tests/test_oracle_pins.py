@@ -528,3 +528,130 @@ def test_temperature_divides_the_scores_not_the_noise():
     p1, s1 = O.selector_sample(g, A, np.zeros_like(B), ids, U, anchors, bs, "f32", 1.0, 5)
     p2, s2 = O.selector_sample(g, A, np.zeros_like(B), ids, 2.0 * U, anchors, bs, "f32", 2.0, 5)
     assert np.array_equal(p1, p2) and np.allclose(2.0 * s1, s2)
+
+
+# ---------------------------------------------------------------- selector CE backward
+
+def _grid(rng, shape, scale, q=8):
+    # values on a 2^-q grid, so that x +/- 2^-(q+4) is exact in float32
+    return (np.rint(rng.standard_normal(shape) * scale * 2 ** q) / 2 ** q).astype(np.float32)
+
+
+def _ce_case(rng, N=14, H=6, V=12, r=4, K=5):
+    """Small case with every row kind: gold in the set, gold forced into the
+    weakest slot, gold excluded; repeated predecessors and candidate ids
+    shared by rows, so the scatter-adds collide."""
+    h = _grid(rng, (N, H), 1.0)
+    w_h = _grid(rng, (r, H), 0.5)
+    A = _grid(rng, (V, r), 0.8)
+    B = _grid(rng, (V, r), 0.8)
+    ids = np.stack([rng.permutation(V)[:K] for _ in range(N)]).astype(np.int32)
+    U = -np.sort(-rng.standard_normal((N, K)), axis=1)
+    pred = rng.integers(0, 3, N).astype(np.int32)
+    gold = ids[np.arange(N), rng.integers(0, K, N)].copy()
+    out = np.flatnonzero(rng.random(N) < 0.5)
+    for n in out:
+        gold[n] = rng.choice(np.setdiff1d(np.arange(V), ids[n]))
+    force = (rng.random(N) < 0.6).astype(np.uint8)
+    force[out[::2]], force[out[1::2]] = 0, 1
+    gl = rng.standard_normal(N)
+    w = rng.random(N) + 0.25
+    return h, w_h, A, B, ids, U, pred, gold, force, gl, w
+
+
+def _weighted_ce(h, w_h, A, B, ids, U, pred, gold, force, gl, w, g=None):
+    if g is None:
+        g = O.context_projection(h, w_h, "f32")
+    _, _, ce, valid = O.selector_score_tf(g, A, B, ids, U, pred, "f32", gold_ids=gold, force=force, gold_logit=gl)
+    return float(np.sum(w * ce)), valid
+
+
+def test_ce_backward_matches_central_differences_of_the_forward():
+    # Every entry of dA, dB and dW_H against a central difference of the
+    # weighted teacher-forced CE (the forward pinned above); dg against a
+    # difference in g itself.  The step 2^-12 is exact on the 2^-8 grid.
+    rng = np.random.default_rng(41)
+    case = _ce_case(rng)
+    h, w_h, A, B, ids, U, pred, gold, force, gl, w = case
+    dA, dB, dW, dg, valid = O.selector_ce_backward(h, w_h, A, B, ids, U, pred, "f32", gold, force, gl, w)
+    base, valid_f = _weighted_ce(*case)
+    assert np.array_equal(valid, valid_f)
+    assert 0 < valid.sum() < len(valid)     # some rows excluded
+    eps = 2.0 ** -12
+    for name, pos, grad in (("A", 2, dA), ("B", 3, dB), ("W", 1, dW)):
+        for idx in np.ndindex(grad.shape):
+            args_p, args_m = list(case), list(case)
+            xp, xm = case[pos].copy(), case[pos].copy()
+            xp[idx] += np.float32(eps)
+            xm[idx] -= np.float32(eps)
+            assert xp[idx] - case[pos][idx] == eps      # the step is exact
+            args_p[pos], args_m[pos] = xp, xm
+            fd = (_weighted_ce(*args_p)[0] - _weighted_ce(*args_m)[0]) / (2 * eps)
+            assert abs(fd - grad[idx]) < 2e-6 * (1 + abs(fd)), (name, idx, fd, grad[idx])
+    g = O.context_projection(h, w_h, "f32")
+    for idx in np.ndindex(g.shape):
+        gp, gm = g.copy(), g.copy()
+        gp[idx] += 1e-6
+        gm[idx] -= 1e-6
+        fd = (_weighted_ce(*case, g=gp)[0] - _weighted_ce(*case, g=gm)[0]) / 2e-6
+        assert abs(fd - dg[idx]) < 1e-6 * (1 + abs(fd))
+    # untouched codebook rows get no gradient
+    assert np.all(dA[np.setdiff1d(np.arange(len(A)), pred[valid == 1])] == 0)
+
+
+def test_ce_backward_obeys_the_euler_identity_of_the_trilinear_pair_term():
+    # The pair term is linear in each of A, B and W_H (g = W_H h), so
+    # d/dlambda L(lambda X) at lambda = 1 is the same for X = A, B or W_H:
+    # <dA, A> = <dB, B> = <dW_H, W_H> = <dg, g>, and it is nonzero.
+    rng = np.random.default_rng(42)
+    N, H, V, r, K = 64, 32, 300, 16, 8
+    h = _bf16(rng.standard_normal((N, H)))
+    w_h = _bf16(rng.standard_normal((r, H)) * 0.2)
+    A = _bf16(rng.standard_normal((V, r)) * 0.7)
+    B = _bf16(rng.standard_normal((V, r)) * 0.7)
+    ids = np.stack([rng.permutation(V)[:K] for _ in range(N)]).astype(np.int32)
+    U = -np.sort(-rng.standard_normal((N, K)), axis=1)
+    pred = rng.integers(0, V, N).astype(np.int32)
+    gold = rng.integers(0, V, N).astype(np.int32)
+    gold[::2] = ids[::2, 3]
+    force = (rng.random(N) < 0.8).astype(np.uint8)
+    gl = rng.standard_normal(N)
+    dA, dB, dW, dg, valid = O.selector_ce_backward(h, w_h, A, B, ids, U, pred, "bf16", gold, force, gl, np.ones(N))
+    g = O.context_projection(h, w_h, "bf16")
+    e = [np.sum(dA * O.widen(A, "bf16")), np.sum(dB * O.widen(B, "bf16")), np.sum(dW * O.widen(w_h, "bf16")),
+         np.sum(dg * g)]
+    assert abs(e[0]) > 1e-2
+    np.testing.assert_allclose(e, e[0], rtol=1e-10, atol=0)
+
+
+def test_ce_backward_closed_forms():
+    rng = np.random.default_rng(43)
+    N, H, V, r, K = 9, 5, 40, 3, 4
+    h, w_h = _grid(rng, (N, H), 1.0), _grid(rng, (r, H), 0.5)
+    A, B = _grid(rng, (V, r), 0.8), _grid(rng, (V, r), 0.8)
+    ids = np.stack([rng.permutation(V)[:K] for _ in range(N)]).astype(np.int32)
+    pred = rng.integers(0, V, N).astype(np.int32)
+    w = rng.random(N) + 0.5
+    # K = 1, gold in the set: the CE is identically 0, so is every gradient
+    z = O.selector_ce_backward(h, w_h, A, B, ids[:, :1], np.zeros((N, 1)), pred, "f32", ids[:, 0], None, None, w)
+    assert all(np.all(t == 0) for t in z[:4]) and z[4].all()
+    # zero successor codebook, equal unary logits: the softmax is uniform, so
+    # the successor gradient of row n is w (1/K - [k = gold]) (A[p] * g), and
+    # nothing else moves (v = 0)
+    kg = rng.integers(0, K, N)
+    Z = np.zeros_like(B)
+    dA, dB, dW, dg, valid = O.selector_ce_backward(h, w_h, A, Z, ids, np.full((N, K), 0.5), pred, "f32",
+                                                   ids[np.arange(N), kg], None, None, w)
+    assert valid.all() and np.all(dA == 0) and np.all(dW == 0) and np.all(dg == 0)
+    g = O.context_projection(h, w_h, "f32")
+    want = np.zeros((V, r))
+    for n in range(N):
+        for k in range(K):
+            want[ids[n, k]] += w[n] * (1 / K - (k == kg[n])) * A[pred[n]].astype(np.float64) * g[n]
+    np.testing.assert_allclose(dB, want, rtol=1e-12, atol=1e-15)
+    # excluded rows (gold outside the set, not forced) contribute nothing
+    far = np.full(N, V - 1, np.int32)
+    ids2 = ids % (V - 1)
+    z = O.selector_ce_backward(h, w_h, A, B, ids2, np.zeros((N, K)), pred, "f32", far, np.zeros(N, np.uint8),
+                               np.zeros(N), w)
+    assert not z[4].any() and all(np.all(t == 0) for t in z[:4])
