@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--selector", choices=("greedy", "sample"), default="greedy",
                     help="walk workloads: greedy walk, or the path sampled from softmax of the same scores "
                          "(temperature 1, a fixed generator key)")
+    ap.add_argument("--train", action="store_true",
+                    help="teacher-forced workloads: the step also runs the selector CE backward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
@@ -81,6 +83,23 @@ def traffic_for(w, launches_key):
     if not e or e.get("source_hash") != lmhead_source_hash():
         return None
     return e["fetch_kib"] * 1024.0 * e["fetch_scale"] + e["write_kib"] * 1024.0 * e["write_scale"]
+
+
+def backward_report(w, ms):
+    """Selector CE backward (context projection, per-row kernel, dW_H
+    contraction): its algorithmic bytes and flops over its measured time.
+    Bytes: h twice (projection and dW_H), W_H, g and dg written and read, the
+    predecessor and K successor rows gathered, ids / logits / per-row scalars,
+    and a read-modify-write of every touched float32 gradient row and of dW_H.
+    Flops: the two N x r x H contractions (the per-row work is O(N K r))."""
+    N, H, r, K = w.n_rows, w.hidden, w.rank, w.top_k
+    es = 2 if w.dtype == "bf16" else 4
+    nbytes = (2 * N * H * es + r * H * es + 4 * N * r * 4 + N * r * es + N * K * r * es + N * K * 8 + N * 17
+              + 2 * (N * r + N * K * r) * 4 + 2 * r * H * 4)
+    flops = 2 * (2 * N * r * H)
+    s = ms * 1e-3
+    return {"ms": ms, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "hbm_frac": nbytes / s / (HBM_PEAK_GBS * 1e9), "gbs": nbytes / s / 1e9, "tflops": flops / s / 1e12}
 
 
 def cpu_baseline(w, inp, budget_s):
@@ -151,10 +170,17 @@ def main():
     ws_topk = D.make_workspace(D.OP_UNARY_TOPK, N, H, V, 0, K, "cuda")
     ws_sel = D.make_workspace(D.OP_SELECTOR_WALK if w.mode != "tf" else D.OP_SELECTOR_TF, N, H, V, r, K, "cuda")
     ws_tf = D.make_workspace(D.OP_SELECTOR_TF, N, H, V, r, K, "cuda")
+    tf_mode = w.mode == "tf"
+    if args.train and not tf_mode:
+        print("--train needs a teacher-forced workload", file=sys.stderr)
+        sys.exit(2)
+    if tf_mode:  # selector CE backward: gradient buffers accumulate across steps (no zeroing in the step)
+        ws_bwd = D.make_workspace(D.OP_SELECTOR_CE_BACKWARD, N, H, V, r, K, "cuda")
+        grads = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in ((V, r), (V, r), (r, H))]
+        grad_ce = torch.full((N,), 1.0 / N, dtype=torch.float32, device="cuda")
     x_out = torch.empty_like(dev["h"])
     k_post = torch.empty((N, T, H // gs), dtype=torch.float32, device="cuda")
     y_out = torch.empty_like(dev["y"])
-    tf_mode = w.mode == "tf"
     gold = dev["gold"] if tf_mode else None
 
     def op_conv():
@@ -174,10 +200,18 @@ def main():
         return D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"],
                                bs, workspace=ws_sel)
 
+    def op_backward(ids, vals, gl):
+        return D.selector_ce_backward(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"],
+                                      gold, grad_ce, force=dev["force"], gold_logit=gl, grad_pred=grads[0],
+                                      grad_succ=grads[1], grad_wh=grads[2], want_ce=False, workspace=ws_bwd)
+
     def step():
         op_conv()
         ids, vals, gl = op_lmhead()
-        return ids, vals, gl, op_selector(ids, vals, gl)
+        res = op_selector(ids, vals, gl)
+        if args.train:
+            op_backward(ids, vals, gl)
+        return ids, vals, gl, res
 
     def timed(fn, n):
         """Device time of n back-to-back calls of `fn`, from events recorded on
@@ -220,7 +254,7 @@ def main():
     # enqueues far faster than the GPU drains a step (the LM head alone is
     # hundreds of microseconds), so each op's events bracket its kernels as
     # the GPU runs them back to back; the LM-head figure feeds the roofline.
-    names = ["conv", "lmhead", "selector"] + ([] if tf_mode else ["tf"])
+    names = ["conv", "lmhead", "selector"] + (["ce_backward"] if tf_mode else ["tf"])
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     for e in evs:
         e[0].record()
@@ -232,10 +266,15 @@ def main():
         e[3].record()
         if not tf_mode:
             op_tf(i_, v_)
-            e[4].record()
+        else:
+            op_backward(i_, v_, g_)
+        e[4].record()
     torch.cuda.synchronize()
     op_ms = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(names)}
     tf_ms = op_ms.pop("tf", None)
+    bwd_ms = op_ms.pop("ce_backward", None)
+    if args.train:
+        op_ms["ce_backward"] = bwd_ms
     replay_ok = None
     if not tf_mode and args.selector == "greedy":  # a sampled path is not the scores' argmax
         _, best, _, _ = op_tf(ids, vals)
@@ -280,11 +319,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n_blocks": w.n_blocks, "block_size": bs, "hidden": H, "vocab": V,
                    "taps": T, "group_size": gs, "rank": r, "top_k": K, "mode": w.mode,
-                   "selector": "teacher-forced" if tf_mode else args.selector},
+                   "selector": ("teacher-forced + CE backward" if args.train else "teacher-forced") if tf_mode
+                   else args.selector},
         "roofline": roof,
         "ops_ms": op_ms,
         "selector_plus_conv_over_lmhead": (op_ms["conv"] + op_ms["selector"]) / lm_ms,
         "tf_ms": tf_ms,
+        "ce_backward": backward_report(w, bwd_ms) if tf_mode else None,
         "tf_replays_walk": replay_ok,
         "wall_s_timed": wall,
     }

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdflash2.so")
-SOURCES = ["api.cpp", "conv.hip", "lmhead.hip", "proj.hip", "selector.hip"]
+SOURCES = ["api.cpp", "conv.hip", "lmhead.hip", "proj.hip", "selector.hip", "selector_bwd.hip"]
 
 ARCH = os.environ.get("DFLASH2_OFFLOAD_ARCH", "gfx950")
 FLAGS = [

@@ -90,6 +90,9 @@ size_t dflash2_workspace_bytes(int op, int64_t n_rows, int32_t hidden, int32_t v
         case DFLASH2_OP_SELECTOR_TF:
             if (rank < 1) return 0;
             return kStatusBytes + (size_t)n_rows * (size_t)rank * 4;
+        case DFLASH2_OP_SELECTOR_CE_BACKWARD:
+            if (rank < 1 || vocab < 1 || top_k < 1) return 0;
+            return ce_bwd_layout(n_rows, vocab, rank, top_k).total;
         default: return 0;
     }
 }
@@ -228,6 +231,49 @@ dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidd
                                        cb_succ, cand_ids, cand_vals, pred_ids, gold_ids, force,
                                        gold_logit, out_scores, out_best_ids, out_ce, out_valid,
                                        workspace, (hipStream_t)stream));
+}
+
+dflash2_status dflash2_selector_ce_backward(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,
+                                            int32_t rank, int32_t top_k, const void *h, const void *w_h,
+                                            const void *cb_pred, const void *cb_succ,
+                                            const int32_t *cand_ids, const float *cand_vals,
+                                            const int32_t *pred_ids, const int32_t *gold_ids,
+                                            const uint8_t *force, const float *gold_logit,
+                                            const float *grad_ce, float *grad_pred, float *grad_succ,
+                                            float *grad_wh, float *out_ce, uint8_t *out_valid,
+                                            void *workspace, size_t workspace_bytes, void *stream) {
+    dflash2_status s = check_selector(dtype, n_rows, hidden, vocab, rank, top_k);
+    if (s != DFLASH2_OK) return s;
+    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !pred_ids || !gold_ids || !grad_ce ||
+        !grad_pred || !grad_succ || !grad_wh || !workspace)
+        return DFLASH2_ERR_NULL;
+    if (force && !gold_logit) return DFLASH2_ERR_NULL;
+    // (row, slot) entries and the 2V + 1 per-target offsets are int32
+    if (n_rows * (int64_t)(top_k + 1) > INT_MAX || 2 * (int64_t)vocab + 1 > INT_MAX) return DFLASH2_ERR_UNSUPPORTED;
+    if (workspace_bytes <
+        dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_CE_BACKWARD, n_rows, hidden, vocab, rank, top_k))
+        return DFLASH2_ERR_WORKSPACE;
+    const size_t es = elem_size(dtype);
+    const size_t cb = (size_t)vocab * rank * 4, wh = (size_t)rank * hidden * 4;
+    const size_t n = (size_t)n_rows, nk = n * top_k;
+    struct Span { const void *p; size_t b; };
+    const Span outs[] = {{grad_pred, cb}, {grad_succ, cb}, {grad_wh, wh}, {out_ce, out_ce ? n * 4 : 0},
+                         {out_valid, out_valid ? n : 0}};
+    const Span ins[] = {{h, n * hidden * es}, {w_h, (size_t)rank * hidden * es},
+                        {cb_pred, (size_t)vocab * rank * es}, {cb_succ, (size_t)vocab * rank * es},
+                        {cand_ids, nk * 4}, {cand_vals, nk * 4}, {pred_ids, n * 4}, {gold_ids, n * 4},
+                        {force, force ? n : 0}, {gold_logit, gold_logit ? n * 4 : 0}, {grad_ce, n * 4},
+                        {workspace, workspace_bytes}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlaps(outs[i].p, outs[i].b, outs[j].p, outs[j].b)) return DFLASH2_ERR_ALIAS;
+        for (const Span &in : ins)
+            if (overlaps(outs[i].p, outs[i].b, in.p, in.b)) return DFLASH2_ERR_ALIAS;
+    }
+    return launched(launch_selector_ce_backward(dtype, n_rows, hidden, vocab, rank, top_k, h, w_h, cb_pred,
+                                                cb_succ, cand_ids, cand_vals, pred_ids, gold_ids, force,
+                                                gold_logit, grad_ce, grad_pred, grad_succ, grad_wh, out_ce,
+                                                out_valid, workspace, (hipStream_t)stream));
 }
 
 dflash2_status dflash2_read_device_status(const void *workspace, void *stream) {

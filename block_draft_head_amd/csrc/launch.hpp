@@ -33,6 +33,32 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
 // the candidate ids and (sampling) the noise.
 inline size_t walk_lds_bytes(int bs, int K) { return (size_t)bs * K * (8 + 4 + 4 + 4); }
 
+// Workspace of the selector CE backward, byte offsets (256-byte aligned).
+// g / gv [N, r], ag [N, r], dg [N, r] float32; per (row, slot) entries
+// (slot K is the predecessor row) with their weight, target and sorted
+// order; per-target counts and offsets over the 2V targets (successor rows,
+// then predecessor rows) plus one; and the scan's per-tile prefixes.
+constexpr int kScanTile = 4096;
+struct CeBwdLayout {
+    size_t g, ag, dg, wgt, tgt, src, counts, offsets, tiles, total;
+};
+inline CeBwdLayout ce_bwd_layout(int64_t N, int V, int r, int K) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t E = (size_t)N * (K + 1), C = 2 * (size_t)V + 1;
+    CeBwdLayout L;
+    L.g = kStatusBytes;
+    L.ag = L.g + up((size_t)N * r * 4);
+    L.dg = L.ag + up((size_t)N * r * 4);
+    L.wgt = L.dg + up((size_t)N * r * 4);
+    L.tgt = L.wgt + up(E * 4);
+    L.src = L.tgt + up(E * 4);
+    L.counts = L.src + up(E * 4);
+    L.offsets = L.counts + up(C * 4);
+    L.tiles = L.offsets + up(C * 4);
+    L.total = L.tiles + up((C + kScanTile - 1) / kScanTile * 4);
+    return L;
+}
+
 // Sampling walk: temperature and the generator's 64-bit key.
 struct SampleParams {
     float temperature;
@@ -61,5 +87,12 @@ hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, 
                               const float *gold_logit, float *out_scores, int32_t *out_best,
                               float *out_ce, uint8_t *out_valid, void *workspace,
                               hipStream_t stream);
+hipError_t launch_selector_ce_backward(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
+                                       const void *w_h, const void *A, const void *B,
+                                       const int32_t *cand_ids, const float *cand_vals,
+                                       const int32_t *pred_ids, const int32_t *gold_ids,
+                                       const uint8_t *force, const float *gold_logit, const float *grad_ce,
+                                       float *grad_pred, float *grad_succ, float *grad_wh, float *out_ce,
+                                       uint8_t *out_valid, void *workspace, hipStream_t stream);
 
 }  // namespace dflash2

@@ -21,12 +21,13 @@ STATUS = {
     4: "DFLASH2_ERR_UNSUPPORTED", 5: "DFLASH2_ERR_ALIAS", 6: "DFLASH2_ERR_WORKSPACE",
     7: "DFLASH2_ERR_LAUNCH", 8: "DFLASH2_ERR_DEVICE_ID_RANGE",
 }
-OP_UNARY_TOPK, OP_SELECTOR_WALK, OP_SELECTOR_TF = 0, 1, 2
+OP_UNARY_TOPK, OP_SELECTOR_WALK, OP_SELECTOR_TF, OP_SELECTOR_CE_BACKWARD = 0, 1, 2, 3
 F32, BF16 = 0, 1
 MAX_TOP_K, MAX_TAPS, MAX_BLOCK_SIZE, MAX_RANK = 64, 16, 64, 4096
 
 EXPORTS = ["dflash2_conv_prepare", "dflash2_conv_finish", "dflash2_unary_topk",
-           "dflash2_selector_walk", "dflash2_selector_sample", "dflash2_selector_score_tf", "dflash2_workspace_bytes",
+           "dflash2_selector_walk", "dflash2_selector_sample", "dflash2_selector_score_tf",
+           "dflash2_selector_ce_backward", "dflash2_workspace_bytes",
            "dflash2_status_str", "dflash2_read_device_status", "dflash2_version"]
 
 
@@ -49,6 +50,7 @@ def _load() -> ctypes.CDLL:
         "dflash2_selector_sample": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P,
                                     ctypes.c_float, ctypes.c_uint64, P, P, P, SZ, P],
         "dflash2_selector_score_tf": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "dflash2_selector_ce_backward": [ctypes.c_int, I64, I32, I32, I32, I32] + [P] * 16 + [P, SZ, P],
         "dflash2_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "dflash2_status_str": [ctypes.c_int],
         "dflash2_read_device_status": [P, P],
@@ -256,6 +258,44 @@ def selector_score_tf(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, pred_ids, g
                                         _ptr(ce), _ptr(valid), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "dflash2_selector_score_tf")
     return scores, best, ce, valid
+
+
+def selector_ce_backward(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, pred_ids, gold_ids, grad_ce, force=None,
+                         gold_logit=None, grad_pred=None, grad_succ=None, grad_wh=None, want_ce=True,
+                         workspace: Optional[torch.Tensor] = None):
+    """Adds the gradients of sum_n grad_ce[n] CE[n] into (grad_pred [V, r], grad_succ [V, r], grad_wh [r, H]),
+    float32, allocated zeroed when not given.  -> (grad_pred, grad_succ, grad_wh, ce [N] or None,
+    valid [N] or None)."""
+    _same_dtype(h, w_h, cb_pred, cb_succ)
+    _ids(cand_ids, "cand_ids")
+    _ids(pred_ids, "pred_ids")
+    _ids(gold_ids, "gold_ids")
+    N, H = h.shape
+    V, r = cb_pred.shape
+    K = cand_ids.shape[1]
+    dev = h.device
+    if force is not None and force.dtype != torch.uint8:
+        raise TypeError("force must be uint8")
+    if grad_ce.dtype != torch.float32:
+        raise TypeError("grad_ce must be float32")
+    grads = []
+    for t, shape in ((grad_pred, (V, r)), (grad_succ, (V, r)), (grad_wh, (r, H))):
+        if t is None:
+            t = torch.zeros(shape, dtype=torch.float32, device=dev)
+        elif t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise TypeError(f"gradient buffers must be contiguous float32 {shape}")
+        grads.append(t)
+    ce = torch.empty(N, dtype=torch.float32, device=dev) if want_ce else None
+    valid = torch.empty(N, dtype=torch.uint8, device=dev) if want_ce else None
+    if workspace is None:
+        workspace = make_workspace(OP_SELECTOR_CE_BACKWARD, N, H, V, r, K, dev)
+    st = _lib.dflash2_selector_ce_backward(_dtype_code(h), N, H, V, r, K, _ptr(h), _ptr(w_h), _ptr(cb_pred),
+                                           _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals), _ptr(pred_ids),
+                                           _ptr(gold_ids), _ptr(force), _ptr(gold_logit), _ptr(grad_ce),
+                                           _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]), _ptr(ce), _ptr(valid),
+                                           _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "dflash2_selector_ce_backward")
+    return grads[0], grads[1], grads[2], ce, valid
 
 
 def read_device_status(workspace: torch.Tensor) -> int:

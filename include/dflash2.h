@@ -74,7 +74,8 @@ typedef enum { DFLASH2_F32 = 0, DFLASH2_BF16 = 1 } dflash2_dtype;
 typedef enum {
     DFLASH2_OP_UNARY_TOPK = 0,
     DFLASH2_OP_SELECTOR_WALK = 1,
-    DFLASH2_OP_SELECTOR_TF = 2
+    DFLASH2_OP_SELECTOR_TF = 2,
+    DFLASH2_OP_SELECTOR_CE_BACKWARD = 3
 } dflash2_op;
 
 /* Kernel limits (sizes beyond them return DFLASH2_ERR_UNSUPPORTED). */
@@ -226,6 +227,42 @@ dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidd
                                          int32_t *out_best_ids, float *out_ce,
                                          uint8_t *out_valid, void *workspace,
                                          size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of the teacher-forced selector CE ([verl PR] "Selector training
+ * objective": the selector's inputs are detached, so the CE trains only the
+ * selector's own parameters; [SpecForge] "Selector objective and schedule",
+ * the stop-gradient switch; [Speculators] "Training Objective", the forced
+ * set).  With the forced set C', valid rows and CE exactly as in
+ * dflash2_selector_score_tf (gold_ids required), and L = sum over valid rows
+ * of grad_ce[n] * CE[n], ADDS dL/dA into grad_pred, dL/dB into grad_succ and
+ * dL/dW_H into grad_wh.  h and the unary logits (cand_vals, gold_logit) are
+ * constants: no gradient flows into them.
+ *   h [N, H], w_h [r, H], cb_pred/cb_succ [V, r]: dtype
+ *   cand_ids [N, K] int32, cand_vals [N, K] float32, pred_ids [N] int32,
+ *   gold_ids [N] int32; force [N] uint8 or NULL; gold_logit [N] float32,
+ *   required when force is given; grad_ce [N] float32 (dL/dCE per row, e.g.
+ *   the loss weight over the number of valid rows)
+ *   grad_pred [V, r], grad_succ [V, r], grad_wh [r, H]: float32, accumulated
+ *   into (zero them for a fresh gradient); distinct, and overlapping no input
+ *   and not the workspace.  The adds are float atomics: the summation order,
+ *   and so the last bits, may differ from call to call.  They must be
+ *   ordinary device memory (not host-mapped).
+ *   out_ce [N] float32, out_valid [N] uint8: optional (NULL to skip), as in
+ *   dflash2_selector_score_tf
+ *   workspace: at least dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_CE_BACKWARD, ...)
+ * Rows whose ids fall outside [0, V) are excluded (no gradient, valid 0) and
+ * set the device status word.
+ */
+dflash2_status dflash2_selector_ce_backward(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,
+                                            int32_t rank, int32_t top_k, const void *h, const void *w_h,
+                                            const void *cb_pred, const void *cb_succ,
+                                            const int32_t *cand_ids, const float *cand_vals,
+                                            const int32_t *pred_ids, const int32_t *gold_ids,
+                                            const uint8_t *force, const float *gold_logit,
+                                            const float *grad_ce, float *grad_pred, float *grad_succ,
+                                            float *grad_wh, float *out_ce, uint8_t *out_valid,
+                                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Workspace bytes an operation needs (host only, no device call).  `op` is a

@@ -235,3 +235,26 @@ def compare_tf(gpu, ref, cand_ids):
             fails += 1
             msgs.append("excluded rows carry a CE")
     return fails, flags, msgs
+
+
+# Gradient tolerance.  The GPU sums in float32 (scores, softmax, atomics in
+# any order, the MFMA contraction over rows): its error is ~1e-7 of the terms,
+# at most ~1e-5 of the tensor's largest entry after N ~ 4096 row sums, and
+# sums that cancel keep that absolute error.  So an entry passes within
+# GRAD_RTOL of itself plus GRAD_SCALE_ATOL of the tensor's largest magnitude.
+GRAD_RTOL, GRAD_SCALE_ATOL = 1e-3, 2e-5
+
+
+def compare_grads(gpu: dict, ref: dict):
+    """gpu/ref: name -> array.  Returns (fails, messages)."""
+    fails, msgs = 0, []
+    for k, r in ref.items():
+        g = np.asarray(gpu[k], np.float64)
+        scale = float(np.abs(r).max()) if r.size else 0.0
+        ok = np.abs(g - r) <= GRAD_RTOL * np.abs(r) + GRAD_SCALE_ATOL * scale
+        if not ok.all():
+            bad = np.argwhere(~ok)
+            fails += len(bad)
+            i = tuple(bad[0])
+            msgs.append(f"{k}: {len(bad)} entries off, e.g. {i}: {g[i]} vs {r[i]} (scale {scale})")
+    return fails, msgs

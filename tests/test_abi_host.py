@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert sorted(D.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -163,10 +163,45 @@ def test_selector_tf_rules():
     assert tf(scores=fake(14)) == ALIAS
 
 
+def bwd(dtype=1, n=16, h=256, v=1000, r=32, k=16, gold=fake(7), force=None, gl=None, gce=fake(9), gp=fake(20),
+        gs=fake(40), gw=fake(60), ce=None, valid=None, ws=fake(12), wsb=None, hp=fake(0)):
+    if wsb is None:
+        wsb = D.workspace_bytes(D.OP_SELECTOR_CE_BACKWARD, n, h, v, r, k) if n > 0 else 1 << 20
+    return L.dflash2_selector_ce_backward(dtype, n, h, v, r, k, hp, fake(1), fake(2), fake(3), fake(4), fake(5),
+                                          fake(6), gold, force, gl, gce, gp, gs, gw, ce, valid, ws, wsb, None)
+
+
+@no_gpu
+def test_selector_ce_backward_rules():
+    # the scorer's size rules
+    assert bwd(k=0) == SHAPE and bwd(n=0) == SHAPE and bwd(k=2000) == SHAPE
+    assert bwd(k=100) == UNSUP and bwd(r=20) == UNSUP and bwd(h=96) == UNSUP
+    assert bwd(dtype=4) == DTYPE
+    # gold ids, the upstream gradient and all three gradient buffers are required
+    for kw in ("gold", "gce", "gp", "gs", "gw", "ws", "hp"):
+        assert bwd(**{kw: None}) == NULL, kw
+    assert bwd(force=fake(8)) == NULL            # forcing needs the gold logits
+    assert bwd(wsb=8) == WS
+    # the three gradients are distinct and overlap no input and no output
+    assert bwd(gs=fake(20)) == ALIAS             # dB on dA
+    assert bwd(gw=fake(20)) == ALIAS             # dW on dA
+    assert bwd(gp=fake(2)) == ALIAS              # dA on the predecessor codebook
+    assert bwd(gw=fake(0)) == ALIAS              # dW on h
+    assert bwd(gs=fake(12)) == ALIAS             # dB on the workspace
+    assert bwd(ce=fake(9)) == ALIAS              # ce on grad_ce
+
+
 def test_workspace_sizes():
     # walk / TF: status header plus the float32 context projection
     assert D.workspace_bytes(D.OP_SELECTOR_WALK, 8, 4096, 151936, 256, 16) == 256 + 8 * 256 * 4
     assert D.workspace_bytes(D.OP_SELECTOR_TF, 4096, 4096, 151936, 256, 16) == 256 + 4096 * 256 * 4
+    # CE backward: g (then gv), ag and dg rows; per-entry weight, target and
+    # order for N (K + 1) entries; counts and offsets over 2V + 1 targets; scan
+    # tile prefixes; each part rounded up to 256 bytes
+    up = lambda x: (x + 255) // 256 * 256
+    N, V, r, K = 4096, 151936, 256, 16
+    want = 256 + 3 * up(N * r * 4) + 3 * up(N * (K + 1) * 4) + 2 * up((2 * V + 1) * 4) + up(-(-(2 * V + 1) // 4096) * 4)
+    assert D.workspace_bytes(D.OP_SELECTOR_CE_BACKWARD, N, 4096, V, r, K) == want
     # top-K: one sorted list of K 8-byte keys per row per vocabulary slice
     b = D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16)
     assert b > 256 and (b - 256) % (8 * 16 * 8) == 0

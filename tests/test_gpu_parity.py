@@ -8,7 +8,7 @@ import torch
 
 from block_draft_head_amd.inputs import Workload, make_inputs, to_storage
 from oracle import dflash2_oracle as O
-from tests.helpers import (act_ok, close, compare_sample, compare_tf, compare_topk, compare_walk, conv_term_scale,
+from tests.helpers import (act_ok, close, compare_grads, compare_sample, compare_tf, compare_topk, compare_walk, conv_term_scale,
                            to_dev,
                            to_np)
 
@@ -405,6 +405,89 @@ def test_out_of_range_ids_are_flagged_not_read(D):
     _, best, _, _ = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids),
                                         to_dev(vals), to_dev(pred), workspace=ws3)
     assert D.read_device_status(ws3) == 8 and int(best[5]) == -1 and int(best[4]) >= 0
+
+
+# -------------------------------------------------------- selector CE backward
+
+CE_BWD_CASES = [
+    # (N, H, V, r, K, dtype): ragged rows, rank and vocab; ids shared by many rows
+    (128, 256, 4096, 32, 16, "f32"), (200, 256, 1000, 256, 16, "bf16"), (333, 512, 3000, 40, 20, "bf16"),
+    (64, 256, 500, 512, 64, "bf16"), (37, 256, 800, 264, 33, "f32"), (24, 256, 300, 8, 1, "bf16"),
+    (1, 256, 100, 16, 5, "bf16"), (1000, 320, 2000, 256, 16, "bf16"),
+]
+
+
+def ce_bwd_inputs(N, H, V, r, K, dtype, seed):
+    w = wl(n_blocks=N, block_size=1, hidden=H, vocab=V, rank=r, top_k=K, dtype=dtype)
+    inp = make_inputs(w, seed=seed, fields=["h", "w_h", "cb_pred", "cb_succ", "pred", "gold", "force"])
+    if dtype == "f32":
+        inp["cb_pred"] *= np.float32(6)
+        inp["cb_succ"] *= np.float32(6)
+    rng = np.random.default_rng(seed + N)
+    ids, vals = rand_cands(rng, N, V, K)
+    gold = inp["gold"].copy()
+    gold[::3] = ids[::3, K // 2]
+    glog = rng.standard_normal(N).astype(np.float32)
+    wgt = (rng.random(N) + 0.5).astype(np.float32)
+    return inp, ids, vals, gold, glog, wgt
+
+
+@pytest.mark.parametrize("N,H,V,r,K,dtype", CE_BWD_CASES)
+def test_selector_ce_backward(D, N, H, V, r, K, dtype):
+    log(f"ce backward N={N} H={H} V={V} r={r} K={K} {dtype}")
+    inp, ids, vals, gold, glog, wgt = ce_bwd_inputs(N, H, V, r, K, dtype, seed=17)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    # the gradients are added into what the buffers hold
+    rng = np.random.default_rng(5)
+    pre = [(rng.standard_normal(s) * 1e-3).astype(np.float32) for s in ((V, r), (V, r), (r, H))]
+    gp, gs, gw, ce, valid = D.selector_ce_backward(
+        dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids), to_dev(vals), dev["pred"], to_dev(gold),
+        to_dev(wgt), force=dev["force"], gold_logit=to_dev(glog), grad_pred=to_dev(pre[0]), grad_succ=to_dev(pre[1]),
+        grad_wh=to_dev(pre[2]))
+    dA, dB, dW, _, rvalid = O.selector_ce_backward(inp["h"], inp["w_h"], inp["cb_pred"], inp["cb_succ"], ids,
+                                                   vals.astype(np.float64), inp["pred"], dtype, gold, inp["force"],
+                                                   glog.astype(np.float64), wgt.astype(np.float64))
+    got = {"dA": to_np(gp) - pre[0], "dB": to_np(gs) - pre[1], "dW": to_np(gw) - pre[2]}
+    fails, msgs = compare_grads(got, {"dA": dA, "dB": dB, "dW": dW})
+    assert np.array_equal(to_np(valid), rvalid)
+    g64 = O.context_projection(inp["h"], inp["w_h"], dtype)
+    _, _, rce, _ = O.selector_score_tf(g64, inp["cb_pred"], inp["cb_succ"], ids, vals.astype(np.float64),
+                                       inp["pred"], dtype, gold_ids=gold, force=inp["force"],
+                                       gold_logit=glog.astype(np.float64))
+    assert close(to_np(ce), rce).all()
+    log(f"  valid {int(rvalid.sum())}/{N} fails={fails}")
+    assert fails == 0, msgs
+    if K > 1 and rvalid.any():
+        assert np.abs(dB).max() > 0 and np.abs(dW).max() > 0
+
+
+def test_selector_ce_backward_accumulates_and_skips_bad_rows(D):
+    N, H, V, r, K = 96, 256, 700, 64, 8
+    inp, ids, vals, gold, glog, wgt = ce_bwd_inputs(N, H, V, r, K, "bf16", seed=23)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    ws = D.make_workspace(D.OP_SELECTOR_CE_BACKWARD, N, H, V, r, K, "cuda")
+    pred = inp["pred"].copy()
+    pred[7] = V  # out of range: that row is excluded and flagged
+    args = (dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids), to_dev(vals), to_dev(pred),
+            to_dev(gold), to_dev(wgt))
+    gp, gs, gw, ce, valid = D.selector_ce_backward(*args, force=dev["force"], gold_logit=to_dev(glog), workspace=ws)
+    assert D.read_device_status(ws) == 8 and int(valid[7]) == 0 and float(ce[7]) == 0.0
+    # a second call adds the same gradient again
+    D.selector_ce_backward(*args, force=dev["force"], gold_logit=to_dev(glog), grad_pred=gp, grad_succ=gs,
+                           grad_wh=gw, want_ce=False, workspace=ws)
+    pred_ok = pred.copy()
+    pred_ok[7] = 0
+    wz = wgt.copy()
+    wz[7] = 0  # the excluded row carries no weight
+    dA, dB, dW, _, rvalid = O.selector_ce_backward(inp["h"], inp["w_h"], inp["cb_pred"], inp["cb_succ"], ids,
+                                                   vals.astype(np.float64), pred_ok, "bf16", gold, inp["force"],
+                                                   glog.astype(np.float64), wz.astype(np.float64))
+    fails, msgs = compare_grads({"dA": to_np(gp), "dB": to_np(gs), "dW": to_np(gw)},
+                                {"dA": 2 * dA, "dB": 2 * dB, "dW": 2 * dW})
+    assert fails == 0, msgs
+    # no force given: rows whose gold is outside the set are excluded
+    _, _, _, _, v2 = D.selector_ce_backward(*args[:6], dev["pred"], to_dev(gold), to_dev(wgt))
+    assert np.array_equal(to_np(v2), np.isin(np.arange(N), np.flatnonzero((ids == gold[:, None]).any(1))))
 
 
 # -------------------------------------------------------------- end to end

@@ -18,7 +18,7 @@ import torch
 
 from block_draft_head_amd.inputs import WORKLOAD_ORDER, WORKLOADS, make_inputs
 from oracle import dflash2_oracle as O
-from tests.helpers import (act_ok, close, compare_tf, compare_topk, compare_walk, conv_term_scale, oracle_logits_rows,
+from tests.helpers import (act_ok, close, compare_grads, compare_tf, compare_topk, compare_walk, conv_term_scale, oracle_logits_rows,
                            to_dev, to_np)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -113,6 +113,22 @@ def test_full_size_workload(D, name):
         assert fails == 0, msgs
         # forced rows always hold gold; the rest only when it is a candidate
         assert 0.75 < cov < 0.85
+        # the selector CE's gradients, mean over the valid rows
+        log(f"[{name}] selector CE backward")
+        wgt = np.full(N, 1.0 / max(1, int(ref[3].sum())), np.float32)
+        ws_b = D.make_workspace(D.OP_SELECTOR_CE_BACKWARD, N, H, V, r, K, "cuda")
+        gp, gs, gw, ce, valid = D.selector_ce_backward(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids,
+                                                       vals, dev["pred"], gold, to_dev(wgt), force=dev["force"],
+                                                       gold_logit=gl, workspace=ws_b)
+        assert D.read_device_status(ws_b) == 0
+        dA, dB, dW, _, rvalid = O.selector_ce_backward(inp["h"], inp["w_h"], inp["cb_pred"], inp["cb_succ"], gids,
+                                                       u_at, inp["pred"], dt, inp["gold"], inp["force"],
+                                                       gold_exact, wgt.astype(np.float64))
+        assert np.array_equal(to_np(valid), rvalid)
+        fails, msgs = compare_grads({"dA": to_np(gp), "dB": to_np(gs), "dW": to_np(gw)},
+                                    {"dA": dA, "dB": dB, "dW": dW})
+        log(f"[{name}] CE backward: fails {fails}")
+        assert fails == 0, msgs
     else:
         ws_sel = D.make_workspace(D.OP_SELECTOR_WALK, N, H, V, r, K, "cuda")
         path, ps = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"],
