@@ -541,3 +541,62 @@ def selector_ce_backward(h, w_h, cb_pred, cb_succ, cand_ids, cand_u, pred_ids, d
         np.add.at(dB, ids, d[:, None] * ag[None, :])
     dW = dg.T @ widen(h, dtype)
     return dA, dB, dW, dg, valid
+
+
+# --------------------------------------------------------------------------
+# unary-logit transforms and candidate metrics
+# --------------------------------------------------------------------------
+#
+# [SpecForge] "Export and serve": the optional output_multiplier and
+# final_logit_softcapping of the draft config act on the unary logits, in
+# local generation and in serving alike.  The page names them and fixes no
+# formula.  READINGS:
+#   * the multiplier scales the raw logit; the softcap then maps x to
+#     c tanh(x / c) (c > 0; 0 = off), so that the cap bounds the final logits;
+#   * candidates, their values and the gold logit are those of the
+#     transformed logits (the transform is increasing for a positive
+#     multiplier, so it never reorders distinct logits).
+# [Explainer] "Problem 1" (recall@1 / recall@16 per position) and
+# [SpecForge] "Selector objective and schedule" (selector_coverage: how often
+# the gold is in the strict unary top-k set): hit[n] = [gold in top-K].
+# [verl PR] "What DFlash2 adds" (validation reports unary candidate recall
+# and target mass): READING: the target mass is the unary softmax
+# probability of the gold token over the full vocabulary,
+# exp(U'(gold) - logsumexp_v U'(v)).
+
+def transform_logits(U, output_multiplier: float = 1.0, softcap: float = 0.0) -> np.ndarray:
+    """U' = softcap(output_multiplier * U), softcap(x) = c tanh(x / c) for
+    c > 0 and the identity for c = 0."""
+    x = np.asarray(U, dtype=np.float64) * float(output_multiplier)
+    if softcap > 0:
+        x = float(softcap) * np.tanh(x / float(softcap))
+    return x
+
+
+def logsumexp_rows(X: np.ndarray) -> np.ndarray:
+    """log sum_v exp(X[n, v]) per row, shifted by the row maximum."""
+    m = X.max(axis=1)
+    return m + np.log(np.exp(X - m[:, None]).sum(axis=1))
+
+
+def unary_topk_ex(h, w_lm, top_k: int, dtype: str, gold_ids=None, output_multiplier: float = 1.0,
+                  softcap: float = 0.0):
+    """The candidate lattice over the transformed logits, with the metrics
+    of the same pass.  Returns (ids [N, K], vals [N, K], lse [N], gold_logit,
+    gold_prob, hit), the last three None without gold ids."""
+    if not (output_multiplier > 0 and np.isfinite(output_multiplier)):
+        raise ValueError("output_multiplier must be positive and finite")
+    if not (softcap >= 0 and np.isfinite(softcap)):
+        raise ValueError("final_logit_softcapping must be >= 0 and finite")
+    U = transform_logits(lm_logits(h, w_lm, dtype), output_multiplier, softcap)
+    if not (1 <= top_k <= U.shape[1]):
+        raise ValueError("selector_top_k must be in [1, vocab_size]")
+    ids, vals = topk_of(U, top_k)
+    lse = logsumexp_rows(U)
+    gl = prob = hit = None
+    if gold_ids is not None:
+        g = np.asarray(gold_ids)
+        gl = U[np.arange(U.shape[0]), g]
+        prob = np.exp(gl - lse)
+        hit = (ids == g[:, None]).any(axis=1).astype(np.uint8)
+    return ids, vals, lse, gl, prob, hit

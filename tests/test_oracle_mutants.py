@@ -43,6 +43,11 @@ MUTANTS = {
     "predecessor gradient without the context": ("dA[p] += g[n] * v", "dA[p] += v"),
     "successor gradient sent to the predecessor row": ("np.add.at(dB, ids, d[:, None]", "np.add.at(dB, np.full_like(ids, p), d[:, None]"),
     "projection gradient against the wrong factor": ("dg[n] = A[p] * v", "dg[n] = g[n] * v"),
+    "softcap before the multiplier": ("    x = np.asarray(U, dtype=np.float64) * float(output_multiplier)\n    if softcap > 0:\n        x = float(softcap) * np.tanh(x / float(softcap))", "    x = np.asarray(U, dtype=np.float64)\n    if softcap > 0:\n        x = float(softcap) * np.tanh(x / float(softcap))\n    x = x * float(output_multiplier)"),
+    "softcap without the inner divide": ("x = float(softcap) * np.tanh(x / float(softcap))", "x = float(softcap) * np.tanh(x)"),
+    "log-sum-exp without its shift added back": ("return m + np.log(np.exp(X - m[:, None]).sum(axis=1))", "return np.log(np.exp(X - m[:, None]).sum(axis=1))"),
+    "target mass against the wrong normaliser": ("prob = np.exp(gl - lse)", "prob = np.exp(gl - lse) * U.shape[1] / (U.shape[1] + 1)"),
+    "hit taken over the first candidate only": ("hit = (ids == g[:, None]).any(axis=1)", "hit = (ids[:, :1] == g[:, None]).any(axis=1)"),
     "backward keeps rows the forward excludes": ("        else:\n            continue\n        valid[n] = 1\n        ag", "        else:\n            pass\n        valid[n] = 1\n        ag"),
 }
 

@@ -655,3 +655,86 @@ def test_ce_backward_closed_forms():
     z = O.selector_ce_backward(h, w_h, A, B, ids2, np.zeros((N, K)), pred, "f32", far, np.zeros(N, np.uint8),
                                np.zeros(N), w)
     assert not z[4].any() and all(np.all(t == 0) for t in z[:4])
+
+
+# ---------------------------------------------------------------- unary transforms and metrics
+
+def _lm_case(rng, N=6, H=16, V=40, scale=1.0):
+    h = rng.standard_normal((N, H)).astype(np.float32)
+    w = (rng.standard_normal((V, H)) * scale).astype(np.float32)
+    return h, w
+
+
+def test_untransformed_ex_is_the_plain_candidate_lattice():
+    rng = np.random.default_rng(51)
+    h, w = _lm_case(rng)
+    gold = rng.integers(0, 40, 6)
+    ids, vals, gl = O.unary_topk(h, w, 7, "f32", gold_ids=gold)
+    ids2, vals2, lse, gl2, prob, hit = O.unary_topk_ex(h, w, 7, "f32", gold_ids=gold)
+    assert np.array_equal(ids, ids2) and np.array_equal(vals, vals2) and np.array_equal(gl, gl2)
+
+
+def test_softcap_is_bounded_odd_and_linear_near_zero():
+    x = np.linspace(-400, 400, 2001)
+    for m, c in ((1.0, 30.0), (2.5, 10.0), (0.5, 50.0)):
+        y = O.transform_logits(x, m, c)
+        assert np.all(np.abs(y) <= c)                       # the cap bounds the final logits
+        assert np.allclose(y, -O.transform_logits(-x, m, c), rtol=0, atol=1e-12)
+        assert np.all(np.diff(y) >= 0)
+        small = np.abs(m * x) < 1e-3 * c
+        assert np.allclose(y[small], m * x[small], rtol=1e-6, atol=0)
+    # a vanishing cap is off, a huge cap is the multiplier alone
+    assert np.array_equal(O.transform_logits(x, 3.0, 0.0), 3.0 * x)
+    assert np.allclose(O.transform_logits(x, 3.0, 1e9), 3.0 * x, rtol=1e-9, atol=0)
+    # tanh(1) at x = c / m
+    assert abs(O.transform_logits(np.array([4.0]), 2.5, 10.0)[0] - 10.0 * math.tanh(1.0)) < 1e-12
+
+
+def test_transforms_keep_the_candidates_and_rescale_the_values():
+    rng = np.random.default_rng(52)
+    h, w = _lm_case(rng, N=8, V=60, scale=3.0)
+    gold = rng.integers(0, 60, 8)
+    ids0, vals0, _ = O.unary_topk(h, w, 10, "f32", gold_ids=gold)
+    for m, c in ((2.0, 0.0), (1.0, 5.0), (0.3, 2.0)):
+        ids, vals, lse, gl, prob, hit = O.unary_topk_ex(h, w, 10, "f32", gold_ids=gold, output_multiplier=m,
+                                                        softcap=c)
+        assert np.array_equal(ids, ids0)
+        want = m * vals0 if c == 0 else c * np.tanh(m * vals0 / c)
+        np.testing.assert_allclose(vals, want, rtol=1e-13, atol=1e-13)
+    with pytest.raises(ValueError):
+        O.unary_topk_ex(h, w, 10, "f32", output_multiplier=-1.0)
+    with pytest.raises(ValueError):
+        O.unary_topk_ex(h, w, 10, "f32", softcap=-2.0)
+
+
+def test_metrics_by_brute_force_on_a_tiny_vocabulary():
+    # target probabilities over every possible gold sum to one; the hit flag,
+    # the log-sum-exp and the probability by scalar loops
+    rng = np.random.default_rng(53)
+    N, H, V, K = 3, 5, 9, 4
+    h, w = _lm_case(rng, N, H, V, scale=2.0)
+    for m, c in ((1.0, 0.0), (1.7, 3.0)):
+        total = np.zeros(N)
+        for g in range(V):
+            gold = np.full(N, g)
+            ids, vals, lse, gl, prob, hit = O.unary_topk_ex(h, w, K, "f32", gold_ids=gold, output_multiplier=m,
+                                                            softcap=c)
+            total += prob
+            for n in range(N):
+                logits = [m * sum(float(h[n, i]) * float(w[v, i]) for i in range(H)) for v in range(V)]
+                if c:
+                    logits = [c * math.tanh(x / c) for x in logits]
+                z = sum(math.exp(x) for x in logits)
+                assert abs(lse[n] - math.log(z)) < 1e-12
+                assert abs(prob[n] - math.exp(logits[g]) / z) < 1e-12
+                ranked = sorted(range(V), key=lambda v: (-logits[v], v))[:K]
+                assert hit[n] == (g in ranked)
+        np.testing.assert_allclose(total, 1.0, rtol=0, atol=1e-12)
+
+
+def test_log_sum_exp_of_equal_logits_and_of_a_dominant_one():
+    U = np.zeros((2, 1000))
+    U[1, 7] = 800.0   # would overflow without the shift
+    lse = O.logsumexp_rows(U)
+    assert abs(lse[0] - math.log(1000)) < 1e-12
+    assert abs(lse[1] - 800.0) < 1e-12
