@@ -46,6 +46,11 @@ def parse():
                          "(temperature 1, a fixed generator key)")
     ap.add_argument("--train", action="store_true",
                     help="teacher-forced workloads: the step also runs the selector CE backward")
+    ap.add_argument("--metrics", action="store_true",
+                    help="the LM head also forms the full-vocabulary log-sum-exp and, on teacher-forced "
+                         "workloads, the gold's probability and top-K hit (recall@K, target mass, coverage)")
+    ap.add_argument("--output-multiplier", type=float, default=1.0)
+    ap.add_argument("--softcap", type=float, default=0.0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
@@ -187,8 +192,18 @@ def main():
         D.conv_prepare(dev["h"], dev["w_proj"], dev["base"], bs, T, gs, out=x_out, k_post=k_post)
         D.conv_finish(dev["y"], k_post, dev["base"], bs, T, gs, out=y_out)
 
+    transformed = args.metrics or args.output_multiplier != 1.0 or args.softcap != 0.0
+    metrics_out = {}
+
     def op_lmhead():
-        return D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=gold, workspace=ws_topk)
+        if not transformed:
+            return D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=gold, workspace=ws_topk)
+        ids, vals, gl, lse, prob, hit = D.unary_topk_ex(dev["h"], dev["w_lm"], K, gold_ids=gold,
+                                                        output_multiplier=args.output_multiplier,
+                                                        softcap=args.softcap, want_lse=args.metrics,
+                                                        want_metrics=args.metrics, workspace=ws_topk)
+        metrics_out.update(lse=lse, prob=prob, hit=hit)
+        return ids, vals, gl
 
     def op_selector(ids, vals, gl):
         if tf_mode:
@@ -286,6 +301,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    metrics = None
+    if args.metrics:
+        metrics = {"mean_log_sum_exp": float(metrics_out["lse"].mean())}
+        if metrics_out.get("hit") is not None:
+            hit = metrics_out["hit"].float()
+            metrics.update({"recall_at_k": float(hit.mean()), "coverage": float(hit.mean()),
+                            "target_mass": float(metrics_out["prob"].mean())})
+
     lm_bytes, lm_flops = lmhead_work(w)
     lm_ms = op_ms["lmhead"]
     mfma_bound = lm_flops / lm_bytes > (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) and w.dtype == "bf16"
@@ -320,11 +343,14 @@ def main():
         "config": {"workload": w.name, "n_blocks": w.n_blocks, "block_size": bs, "hidden": H, "vocab": V,
                    "taps": T, "group_size": gs, "rank": r, "top_k": K, "mode": w.mode,
                    "selector": ("teacher-forced + CE backward" if args.train else "teacher-forced") if tf_mode
-                   else args.selector},
+                   else args.selector,
+                   "unary": {"output_multiplier": args.output_multiplier, "softcap": args.softcap,
+                             "metrics": args.metrics}},
         "roofline": roof,
         "ops_ms": op_ms,
         "selector_plus_conv_over_lmhead": (op_ms["conv"] + op_ms["selector"]) / lm_ms,
         "tf_ms": tf_ms,
+        "unary_metrics": metrics,
         "ce_backward": backward_report(w, bwd_ms) if tf_mode else None,
         "tf_replays_walk": replay_ok,
         "wall_s_timed": wall,

@@ -150,6 +150,38 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
                                       out_vals, out_gold_logit, workspace, (hipStream_t)stream));
 }
 
+dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab, int32_t top_k,
+                                     const void *h, const void *w_lm, const int32_t *gold_ids,
+                                     float output_multiplier, float final_logit_softcapping, int32_t *out_ids,
+                                     float *out_vals, float *out_gold_logit, float *out_lse, float *out_gold_prob,
+                                     uint8_t *out_gold_hit, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    if (!dtype_ok(dtype)) return DFLASH2_ERR_DTYPE;
+    if (n_rows < 1 || hidden < 1 || vocab < 1) return DFLASH2_ERR_SHAPE;
+    if (top_k < 1 || top_k > vocab) return DFLASH2_ERR_SHAPE;
+    if (!(output_multiplier > 0.f) || !std::isfinite(output_multiplier)) return DFLASH2_ERR_SHAPE;
+    if (!(final_logit_softcapping >= 0.f) || !std::isfinite(final_logit_softcapping)) return DFLASH2_ERR_SHAPE;
+    if (top_k > DFLASH2_MAX_TOP_K || !hidden_supported(hidden) || n_rows > INT_MAX)
+        return DFLASH2_ERR_UNSUPPORTED;
+    if (!h || !w_lm || !out_ids || !out_vals || !workspace) return DFLASH2_ERR_NULL;
+    if (gold_ids && !out_gold_logit) return DFLASH2_ERR_NULL;
+    if ((out_gold_prob || out_gold_hit) && !gold_ids) return DFLASH2_ERR_NULL;
+    if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_UNARY_TOPK, n_rows, hidden, vocab, 0, top_k))
+        return DFLASH2_ERR_WORKSPACE;
+    const size_t nk = (size_t)n_rows * top_k, n = (size_t)n_rows;
+    struct Span { const void *p; size_t b; };
+    const Span outs[] = {{out_ids, nk * 4}, {out_vals, nk * 4}, {out_gold_logit, out_gold_logit ? n * 4 : 0},
+                         {out_lse, out_lse ? n * 4 : 0}, {out_gold_prob, out_gold_prob ? n * 4 : 0},
+                         {out_gold_hit, out_gold_hit ? n : 0}, {workspace, workspace_bytes}};
+    constexpr size_t no = sizeof(outs) / sizeof(outs[0]);
+    for (size_t i = 0; i < no; ++i)
+        for (size_t j = i + 1; j < no; ++j)
+            if (overlaps(outs[i].p, outs[i].b, outs[j].p, outs[j].b)) return DFLASH2_ERR_ALIAS;
+    const UnaryMetrics um{output_multiplier, final_logit_softcapping, out_lse, out_gold_prob, out_gold_hit};
+    return launched(launch_unary_topk(dtype, n_rows, hidden, vocab, top_k, h, w_lm, gold_ids, out_ids, out_vals,
+                                      out_gold_logit, workspace, (hipStream_t)stream, &um));
+}
+
 dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,
                                      int32_t vocab, int32_t rank, int32_t top_k, const void *h,
                                      const void *w_h, const void *cb_pred, const void *cb_succ,

@@ -26,6 +26,7 @@ struct LmheadPlan {
     int merge_rows;
     size_t lds, merge_lds, partial_bytes;
     size_t tiles_offset;  // big: byte offset of the exact-path tile buffers after the partial lists
+    size_t lse_offset;    // byte offset of the per-list log-sum-exp partials (float2 [M][n_lists])
 };
 LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
 
@@ -70,9 +71,18 @@ hipError_t launch_conv_prepare(int dtype, int64_t N, int bs, int H, int taps, in
                                hipStream_t stream);
 hipError_t launch_conv_finish(int dtype, int64_t N, int bs, int H, int taps, int gs, const void *y,
                               const float *k_post, const void *base, void *y_out, hipStream_t stream);
+// Unary-logit transform (mult, then softcap cap; 1 and 0: none) and the
+// optional per-row metrics of the same pass.
+struct UnaryMetrics {
+    float mult, cap;
+    float *lse;        // [M] log-sum-exp of the transformed logits over the vocabulary, or null
+    float *gold_prob;  // [M] softmax probability of the gold id, or null
+    uint8_t *hit;      // [M] gold id among the top K, or null
+};
 hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const void *h, const void *w,
                              const int32_t *gold, int32_t *out_ids, float *out_vals,
-                             float *gold_logit, void *workspace, hipStream_t stream);
+                             float *gold_logit, void *workspace, hipStream_t stream,
+                             const UnaryMetrics *metrics = nullptr);
 hipError_t launch_context_proj(int dtype, int64_t N, int H, int r, const void *h, const void *w_h,
                                float *g, uint32_t *status, hipStream_t stream);
 hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, int r, int K,

@@ -17,6 +17,37 @@ namespace dflash2 {
 
 constexpr int kMergeChunk = 512;
 
+// ---------------------------------------------------------------- unary transform, log-sum-exp
+// U' = softcap(mult * U), softcap(x) = cap tanh(x / cap) (cap 0: off).  The
+// transform is increasing, so the kernels select on raw logits and apply it
+// to the K values; the log-sum-exp runs over the transformed logits.
+struct UnaryEpi {
+    float mult, cap;
+    float2 *lse_part;  // per (row, list): running max and sum of exp(U' - max); null: not wanted
+};
+__device__ __forceinline__ float unary_transform(float x, float mult, float cap) {
+    x *= mult;
+    return cap > 0.f ? cap * tanhf(x / cap) : x;
+}
+// (m, s) += one transformed logit t
+__device__ __forceinline__ void lse_add(float &m, float &s, float t) {
+    const float mn = fmaxf(m, t);
+    s = s * __expf(m - mn) + __expf(t - mn);
+    m = mn;
+}
+// (m, s) += (m2, s2)
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -__builtin_inff()) return;  // both empty
+    s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+    m = mn;
+}
+// (m, s) over the 16 lanes of this lane's quarter (lanes with equal lane / 16)
+__device__ __forceinline__ void lse_merge16(float &m, float &s) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) lse_merge(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
+}
+
 // Bitonic sort, descending, of 128 keys held two per lane (element 2*lane+h).
 __device__ __forceinline__ void bitonic128_desc(uint64_t &x0, uint64_t &x1) {
     const int l = lane_id();
@@ -115,11 +146,11 @@ __device__ __forceinline__ uint64_t shrink_candidates(uint64_t *B, int &n, int K
     return readlane_u64(top, K - 1);
 }
 
-template <typename T, int NW, int P>
+template <typename T, int NW, int P, bool LSE>
 __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
     const T *__restrict__ h, const T *__restrict__ w, int M, int H, int V, int K, int n_tiles,
     const int32_t *__restrict__ gold, float *__restrict__ gold_logit, uint64_t *__restrict__ partial,
-    uint32_t *__restrict__ status) {
+    uint32_t *__restrict__ status, UnaryEpi ue) {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int KC = 16 / (int)sizeof(T);
     constexpr int KS = 4 * KC;
@@ -129,6 +160,8 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
     uint64_t *scratch = bufs + NW * 8 * kCandCap;                                // [NW][128]
     int *cnts = reinterpret_cast<int *>(scratch + NW * 128);                     // [NW][8]
     int *qctr = cnts + NW * 8;
+    float2 *lse_sm = reinterpret_cast<float2 *>(smem + (size_t)S * 32 * 16 + (size_t)NW * (8 * kCandCap + 128) * 8 +
+                                                (size_t)NW * 8 * 4 + 16);  // [NW][8]
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     if (blockIdx.x == 0 && threadIdx.x == 0 && status) *status = 0u;
 
@@ -156,6 +189,12 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
     int cnt[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) cnt[r] = 0;
+    float lm[4], ls[4];  // log-sum-exp of rows 4 q + e over this lane's logits
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lm[e] = -__builtin_inff();
+        ls[e] = 0.f;
+    }
     uint64_t *myscratch = scratch + wave * 128;
     // Shrink row r's candidates and raise its threshold.
     auto compact = [&](int r) {
@@ -199,6 +238,9 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
                 const bool ok = row < M && v < V;
                 const uint64_t key = ok ? make_key(acc[e], (uint32_t)v) : 0ull;
                 if (ok && grow[e] == v) gold_logit[row] = acc[e];
+                if constexpr (LSE) {
+                    if (ok) lse_add(lm[e], ls[e], unary_transform(acc[e], ue.mult, ue.cap));
+                }
                 const bool pass = key > thr[e];
                 const unsigned long long mask = __ballot(pass);
                 const int c0 = __popcll(mask & 0xffffull), c1 = __popcll(mask & 0xffff0000ull);
@@ -222,9 +264,23 @@ __global__ __launch_bounds__(64 * NW) void lmhead_stream_kernel(
         for (int r = 0; r < 8; ++r)
             if (lane == r) cnts[wave * 8 + r] = cnt[r];
     }
+    if constexpr (LSE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lse_merge16(lm[e], ls[e]);
+            if (n == 0 && 4 * q + e < 8) lse_sm[wave * 8 + 4 * q + e] = make_float2(lm[e], ls[e]);
+        }
+    }
     __syncthreads();
     // the workgroup's list per row: top K over every wave's candidates
     for (int row = wave; row < M; row += NW) {
+        if constexpr (LSE) {
+            if (lane == 0) {
+                float m = -__builtin_inff(), sm = 0.f;
+                for (int ww = 0; ww < NW; ++ww) lse_merge(m, sm, lse_sm[ww * 8 + row].x, lse_sm[ww * 8 + row].y);
+                ue.lse_part[(size_t)row * gridDim.x + blockIdx.x] = make_float2(m, sm);
+            }
+        }
         constexpr int R = 2 * NW;
         uint64_t k[R];
 #pragma unroll
@@ -279,12 +335,13 @@ inline int dma_ksplit(int H) {
 }
 
 inline size_t dma_lds_bytes(int H, int KS) {
+    // (plus the log-sum-exp of each wave's rows: kDmaWaves x 8 float2)
     // A fragments (each K share followed by its first two blocks again, read
     // ahead across a tile boundary), rings, candidate buffers, two sets of
     // partial tiles (K split only), merge scratch, counts
     return (size_t)(H / 64 + 2 * KS) * 1024 + (size_t)kDmaWaves * kDmaRing * 2048 +
            (size_t)kDmaWaves * (8 / KS) * kDmaCandCap * 8 + (KS > 1 ? (size_t)2 * kDmaWaves * 1024 : 0) +
-           (size_t)kDmaWaves * 128 * 8 + (size_t)kDmaWaves * 8 * 4 + 16;
+           (size_t)kDmaWaves * 128 * 8 + (size_t)kDmaWaves * 8 * 4 + (size_t)kDmaWaves * 8 * 8 + 16;
 }
 
 template <typename F, int... I>
@@ -311,11 +368,11 @@ __device__ void load_afrag_shares(uint4 *afrag, const uint16_t *__restrict__ A, 
     }
 }
 
-template <int KS>
+template <int KS, bool LSE>
 __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K,
     const int32_t *__restrict__ gold, float *__restrict__ gold_logit, uint64_t *__restrict__ partial,
-    uint32_t *__restrict__ status) {
+    uint32_t *__restrict__ status, UnaryEpi ue) {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int NW = kDmaWaves, NB = kDmaRing, CAP = kDmaCandCap, AH = kDmaAhead, LD = kDmaLead;
     constexpr int G = NW / KS;   // wave groups
@@ -330,6 +387,7 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     f32x4 *parts = reinterpret_cast<f32x4 *>(bufs + NW * OWN * CAP);                // [2][NW][64]
     uint64_t *scratch = reinterpret_cast<uint64_t *>(parts + (KS > 1 ? 2 * NW * 64 : 0));  // [NW][128]
     int *cnts = reinterpret_cast<int *>(scratch + NW * 128);                         // [NW][OWN]
+    float2 *lse_sm = reinterpret_cast<float2 *>(cnts + NW * 8);                     // [NW][8]
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gi = wave / KS, kp = wave % KS;
     if (blockIdx.x == 0 && threadIdx.x == 0 && status) *status = 0u;
@@ -365,6 +423,12 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     int cnt[OWN];
 #pragma unroll
     for (int r = 0; r < OWN; ++r) cnt[r] = 0;
+    float lm[4], ls[4];  // log-sum-exp of rows 4 q + e (e % KS == kp) over this lane's logits
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lm[e] = -__builtin_inff();
+        ls[e] = 0.f;
+    }
     uint64_t *myscratch = scratch + wave * 128;
 
     // copies: lane L of copy j of a block fills row 8 j + L / 8, position L % 8,
@@ -497,6 +561,9 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
                     gval[e] = acc[e];
                     ghit[e] = true;
                 }
+                if constexpr (LSE) {
+                    if (ok) lse_add(lm[e], ls[e], unary_transform(acc[e], ue.mult, ue.cap));
+                }
                 const bool pass = key > thr[e];
                 const unsigned long long mask = __ballot(pass);
                 const int c0 = __popcll(mask & 0xffffull), c1 = __popcll(mask & 0xffff0000ull);
@@ -533,12 +600,30 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
 #pragma unroll
         for (int r = 0; r < OWN; ++r) cnts[wave * OWN + r] = cnt[r];
     }
+    if constexpr (LSE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e % KS != kp) continue;
+            lse_merge16(lm[e], ls[e]);
+            if (n == 0 && 4 * q + e < 8) lse_sm[wave * 8 + 4 * q + e] = make_float2(lm[e], ls[e]);
+        }
+    }
     __syncthreads();
     // row 4 q + e: candidates of wave e % KS of every group, buffer
     // q (4 / KS) + e / KS
     for (int row = wave; row < M; row += NW) {
         constexpr int R = 2 * G;
         const int e = row & 3, sl = (row >> 2) * (4 / KS) + e / KS;
+        if constexpr (LSE) {
+            if (lane == 0) {
+                float m = -__builtin_inff(), sm = 0.f;
+                for (int gg = 0; gg < G; ++gg) {
+                    const int ww = gg * KS + e % KS;
+                    lse_merge(m, sm, lse_sm[ww * 8 + row].x, lse_sm[ww * 8 + row].y);
+                }
+                ue.lse_part[(size_t)row * gridDim.x + blockIdx.x] = make_float2(m, sm);
+            }
+        }
         uint64_t k[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -556,16 +641,17 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
 // vocabulary tiles of its slab; each 128 x 128 logit tile goes through LDS,
 // and wave w merges the new values of rows w, w + 4, ... into their lists
 // (bitonic sort for the first tile, threshold-filtered insertion after).
-template <typename T>
+template <typename T, bool LSE>
 __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
     const T *__restrict__ h, const T *__restrict__ w, int M, int H, int V, int K, int n_vtiles,
     const int32_t *__restrict__ gold, float *__restrict__ gold_logit, uint64_t *__restrict__ partial,
-    uint32_t *__restrict__ status) {
+    uint32_t *__restrict__ status, UnaryEpi ue) {
     using Cfg = TiledCfg<T, 128, 128>;
     constexpr int BIG = Cfg::STAGE_BYTES > Cfg::CTILE_BYTES ? Cfg::STAGE_BYTES : Cfg::CTILE_BYTES;
     extern __shared__ __align__(16) uint8_t smem[];
     float *ctile = reinterpret_cast<float *>(smem);
     uint64_t *lists = reinterpret_cast<uint64_t *>(smem + BIG);  // [128][K]
+    float2 *lse_sm = reinterpret_cast<float2 *>(lists + Cfg::BM * K);  // [128]: row r's, kept by wave r % 4
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int slab = blockIdx.x, n_slabs = gridDim.x, mt = blockIdx.y;
     const int m0 = mt * Cfg::BM;
@@ -573,6 +659,9 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
     const int vt0 = (int)((long long)slab * n_vtiles / n_slabs);
     const int vt1 = (int)((long long)(slab + 1) * n_vtiles / n_slabs);
     for (int i = threadIdx.x; i < Cfg::BM * K; i += blockDim.x) lists[i] = 0ull;
+    if constexpr (LSE) {
+        for (int i = threadIdx.x; i < Cfg::BM; i += blockDim.x) lse_sm[i] = make_float2(-__builtin_inff(), 0.f);
+    }
 
     for (int vt = vt0; vt < vt1; ++vt) {
         const int v0 = vt * Cfg::BN;
@@ -598,6 +687,17 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
                 if (g == va && va < V) gold_logit[gr] = fa;
                 if (g == vb && vb < V) gold_logit[gr] = fb;
             }
+            if constexpr (LSE) {
+                const float ta = va < V ? unary_transform(fa, ue.mult, ue.cap) : -__builtin_inff();
+                const float tb = vb < V ? unary_transform(fb, ue.mult, ue.cap) : -__builtin_inff();
+                const float mx = wave_max_f32(fmaxf(ta, tb));  // column 0 of the tile is always real
+                const float sm = wave_sum_f32((va < V ? __expf(ta - mx) : 0.f) + (vb < V ? __expf(tb - mx) : 0.f));
+                if (lane == 0) {
+                    float2 run = lse_sm[r];
+                    lse_merge(run.x, run.y, mx, sm);
+                    lse_sm[r] = run;
+                }
+            }
             if (vt == vt0) {
                 // element 2l+h after the sort is the (2l+h)-th best of the tile
                 uint64_t x0 = ka, x1 = kb;
@@ -618,6 +718,9 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
         const int gr = m0 + r;
         if (gr >= M) break;
         if (lane < K) partial[((size_t)gr * n_slabs + slab) * K + lane] = lists[r * K + lane];
+        if constexpr (LSE) {
+            if (lane == 0) ue.lse_part[(size_t)gr * n_slabs + slab] = lse_sm[r];
+        }
     }
 }
 
@@ -785,7 +888,9 @@ typedef __attribute__((address_space(3))) uint64_t lu64;
 typedef __attribute__((address_space(3))) float lfloat;
 template <int KL>
 __device__ __attribute__((noinline)) void exact_row_scan(gfloat4 *__restrict__ row4, int nvalid, int v0, bool fresh,
-                                                         gu64 *list, lfloat *thr_out, lu64 *buf) {
+                                                         gu64 *list, lfloat *thr_out, lu64 *buf, lfloat *lse_m,
+                                                         lfloat *lse_s, float mult, float cap) {
+    float rowmax = -__builtin_inff();
     float top[KL];
 #pragma unroll
     for (int j = 0; j < KL; ++j) top[j] = -__builtin_inff();
@@ -800,6 +905,7 @@ __device__ __attribute__((noinline)) void exact_row_scan(gfloat4 *__restrict__ r
                             fmaxf(c + 2 < nvalid ? v4[u].z : -__builtin_inff(),
                                   c + 3 < nvalid ? v4[u].w : -__builtin_inff()));
             if (c >= nvalid) m = -__builtin_inff();
+            rowmax = fmaxf(rowmax, m);
 #pragma unroll
             for (int j = 0; j < KL; ++j) {
                 const float hi = fmaxf(top[j], m);
@@ -809,6 +915,9 @@ __device__ __attribute__((noinline)) void exact_row_scan(gfloat4 *__restrict__ r
         }
     }
     float th = fmaxf(*thr_out, top[KL - 1]);
+    // log-sum-exp of the tile row (transformed logits), shifted by its maximum
+    const float tmax = lse_m ? unary_transform(rowmax, mult, cap) : 0.f;
+    float esum = 0.f;
     bool loaded = false, changed = false;
     uint64_t L[KL];
     int n = 0;
@@ -841,6 +950,7 @@ __device__ __attribute__((noinline)) void exact_row_scan(gfloat4 *__restrict__ r
                 for (int e = 0; e < 4; ++e) {
                     const int c = 4 * (q0 + u) + e;
                     if (vv[e] >= th && c < nvalid) buf[n++] = make_key(vv[e], (uint32_t)(v0 + c));
+                    if (lse_m && c < nvalid) esum += __expf(unary_transform(vv[e], mult, cap) - tmax);
                 }
             }
             // all lanes merge together once any buffer is past the mark (a merge
@@ -849,6 +959,12 @@ __device__ __attribute__((noinline)) void exact_row_scan(gfloat4 *__restrict__ r
         }
     }
     if (n) flush();
+    if (lse_m) {
+        float m = *lse_m, sm = *lse_s;
+        lse_merge(m, sm, tmax, esum);
+        *lse_m = m;
+        *lse_s = sm;
+    }
     if (changed) {
 #pragma unroll
         for (int j = 0; j < KL; ++j) list[j] = L[j];
@@ -856,10 +972,11 @@ __device__ __attribute__((noinline)) void exact_row_scan(gfloat4 *__restrict__ r
     }
 }
 
-template <int KL>
+template <int KL, bool LSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_big_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int n_mt, int n_slabs,
-    int n_vt, uint64_t *__restrict__ partial, float *__restrict__ tiles, uint32_t *__restrict__ status) {
+    int n_vt, uint64_t *__restrict__ partial, float *__restrict__ tiles, uint32_t *__restrict__ status,
+    UnaryEpi ue) {
     using namespace big;
     __shared__ __align__(16) uint8_t st0[STAGE];
     __shared__ __align__(16) uint8_t st1[STAGE];
@@ -867,6 +984,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __align__(16) float thr[BM];  // per tile row: value of its KL-th key (+inf: not a row)
     __shared__ uint32_t cnt[BM];             // per tile row: register-scan hits this tile
     __shared__ uint32_t ovf[2];              // per tile parity: some row overflowed its slots
+    __shared__ float lse_m[LSE ? BM : 1], lse_s[LSE ? BM : 1];  // per tile row: running log-sum-exp
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
     int mt, slab;
     big_tile_of(blockIdx.x, gridDim.x, n_mt, n_slabs, mt, slab);
@@ -878,6 +996,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float *tile = tiles + (size_t)blockIdx.x * kBigTileFloats;  // exact path: [256 rows][256 cols]
     thr[t] = my_ok ? -__builtin_inff() : __builtin_inff();
     cnt[t] = 0u;
+    if constexpr (LSE) {
+        lse_m[t] = -__builtin_inff();
+        lse_s[t] = 0.f;
+    }
     if (t < 2) ovf[t] = 0u;
     // (the mainloop's barriers order these before their first use)
     // A tile is kept in the workspace buffer ("stored") when it is the slab's
@@ -902,7 +1024,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // next, and a tile in which any of its 256 rows overflows the 32
         // slots would be formed twice, so the register scan starts once
         // that expectation is down to 16.
-        const bool scan = !fresh && v0 + BN <= V && (vt - vt0) * 16 >= KL;
+        // (with the log-sum-exp wanted every tile takes the exact path, whose
+        // owner thread sees its whole row)
+        const bool scan = !LSE && !fresh && v0 + BN <= V && (vt - vt0) * 16 >= KL;
         store = store || !scan;
         f32x16 acc[4][4];
         mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H, prefilled);
@@ -971,7 +1095,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     if (!fresh) store_list<KL>(RL, my_list);
                 }
                 exact_row_scan<KL>((gfloat4 *)(tile + t * BN), V - v0, v0, fresh, (gu64 *)my_list,
-                                   (lfloat *)&thr[t], (lu64 *)(reinterpret_cast<uint64_t *>(st0) + t * kCandStride));
+                                   (lfloat *)&thr[t], (lu64 *)(reinterpret_cast<uint64_t *>(st0) + t * kCandStride),
+                                   LSE ? (lfloat *)&lse_m[t] : nullptr, LSE ? (lfloat *)&lse_s[t] : nullptr, ue.mult,
+                                   ue.cap);
                 if constexpr (kRegList) load_list<KL>(RL, my_list);
             }
             __syncthreads();  // the buffers in st0 are the next mainloop's first stage
@@ -982,6 +1108,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if constexpr (kRegList) {
         if (my_ok) store_list<KL>(RL, my_list);
     }
+    if constexpr (LSE) {
+        if (my_ok) ue.lse_part[(size_t)(m0 + t) * n_slabs + slab] = make_float2(lse_m[t], lse_s[t]);
+    }
 }
 
 // ---------------------------------------------------------------- merge
@@ -991,7 +1120,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 __device__ __forceinline__ void merge_stage(const uint64_t *src, int n, int K, uint64_t *dst,
                                             bool final_stage, int32_t *out_ids, float *out_vals,
-                                            uint64_t *scratch) {
+                                            uint64_t *scratch, float mult, float cap) {
     const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int chunks = (n + kMergeChunk - 1) / kMergeChunk;
     for (int c = wave; c < chunks; c += nw) {
@@ -1014,7 +1143,7 @@ __device__ __forceinline__ void merge_stage(const uint64_t *src, int n, int K, u
         if (lane < K) {
             if (final_stage) {
                 out_ids[lane] = top ? (int32_t)key_id(top) : -1;
-                out_vals[lane] = top ? key_val(top) : -__builtin_inff();
+                out_vals[lane] = top ? unary_transform(key_val(top), mult, cap) : -__builtin_inff();
             } else {
                 dst[(size_t)c * K + lane] = top;
             }
@@ -1033,7 +1162,8 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const uint64_t *__restr
                                                          float *__restrict__ gold_logit,
                                                          uint32_t *__restrict__ status, int lds_keys,
                                                          const T *__restrict__ gold_h, const T *__restrict__ gold_w,
-                                                         int H) {
+                                                         int H, UnaryEpi ue, int n_lists, float *__restrict__ out_lse,
+                                                         float *__restrict__ out_prob, uint8_t *__restrict__ out_hit) {
     extern __shared__ __align__(16) uint8_t smem[];
     uint64_t *bufA = reinterpret_cast<uint64_t *>(smem);
     uint64_t *bufB = bufA + lds_keys;
@@ -1046,16 +1176,44 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const uint64_t *__restr
     float *ov = out_vals + (size_t)row * K;
     while (true) {
         const bool fin = n <= kMergeChunk;
-        merge_stage(src, n, K, dst, fin, oi, ov, scratch);
+        merge_stage(src, n, K, dst, fin, oi, ov, scratch, ue.mult, ue.cap);
         if (fin) break;
         __syncthreads();
         n = (n + kMergeChunk - 1) / kMergeChunk * K;
         src = dst;
         dst = dst == bufA ? bufB : bufA;
     }
+    // log-sum-exp over the full vocabulary from the lists' partial sums
+    float lse = 0.f;
+    if (ue.lse_part) {
+        __syncthreads();  // scratch is free again
+        float m = -__builtin_inff(), sm = 0.f;
+        for (int i = threadIdx.x; i < n_lists; i += blockDim.x) {
+            const float2 ps = ue.lse_part[(size_t)row * n_lists + i];
+            lse_merge(m, sm, ps.x, ps.y);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) lse_merge(m, sm, __shfl_xor(m, o), __shfl_xor(sm, o));
+        float2 *part = reinterpret_cast<float2 *>(scratch);
+        if (lane_id() == 0) part[threadIdx.x >> 6] = make_float2(m, sm);
+        __syncthreads();
+        m = -__builtin_inff();
+        sm = 0.f;
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) lse_merge(m, sm, part[i].x, part[i].y);
+        lse = m + logf(sm);
+        if (out_lse && threadIdx.x == 0) out_lse[row] = lse;
+    }
     if (!gold) return;
     const int g = gold[row];
     const bool g_ok = g >= 0 && g < V;
+    if (out_hit) {
+        __syncthreads();  // the final stage's ids are visible to the workgroup
+        if (threadIdx.x < 64) {
+            const bool hit = g_ok && (int)threadIdx.x < K && oi[threadIdx.x] == g;
+            const unsigned long long b = __ballot(hit);
+            if (threadIdx.x == 0) out_hit[row] = b ? 1 : 0;
+        }
+    }
     if (gold_h && g_ok) {
         __syncthreads();  // scratch is free again
         const T *x = gold_h + (size_t)row * H, *y = gold_w + (size_t)g * H;
@@ -1081,6 +1239,13 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const uint64_t *__restr
         gold_logit[row] = __builtin_nanf("");
         flag_status(status, kStatusIdRange);
     }
+    // the gold logit (written above, or by the LM-head kernel before this
+    // launch) in transformed form, and its probability
+    if (g_ok && threadIdx.x == 0) {
+        const float u = unary_transform(gold_logit[row], ue.mult, ue.cap);
+        gold_logit[row] = u;
+        if (out_prob) out_prob[row] = __expf(u - lse);
+    }
 }
 
 // ---------------------------------------------------------------- host side
@@ -1094,7 +1259,8 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
     const int es = dtype == 0 ? 4 : 2;
     const int S = H / (4 * (16 / es));
     const int nw = 8;
-    size_t stream_lds = (size_t)S * 32 * 16 + (size_t)nw * (8 * kCandCap + 128) * 8 + (size_t)nw * 8 * 4 + 16;
+    size_t stream_lds = (size_t)S * 32 * 16 + (size_t)nw * (8 * kCandCap + 128) * 8 + (size_t)nw * 8 * 4 + 16 +
+                        (size_t)nw * 8 * 8;
     if (stream_lds < (size_t)kStreamMinLds) stream_lds = kStreamMinLds;
     const int ks = dma_ksplit(H);
     if (dtype != 0 && M <= kStreamMaxRows && ks > 0 && dma_lds_bytes(H, ks) <= 160 * 1024 &&
@@ -1143,7 +1309,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.n_tiles = n_vt;
         const size_t stage = (size_t)(128 + 128) * (8 * 16 + 16);
         const size_t ctile = (size_t)128 * (128 + 4) * 4;
-        p.lds = (stage > ctile ? stage : ctile) + (size_t)128 * K * 8;
+        p.lds = (stage > ctile ? stage : ctile) + (size_t)128 * K * 8 + (size_t)128 * 8;
     }
     // merge: LDS for the first reduction stage's survivors (later stages are smaller)
     if (!p.big) p.list_len = K;
@@ -1156,6 +1322,10 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.tiles_offset = p.partial_bytes;
         p.partial_bytes += (size_t)p.grid_x * kBigTileFloats * 4;
     }
+    // then each list's log-sum-exp partial (float2)
+    p.partial_bytes = (p.partial_bytes + 255) / 256 * 256;
+    p.lse_offset = p.partial_bytes;
+    p.partial_bytes += (size_t)M * p.n_lists * 8;
     return p;
 }
 
@@ -1165,23 +1335,23 @@ static hipError_t set_lds(F *kernel, size_t lds) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <typename T, int P>
+template <typename T, int P, bool LSE>
 static hipError_t launch_stream(const LmheadPlan &p, int64_t M, int H, int V, int K, const void *h,
                                 const void *w, const int32_t *gold, float *gold_logit, uint64_t *partial,
-                                uint32_t *status, hipStream_t stream) {
-    auto kern = lmhead_stream_kernel<T, 8, P>;
+                                uint32_t *status, const UnaryEpi &ue, hipStream_t stream) {
+    auto kern = lmhead_stream_kernel<T, 8, P, LSE>;
     hipError_t e = set_lds(kern, p.lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(64 * 8), p.lds, stream, (const T *)h, (const T *)w,
-                       (int)M, H, V, K, p.n_tiles, gold, gold_logit, partial, status);
+                       (int)M, H, V, K, p.n_tiles, gold, gold_logit, partial, status, ue);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool LSE>
 static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K, const void *h,
                              const void *w, const int32_t *gold, int32_t *out_ids, float *out_vals,
-                             float *gold_logit, uint64_t *partial, uint32_t *status,
-                             hipStream_t stream) {
+                             float *gold_logit, uint64_t *partial, uint32_t *status, const UnaryEpi &ue,
+                             const UnaryMetrics &um, hipStream_t stream) {
     hipError_t e;
     if (p.dma) {
         if constexpr (sizeof(T) == 2) {
@@ -1189,17 +1359,17 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
                 hipError_t err = set_lds(kern, p.lds);
                 if (err != hipSuccess) return err;
                 hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(64 * kDmaWaves), p.lds, stream, (const uint16_t *)h,
-                                   (const uint16_t *)w, (int)M, H, V, K, gold, gold_logit, partial, status);
+                                   (const uint16_t *)w, (int)M, H, V, K, gold, gold_logit, partial, status, ue);
                 return hipGetLastError();
             };
-            e = p.ksplit == 4 ? launch(lmhead_dma_kernel<4>)
-                : p.ksplit == 2 ? launch(lmhead_dma_kernel<2>)
-                                : launch(lmhead_dma_kernel<1>);
+            e = p.ksplit == 4 ? launch(lmhead_dma_kernel<4, LSE>)
+                : p.ksplit == 2 ? launch(lmhead_dma_kernel<2, LSE>)
+                                : launch(lmhead_dma_kernel<1, LSE>);
         } else {
             return hipErrorInvalidValue;
         }
     } else if (p.streaming) {
-#define DF2_STREAM(PP) launch_stream<T, PP>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, stream)
+#define DF2_STREAM(PP) launch_stream<T, PP, LSE>(p, M, H, V, K, h, w, gold, gold_logit, partial, status, ue, stream)
         switch (p.prefetch) {
             case 16: e = DF2_STREAM(16); break;
             case 8: e = DF2_STREAM(8); break;
@@ -1210,24 +1380,24 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
 #undef DF2_STREAM
     } else if (p.big) {
         if constexpr (sizeof(T) == 2) {
-            auto kern = p.list_len == 8    ? lmhead_big_kernel<8>
-                        : p.list_len == 16 ? lmhead_big_kernel<16>
-                        : p.list_len == 32 ? lmhead_big_kernel<32>
-                                           : lmhead_big_kernel<64>;
+            auto kern = p.list_len == 8    ? lmhead_big_kernel<8, LSE>
+                        : p.list_len == 16 ? lmhead_big_kernel<16, LSE>
+                        : p.list_len == 32 ? lmhead_big_kernel<32, LSE>
+                                           : lmhead_big_kernel<64, LSE>;
             float *tiles = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(partial) + p.tiles_offset);
             hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(big::NT), p.lds, stream, (const uint16_t *)h,
                                (const uint16_t *)w, (int)M, H, V, p.n_mt, p.n_lists, p.n_tiles, partial, tiles,
-                               status);
+                               status, ue);
             e = hipGetLastError();
         } else {
             return hipErrorInvalidValue;
         }
     } else {
-        auto kern = lmhead_tiled_kernel<T>;
+        auto kern = lmhead_tiled_kernel<T, LSE>;
         if ((e = set_lds(kern, p.lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(p.grid_x, p.grid_y), dim3(256), p.lds, stream, (const T *)h,
                            (const T *)w, (int)M, H, V, K, p.n_tiles, gold, gold_logit, partial,
-                           status);
+                           status, ue);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
@@ -1236,19 +1406,30 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
     const int n_keys = p.n_lists * p.list_len;
     hipLaunchKernelGGL(merge, dim3((unsigned)M), dim3(512), p.merge_lds, stream, partial, (int)M, n_keys, K, V,
                        out_ids, out_vals, gold, gold_logit, status, first_stage_keys(n_keys, K),
-                       p.big ? (const T *)h : nullptr, p.big ? (const T *)w : nullptr, H);
+                       p.big ? (const T *)h : nullptr, p.big ? (const T *)w : nullptr, H, ue, p.n_lists, um.lse,
+                       um.gold_prob, um.hit);
     return hipGetLastError();
 }
 
 hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const void *h, const void *w,
                              const int32_t *gold, int32_t *out_ids, float *out_vals,
-                             float *gold_logit, void *workspace, hipStream_t stream) {
+                             float *gold_logit, void *workspace, hipStream_t stream, const UnaryMetrics *metrics) {
     const LmheadPlan p = plan_lmhead(dtype, M, H, V, K);
     uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
     uint64_t *partial = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
+    const UnaryMetrics um = metrics ? *metrics : UnaryMetrics{1.f, 0.f, nullptr, nullptr, nullptr};
+    const bool lse = um.lse || um.gold_prob;
+    UnaryEpi ue{um.mult, um.cap,
+                lse ? reinterpret_cast<float2 *>(reinterpret_cast<uint8_t *>(partial) + p.lse_offset) : nullptr};
     if (dtype == 0)
-        return run_lmhead<float>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial, status, stream);
-    return run_lmhead<uint16_t>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial, status, stream);
+        return lse ? run_lmhead<float, true>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial,
+                                             status, ue, um, stream)
+                   : run_lmhead<float, false>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial,
+                                              status, ue, um, stream);
+    return lse ? run_lmhead<uint16_t, true>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial,
+                                            status, ue, um, stream)
+               : run_lmhead<uint16_t, false>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial,
+                                             status, ue, um, stream);
 }
 
 }  // namespace dflash2

@@ -25,7 +25,7 @@ OP_UNARY_TOPK, OP_SELECTOR_WALK, OP_SELECTOR_TF, OP_SELECTOR_CE_BACKWARD = 0, 1,
 F32, BF16 = 0, 1
 MAX_TOP_K, MAX_TAPS, MAX_BLOCK_SIZE, MAX_RANK = 64, 16, 64, 4096
 
-EXPORTS = ["dflash2_conv_prepare", "dflash2_conv_finish", "dflash2_unary_topk",
+EXPORTS = ["dflash2_conv_prepare", "dflash2_conv_finish", "dflash2_unary_topk", "dflash2_unary_topk_ex",
            "dflash2_selector_walk", "dflash2_selector_sample", "dflash2_selector_score_tf",
            "dflash2_selector_ce_backward", "dflash2_workspace_bytes",
            "dflash2_status_str", "dflash2_read_device_status", "dflash2_version"]
@@ -46,6 +46,8 @@ def _load() -> ctypes.CDLL:
         "dflash2_conv_prepare": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P],
         "dflash2_conv_finish": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P],
         "dflash2_unary_topk": [ctypes.c_int, I64, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
+        "dflash2_unary_topk_ex": [ctypes.c_int, I64, I32, I32, I32, P, P, P, ctypes.c_float, ctypes.c_float,
+                                  P, P, P, P, P, P, P, SZ, P],
         "dflash2_selector_walk": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "dflash2_selector_sample": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P,
                                     ctypes.c_float, ctypes.c_uint64, P, P, P, SZ, P],
@@ -182,6 +184,35 @@ def unary_topk(h: torch.Tensor, w_lm: torch.Tensor, top_k: int, gold_ids: Option
                                  _ptr(vals), _ptr(gl), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "dflash2_unary_topk")
     return ids, vals, gl
+
+
+def unary_topk_ex(h: torch.Tensor, w_lm: torch.Tensor, top_k: int, gold_ids: Optional[torch.Tensor] = None,
+                  output_multiplier: float = 1.0, softcap: float = 0.0, want_lse: bool = False,
+                  want_metrics: bool = False, workspace: Optional[torch.Tensor] = None):
+    """unary_topk over softcap(output_multiplier * U).  -> (ids, vals, gold_logit or None, lse [N] or None,
+    gold_prob [N] or None, gold_hit [N] uint8 or None); the gold metrics need gold_ids and want_metrics."""
+    _same_dtype(h, w_lm)
+    N, H = h.shape
+    V = w_lm.shape[0]
+    dev = h.device
+    ids = torch.empty((N, top_k), dtype=torch.int32, device=dev)
+    vals = torch.empty((N, top_k), dtype=torch.float32, device=dev)
+    gl = prob = hit = None
+    if gold_ids is not None:
+        _ids(gold_ids, "gold_ids")
+        gl = torch.empty(N, dtype=torch.float32, device=dev)
+        if want_metrics:
+            prob = torch.empty(N, dtype=torch.float32, device=dev)
+            hit = torch.empty(N, dtype=torch.uint8, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if want_lse else None
+    if workspace is None:
+        workspace = make_workspace(OP_UNARY_TOPK, N, H, V, 0, top_k, dev)
+    st = _lib.dflash2_unary_topk_ex(_dtype_code(h), N, H, V, top_k, _ptr(h), _ptr(w_lm), _ptr(gold_ids),
+                                    float(output_multiplier), float(softcap), _ptr(ids), _ptr(vals), _ptr(gl),
+                                    _ptr(lse), _ptr(prob), _ptr(hit), _ptr(workspace), workspace.numel(),
+                                    _stream(dev))
+    _check(st, "dflash2_unary_topk_ex")
+    return ids, vals, gl, lse, prob, hit
 
 
 def selector_walk(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, block_size: int,

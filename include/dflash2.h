@@ -147,6 +147,36 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * dflash2_unary_topk with the unary-logit transforms of the draft config and
+ * the candidate metrics of the same pass ([SpecForge] "Export and serve":
+ * output_multiplier and final_logit_softcapping act on the unary logits;
+ * [Explainer] "Problem 1", recall@K; [SpecForge] "Selector objective and
+ * schedule", selector coverage; [verl PR] "What DFlash2 adds", unary
+ * candidate recall and target mass).
+ *   U'[n, v] = softcap(output_multiplier * U[n, v]),
+ *   softcap(x) = c * tanh(x / c) with c = final_logit_softcapping (0: off).
+ *   out_ids / out_vals: the top_k of U' (ids as dflash2_unary_topk: the
+ *   transform is increasing), values U'; out_gold_logit[n] = U'[n, gold[n]].
+ *   out_lse[n] = log sum_v exp(U'[n, v]) over the full vocabulary, or NULL.
+ *   out_gold_prob[n] = exp(U'[n, gold[n]] - lse[n]), the gold's softmax
+ *   probability (target mass), or NULL; needs gold_ids.
+ *   out_gold_hit[n] = 1 if gold[n] is among out_ids[n, :] (recall@K and
+ *   coverage indicator), else 0; uint8 or NULL; needs gold_ids.
+ *   output_multiplier > 0 and finite, final_logit_softcapping >= 0 and finite
+ *   (DFLASH2_ERR_SHAPE otherwise).  Asking for out_lse or out_gold_prob on
+ *   more than 8 bf16 rows sends every vocabulary tile through the kernel's
+ *   exact per-row path (slower; the default path is unchanged).  Outputs
+ *   must not overlap each other or the workspace.  Workspace: that of
+ *   DFLASH2_OP_UNARY_TOPK.  Other rules as dflash2_unary_topk.
+ */
+dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab, int32_t top_k,
+                                     const void *h, const void *w_lm, const int32_t *gold_ids,
+                                     float output_multiplier, float final_logit_softcapping, int32_t *out_ids,
+                                     float *out_vals, float *out_gold_logit, float *out_lse, float *out_gold_prob,
+                                     uint8_t *out_gold_hit, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/*
  * Greedy selector walk per anchor block ([verl PR] "What DFlash2 adds",
  * selector equation; [Speculators] "Candidate Selector"; [Explainer]
  * "Problem 1" and the "One Cycle, Step by Step" diagram: candidate lists plus

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert sorted(D.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -102,6 +102,32 @@ def test_unary_topk_rules():
     assert topk(gold=fake(5), gl=None) == NULL
     assert topk(wsb=16) == WS
     assert topk(ids=fake(3)) == ALIAS    # ids on vals
+
+
+def topk_ex(dtype=1, n=8, h=256, v=4096, k=16, hp=fake(0), w=fake(1), gold=None, mult=1.0, cap=0.0, ids=fake(2),
+            vals=fake(3), gl=None, lse=None, prob=None, hit=None, ws=fake(4), wsb=None):
+    if wsb is None:
+        wsb = D.workspace_bytes(D.OP_UNARY_TOPK, n, h, v, 0, k) if n > 0 else 1 << 20
+    return L.dflash2_unary_topk_ex(dtype, n, h, v, k, hp, w, gold, mult, cap, ids, vals, gl, lse, prob, hit, ws, wsb,
+                                   None)
+
+
+@no_gpu
+def test_unary_topk_ex_rules():
+    # the plain call's rules
+    assert topk_ex(k=0) == SHAPE and topk_ex(k=65) == UNSUP and topk_ex(h=100) == UNSUP and topk_ex(dtype=-1) == DTYPE
+    assert topk_ex(hp=None) == NULL and topk_ex(ws=None) == NULL and topk_ex(wsb=16) == WS
+    # a positive finite multiplier, a non-negative finite cap
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert topk_ex(mult=bad) == SHAPE
+    for bad in (-0.5, float("inf"), float("nan")):
+        assert topk_ex(cap=bad) == SHAPE
+    # gold metrics need gold ids; gold ids need the gold logit
+    assert topk_ex(prob=fake(6)) == NULL and topk_ex(hit=fake(7)) == NULL
+    assert topk_ex(gold=fake(5)) == NULL
+    # outputs overlap neither each other nor the workspace
+    assert topk_ex(lse=fake(3)) == ALIAS and topk_ex(gold=fake(5), gl=fake(6), hit=fake(6)) == ALIAS
+    assert topk_ex(lse=fake(4)) == ALIAS
 
 
 def walk(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, ws=fake(9), wsb=None, path=fake(7), anchors=fake(6), ps=None):

@@ -128,6 +128,50 @@ def test_unary_topk(D, N, H, V, K, dtype):
     assert close(to_np(gl), U[np.arange(N), inp["gold"]]).all()
 
 
+TOPK_EX_CASES = [
+    # (N, H, V, K, dtype, multiplier, softcap): every kernel regime (LDS-streamed
+    # bf16 with K splits 4 / 2 / 1, register-streamed, 256 x 256 MFMA tiles
+    # with lists of 8 / 16 / 64, float32 tiles), ragged vocabulary tails
+    (8, 4096, 30011, 16, "bf16", 1.0, 30.0), (3, 1024, 20000, 16, "bf16", 1.7, 0.0),
+    (5, 512, 5003, 64, "bf16", 0.8, 8.0), (8, 320, 4099, 8, "bf16", 1.0, 0.0), (5, 256, 7001, 16, "f32", 2.0, 3.0),
+    (300, 256, 5000, 16, "bf16", 1.0, 30.0), (40, 512, 9001, 64, "bf16", 0.5, 0.0),
+    (600, 256, 70001, 5, "bf16", 1.3, 4.0), (100, 256, 3001, 16, "f32", 1.0, 1.5),
+]
+
+
+@pytest.mark.parametrize("N,H,V,K,dtype,mult,cap", TOPK_EX_CASES)
+def test_unary_topk_ex_transforms_and_metrics(D, N, H, V, K, dtype, mult, cap):
+    log(f"topk_ex N={N} H={H} V={V} K={K} {dtype} mult={mult} cap={cap}")
+    w = wl(n_blocks=N, block_size=1, hidden=H, vocab=V, top_k=K, dtype=dtype)
+    inp = make_inputs(w, seed=8, fields=["h", "w_lm", "gold"])
+    gold = inp["gold"].copy()
+    U = O.lm_logits(inp["h"], inp["w_lm"], dtype)
+    # a third of the golds are in the top K, so the hit flag takes both values
+    gold[::3] = np.argmax(U[::3], axis=1)
+    ids, vals, gl, lse, prob, hit = D.unary_topk_ex(to_dev(inp["h"]), to_dev(inp["w_lm"]), K, gold_ids=to_dev(gold),
+                                                    output_multiplier=mult, softcap=cap, want_lse=True,
+                                                    want_metrics=True)
+    rids, rvals, rlse, rgl, rprob, rhit = O.unary_topk_ex(inp["h"], inp["w_lm"], K, dtype, gold_ids=gold,
+                                                          output_multiplier=mult, softcap=cap)
+    Ut = O.transform_logits(U, mult, cap)
+    fails, flags, msgs = compare_topk(to_np(ids), to_np(vals), Ut, K)
+    log(f"  fails={fails} flags={flags}")
+    assert fails == 0, msgs[:5]
+    assert close(to_np(gl), rgl).all()
+    assert close(to_np(lse), rlse).all(), (to_np(lse)[:4], rlse[:4])
+    assert close(to_np(prob), rprob, atol=1e-6).all()
+    gi, gh = to_np(ids), to_np(hit)
+    # the hit flag is the GPU's own candidate set; the oracle's agrees unless
+    # that row's set was flagged as a boundary near-tie
+    assert np.array_equal(gh, (gi == gold[:, None]).any(1).astype(np.uint8))
+    assert 0 < gh.sum() < N or N < 3
+    assert int((gh != rhit).sum()) <= flags
+    # the plain call gives the same ids; with no transform, the same values
+    if mult == 1.0 and cap == 0.0:
+        ids0, vals0, _ = D.unary_topk(to_dev(inp["h"]), to_dev(inp["w_lm"]), K, gold_ids=to_dev(gold))
+        assert torch.equal(ids0, ids) and torch.equal(vals0, vals)
+
+
 @pytest.mark.parametrize("N", [8, 40])
 def test_unary_topk_exact_ties_take_the_lower_id(D, N):
     H, V, K = 256, 1000, 16
