@@ -814,6 +814,51 @@ __device__ __forceinline__ void agpr_store_lds4(float *p, f32x4 a) {
 // walks its own hits: value by index from the scratch, a slot of the row
 // claimed with an LDS atomic (a row's hits come from two waves), the key
 // written there.  A row with more than kRowCand hits sets *ovf.
+// The tile's share of each row's log-sum-exp, shifted by the row's running
+// maximum `shift` (LDS): lanes sum exp(U' - shift) over their values of a row,
+// the 32 lanes of a half-wave reduce it, and one lane per half-wave and wave
+// adds it to tile_sum.  A value more than 60 above its shift (the sum could
+// leave float32 range) flags the tile for the exact path instead.
+constexpr float kLseSpan = 60.f;
+__device__ __forceinline__ float fast_transform(float x, float mult, float cap) {
+    x *= mult;
+    // cap tanh(x / cap) as cap (1 - 2 / (exp(2 x / cap) + 1)): one exp and a
+    // divide; absolute error ~1e-7 cap, which the sum of exponentials absorbs
+    return cap > 0.f ? cap * (1.f - 2.f / (__expf(2.f * x / cap) + 1.f)) : x;
+}
+__device__ __forceinline__ void register_lse(const big::f32x16 (&acc)[4][4], const float *shift, float *tile_sum,
+                                             uint32_t *ovf, float mult, float cap) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1;
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    const int hl = (lane >> 5) + zero;
+    bool far = false;
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+        const int rbase = wm * 128 + tm * 32 + 4 * hl;  // rows of acc[tm][*][i]: rbase + 8 (i / 4) + i % 4
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 c4 = *reinterpret_cast<const float4 *>(shift + rbase + 8 * g);
+            const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float sum = 0.f;
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn) {
+                    const float d = fast_transform(agpr_read(acc[tm][tn][4 * g + e]), mult, cap) - c[e];
+                    far = far || d > kLseSpan;
+                    sum += __expf(d);
+                }
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) sum += __shfl_xor(sum, o);
+                if ((lane & 31) == 0) atomicAdd(tile_sum + rbase + 8 * g + e, sum);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (far) *ovf = 1u;
+}
+
 __device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], const float *thr, uint32_t *cnt,
                                               uint64_t *slots, uint32_t *ovf, float *scr, int v0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
@@ -984,7 +1029,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __align__(16) float thr[BM];  // per tile row: value of its KL-th key (+inf: not a row)
     __shared__ uint32_t cnt[BM];             // per tile row: register-scan hits this tile
     __shared__ uint32_t ovf[2];              // per tile parity: some row overflowed its slots
-    __shared__ float lse_m[LSE ? BM : 1], lse_s[LSE ? BM : 1];  // per tile row: running log-sum-exp
+    // per tile row: running log-sum-exp (max, sum of exp(U' - max)) and this tile's share
+    __shared__ __align__(16) float lse_m[LSE ? BM : 1];
+    __shared__ float lse_s[LSE ? BM : 1], lse_t[LSE ? BM : 1];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
     int mt, slab;
     big_tile_of(blockIdx.x, gridDim.x, n_mt, n_slabs, mt, slab);
@@ -999,6 +1046,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if constexpr (LSE) {
         lse_m[t] = -__builtin_inff();
         lse_s[t] = 0.f;
+        lse_t[t] = 0.f;
     }
     if (t < 2) ovf[t] = 0u;
     // (the mainloop's barriers order these before their first use)
@@ -1024,9 +1072,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // next, and a tile in which any of its 256 rows overflows the 32
         // slots would be formed twice, so the register scan starts once
         // that expectation is down to 16.
-        // (with the log-sum-exp wanted every tile takes the exact path, whose
-        // owner thread sees its whole row)
-        const bool scan = !LSE && !fresh && v0 + BN <= V && (vt - vt0) * 16 >= KL;
+        const bool scan = !fresh && v0 + BN <= V && (vt - vt0) * 16 >= KL;
         store = store || !scan;
         f32x16 acc[4][4];
         mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H, prefilled);
@@ -1055,11 +1101,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (scan) {
             // the idle stage buffers hold the scan's scratch
             register_scan(acc, thr, cnt, slots, &ovf[par], reinterpret_cast<float *>(st0), v0);
+            if constexpr (LSE) register_lse(acc, lse_m, lse_t, &ovf[par], ue.mult, ue.cap);
             __syncthreads();
             over = ovf[par] != 0u;
             if (t == 0) ovf[par ^ 1] = 0u;  // last read a pass ago; next written a pass from now
             const uint32_t n = cnt[t];
             cnt[t] = 0u;
+            if constexpr (LSE) {
+                // the tile's share, relative to the same shift; dropped if the
+                // tile is formed again for the exact path
+                if (!over) lse_s[t] += lse_t[t];
+                lse_t[t] = 0.f;
+            }
             if (!over && vt + 1 < vt1) {
                 // the next tile's first k-slice loads under the list insertion (the
                 // barrier above ended the scan's use of st0)

@@ -163,11 +163,12 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
  *   out_gold_hit[n] = 1 if gold[n] is among out_ids[n, :] (recall@K and
  *   coverage indicator), else 0; uint8 or NULL; needs gold_ids.
  *   output_multiplier > 0 and finite, final_logit_softcapping >= 0 and finite
- *   (DFLASH2_ERR_SHAPE otherwise).  Asking for out_lse or out_gold_prob on
- *   more than 8 bf16 rows sends every vocabulary tile through the kernel's
- *   exact per-row path (slower; the default path is unchanged).  Outputs
- *   must not overlap each other or the workspace.  Workspace: that of
- *   DFLASH2_OP_UNARY_TOPK.  Other rules as dflash2_unary_topk.
+ *   (DFLASH2_ERR_SHAPE otherwise).  Asking for out_lse or out_gold_prob
+ *   adds a sum of exponentials to every logit tile (about a fifth more time
+ *   on many bf16 rows, a few percent at decode sizes); without them the
+ *   kernels are those of dflash2_unary_topk.  Outputs must not overlap each
+ *   other or the workspace.  Workspace: that of DFLASH2_OP_UNARY_TOPK.  Other
+ *   rules as dflash2_unary_topk.
  */
 dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab, int32_t top_k,
                                      const void *h, const void *w_lm, const int32_t *gold_ids,
