@@ -35,7 +35,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
 inline size_t walk_lds_bytes(int bs, int K) { return (size_t)bs * K * (8 + 4 + 4 + 4); }
 
 // Workspace of the selector CE backward, byte offsets (256-byte aligned).
-// g / gv [N, r], ag [N, r], dg [N, r] float32; per (row, slot) entries
+// g / gv [N, r], ag [N, r] float32, dg (float32 [N, r] or bf16 packed); per (row, slot) entries
 // (slot K is the predecessor row) with their weight, target and sorted
 // order; per-target counts and offsets over the 2V targets (successor rows,
 // then predecessor rows) plus one; and the scan's per-tile prefixes.
@@ -50,7 +50,8 @@ inline CeBwdLayout ce_bwd_layout(int64_t N, int V, int r, int K) {
     L.g = kStatusBytes;
     L.ag = L.g + up((size_t)N * r * 4);
     L.dg = L.ag + up((size_t)N * r * 4);
-    L.wgt = L.dg + up((size_t)N * r * 4);
+    // dg: float32 [N, r], or (bf16) high and low parts packed 8 rows deep
+    L.wgt = L.dg + up((size_t)(N + 7) / 8 * 8 * r * 4);
     L.tgt = L.wgt + up(E * 4);
     L.src = L.tgt + up(E * 4);
     L.counts = L.src + up(E * 4);

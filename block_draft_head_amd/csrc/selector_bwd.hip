@@ -26,9 +26,11 @@
 //    of taking one float atomic per contribution and element; only a target
 //    with more than kSegChunk entries (a token in many rows' candidate sets)
 //    adds its chunks atomically.
-//  * wh_grad_kernel: dW_H += dg^T h, an fp32 MFMA contraction over the rows
-//    (dg is float32); the eight waves of a workgroup split the rows of one
-//    64 x 64 tile and reduce their partial tiles through LDS.
+//  * dW_H += dg^T h, a contraction over the rows: for bf16 inputs on the bf16
+//    MFMA with dg split into bf16 high and low parts (wh_grad_bf16_kernel),
+//    for float32 inputs on the float32 MFMA (wh_grad_kernel); the eight waves
+//    of a workgroup split the rows of one 64 x 64 tile and reduce their
+//    partial tiles through LDS.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -97,8 +99,37 @@ __global__ __launch_bounds__(256) void ce_grad_rows_kernel(
         }
     }
     float *dg_row = dg + (size_t)n * r;
+    // bf16: dg goes out as its truncated bf16 high part and the bf16 of the
+    // remainder, packed 8 rows deep: element (n, i) at ((n / 8) r + i) 8 + n % 8
+    // of each half (the last group's missing rows are zero)
+    uint16_t *dg_hi = reinterpret_cast<uint16_t *>(dg), *dg_lo = dg_hi + (size_t)(N + 7) / 8 * 8 * r;
+    auto put_dg = [&](int e, f32x4 v) {
+        if constexpr (sizeof(T) == 2) {
+            const size_t base = ((size_t)(n >> 3) * r + e) * 8 + (n & 7);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t hb = __float_as_uint(v[i]) & 0xffff0000u;
+                dg_hi[base + 8 * i] = (uint16_t)(hb >> 16);
+                dg_lo[base + 8 * i] = (uint16_t)(__float_as_uint(v[i] - __uint_as_float(hb)) >> 16);
+            }
+        } else {
+            *reinterpret_cast<f32x4 *>(dg_row + e) = v;
+        }
+    };
+    if constexpr (sizeof(T) == 2) {
+        if (n == N - 1 && (N & 7) != 0) {
+            for (int e = 4 * lane; e < r; e += 256)
+                for (int p = (int)(N & 7); p < 8; ++p)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const size_t at = ((size_t)(n >> 3) * r + e + i) * 8 + p;
+                        dg_hi[at] = 0;
+                        dg_lo[at] = 0;
+                    }
+        }
+    }
     if (kg < 0) {  // excluded row: no CE, no gradient, no entries
-        for (int e = 4 * lane; e < r; e += 256) *reinterpret_cast<f32x4 *>(dg_row + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 4 * lane; e < r; e += 256) put_dg(e, f32x4{0.f, 0.f, 0.f, 0.f});
         for (int j = lane; j <= K; j += 64) tgt[e0 + j] = -1;
         if (lane == 0) {
             if (out_ce) out_ce[n] = 0.f;
@@ -155,7 +186,7 @@ __global__ __launch_bounds__(256) void ce_grad_rows_kernel(
     for (int c = 0; c < NC; ++c) {
         const int e = 4 * lane + 256 * c;
         if (e < r) {
-            *reinterpret_cast<f32x4 *>(dg_row + e) = load4<T>(a_row + e) * v[c];
+            put_dg(e, load4<T>(a_row + e) * v[c]);
             *reinterpret_cast<f32x4 *>(g_row + e) = gr[c] * v[c];
             *reinterpret_cast<f32x4 *>(ag_row + e) = ag[c];
         }
@@ -395,6 +426,102 @@ __global__ __launch_bounds__(512) void wh_grad_kernel(const float *__restrict__ 
     }
 }
 
+// bf16 operands: dW_H += (dg_hi + dg_lo)^T h on the bf16 MFMA 16x16x32, k =
+// 32 rows per step.  Lane l (m = l % 16, q = l / 16) feeds rank rows
+// i0 + 4 m + s of tile s (one 16-byte load of 8 packed rows per half) and
+// hidden columns j0 + 4 m + t of tile t: it loads 4 columns of each of its 8
+// rows (8 bytes each) and rearranges them into one 8-row fragment per column.
+// Tile (s, t) then holds C[i0 + 4 (4 q + e) + s][j0 + 4 m + t] in register e.
+// The eight waves of a workgroup take the 32-row steps in turn and sum their
+// partial tiles in LDS.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+__global__ __launch_bounds__(512) void wh_grad_bf16_kernel(const uint16_t *__restrict__ dg_hi,
+                                                           const uint16_t *__restrict__ dg_lo,
+                                                           const uint16_t *__restrict__ h, int N, int H, int r,
+                                                           float *__restrict__ dW) {
+    extern __shared__ __align__(16) float part[];  // [wave][64][64]
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int i0 = blockIdx.x * kWhTile, j0 = blockIdx.y * kWhTile;
+    const int m = lane & 15, q = lane >> 4;
+    const int ia = i0 + 4 * m, jb = j0 + 4 * m;
+    const bool a_ok = ia < r;  // r % 8 == 0: the 4 rows of a lane are wholly in or out
+    const int n_steps = (N + 31) / 32;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    struct Ops {
+        uint4 hi[4], lo[4];
+        uint2 hv[8];
+    };
+    auto fetch = [&](int step, Ops &o) {
+        const int g8 = step * 4 + q;  // this lane group's 8-row group
+        const bool ok = step < n_steps && g8 < (N + 7) / 8;
+        const size_t abase = ((size_t)(ok ? g8 : 0) * r + (a_ok ? ia : 0)) * 8;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            o.hi[s] = (ok && a_ok) ? *reinterpret_cast<const uint4 *>(dg_hi + abase + 8 * s) : make_uint4(0u, 0u, 0u, 0u);
+            o.lo[s] = (ok && a_ok) ? *reinterpret_cast<const uint4 *>(dg_lo + abase + 8 * s) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int n = g8 * 8 + p;
+            const bool rok = ok && n < N;  // rows past N: dg is zero there, h is not read
+            o.hv[p] = rok ? *reinterpret_cast<const uint2 *>(h + (size_t)n * H + jb) : make_uint2(0u, 0u);
+        }
+    };
+    Ops cur, nxt;
+    fetch(wave, cur);
+    for (int step = wave; step < n_steps; step += kWhWaves) {
+        fetch(step + kWhWaves, nxt);
+        uint4 b[4];  // column t of the 8 rows, rows in pairs
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint2 x = cur.hv[2 * d], y = cur.hv[2 * d + 1];
+            reinterpret_cast<uint32_t *>(&b[0])[d] = pack_lo16(x.x, y.x);
+            reinterpret_cast<uint32_t *>(&b[1])[d] = pack_hi16(x.x, y.x);
+            reinterpret_cast<uint32_t *>(&b[2])[d] = pack_lo16(x.y, y.y);
+            reinterpret_cast<uint32_t *>(&b[3])[d] = pack_hi16(x.y, y.y);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                acc[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.hi[s]),
+                                                                    __builtin_bit_cast(bf16x8, b[t]), acc[s][t], 0, 0, 0);
+                acc[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.lo[s]),
+                                                                    __builtin_bit_cast(bf16x8, b[t]), acc[s][t], 0, 0, 0);
+            }
+        cur = nxt;
+    }
+    float *mine = part + (size_t)wave * kWhTile * kWhTile;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int il = 4 * (4 * q + e) + s;
+            *reinterpret_cast<f32x4 *>(mine + il * kWhTile + 4 * m) =
+                f32x4{acc[s][0][e], acc[s][1][e], acc[s][2][e], acc[s][3][e]};
+        }
+    __syncthreads();
+    const int il = (8 * (int)threadIdx.x) / kWhTile, jl = (8 * (int)threadIdx.x) % kWhTile;
+    f32x4 s0{0.f, 0.f, 0.f, 0.f}, s1{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWhWaves; ++w) {
+        const float *pw = part + (size_t)w * kWhTile * kWhTile + il * kWhTile + jl;
+        s0 += *reinterpret_cast<const f32x4 *>(pw);
+        s1 += *reinterpret_cast<const f32x4 *>(pw + 4);
+    }
+    if (i0 + il < r) {
+        float *out = dW + (size_t)(i0 + il) * H + j0 + jl;
+        *reinterpret_cast<f32x4 *>(out) = *reinterpret_cast<const f32x4 *>(out) + s0;
+        *reinterpret_cast<f32x4 *>(out + 4) = *reinterpret_cast<const f32x4 *>(out + 4) + s1;
+    }
+}
+
 // ------------------------------------------------------------------ host side
 
 hipError_t launch_selector_ce_backward(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
@@ -467,7 +594,15 @@ hipError_t launch_selector_ce_backward(int dtype, int64_t N, int H, int V, int r
         hipLaunchKernelGGL(kern, wgrid, dim3(64 * kWhWaves), kWhLds, stream, dg, hp, (int)N, H, r, grad_wh);
         return hipGetLastError();
     };
-    return dtype == 0 ? wh(wh_grad_kernel<float>, (const float *)h) : wh(wh_grad_kernel<uint16_t>, (const uint16_t *)h);
+    if (dtype == 0) return wh(wh_grad_kernel<float>, (const float *)h);
+    const uint16_t *dg_hi = reinterpret_cast<const uint16_t *>(dg);
+    const uint16_t *dg_lo = dg_hi + (size_t)(N + 7) / 8 * 8 * r;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(wh_grad_bf16_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWhLds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(wh_grad_bf16_kernel, wgrid, dim3(64 * kWhWaves), kWhLds, stream, dg_hi, dg_lo,
+                       (const uint16_t *)h, (int)N, H, r, grad_wh);
+    return hipGetLastError();
 }
 
 }  // namespace dflash2
