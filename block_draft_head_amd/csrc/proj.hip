@@ -356,11 +356,12 @@ static hipError_t run_proj_dma(int64_t M, int H, int n_col_tiles, const void *A,
     return hipGetLastError();
 }
 
-// The largest tile whose grid still fills the chip: larger tiles read fewer
+// The larger tile once its grid covers half the chip: larger tiles read fewer
 // bytes per MFMA, and a workgroup's stream rate is bounded by the bytes its
-// ring keeps in flight.
+// ring keeps in flight (measured on 512 rows x 5120 x 1280: 64 x 64 tiles on
+// 160 workgroups 41 us, 32 x 32 tiles on 640 workgroups 46 us).
 template <class Cfg> static bool proj_fills(int64_t M, int n_col_tiles) {
-    return (M + Cfg::BM - 1) / Cfg::BM * n_col_tiles >= 256;
+    return (M + Cfg::BM - 1) / Cfg::BM * n_col_tiles >= 128;
 }
 
 template <typename T, class Epi>
