@@ -136,6 +136,8 @@ TOPK_EX_CASES = [
     (5, 512, 5003, 64, "bf16", 0.8, 8.0), (8, 320, 4099, 8, "bf16", 1.0, 0.0), (5, 256, 7001, 16, "f32", 2.0, 3.0),
     (300, 256, 5000, 16, "bf16", 1.0, 30.0), (40, 512, 9001, 64, "bf16", 0.5, 0.0),
     (600, 256, 70001, 5, "bf16", 1.3, 4.0), (100, 256, 3001, 16, "f32", 1.0, 1.5),
+    # K = V (every id a candidate); K = 1 under a tight cap
+    (1, 256, 64, 64, "bf16", 1.0, 5.0), (9, 256, 100, 1, "f32", 2.0, 0.5),
 ]
 
 
@@ -458,6 +460,8 @@ CE_BWD_CASES = [
     (128, 256, 4096, 32, 16, "f32"), (200, 256, 1000, 256, 16, "bf16"), (333, 512, 3000, 40, 20, "bf16"),
     (64, 256, 500, 512, 64, "bf16"), (37, 256, 800, 264, 33, "f32"), (24, 256, 300, 8, 1, "bf16"),
     (1, 256, 100, 16, 5, "bf16"), (1000, 320, 2000, 256, 16, "bf16"),
+    # the rank limit; every vocabulary id a candidate of every row
+    (16, 256, 500, 4096, 8, "bf16"), (9, 256, 64, 8, 64, "f32"),
 ]
 
 
@@ -503,6 +507,21 @@ def test_selector_ce_backward(D, N, H, V, r, K, dtype):
     assert fails == 0, msgs
     if K > 1 and rvalid.any():
         assert np.abs(dB).max() > 0 and np.abs(dW).max() > 0
+
+
+def test_selector_ce_backward_with_every_row_excluded_adds_nothing(D):
+    # no gold among the candidates and nothing forced: no CE, no gradient
+    N, H, V, r, K = 40, 256, 600, 32, 8
+    inp, ids, vals, _, glog, wgt = ce_bwd_inputs(N, H, V, r, K, "bf16", seed=29)
+    gold = np.full(N, V - 1, np.int32)
+    ids = ids % (V - 1)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    pre = [torch.full(sh, 0.25, dtype=torch.float32, device="cuda") for sh in ((V, r), (V, r), (r, H))]
+    gp, gs, gw, ce, valid = D.selector_ce_backward(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], to_dev(ids),
+                                                   to_dev(vals), dev["pred"], to_dev(gold), to_dev(wgt),
+                                                   grad_pred=pre[0], grad_succ=pre[1], grad_wh=pre[2])
+    assert not to_np(valid).any() and not to_np(ce).any()
+    assert all(bool((t == 0.25).all()) for t in (gp, gs, gw))
 
 
 def test_selector_ce_backward_accumulates_and_skips_bad_rows(D):
