@@ -264,24 +264,33 @@ __device__ __forceinline__ void proj_tile_of(int bid, int n_rt, int n_ct, int &r
 using DmaTileBig = DmaTileCfg<64, 64, 4>;
 using DmaTileSmall = DmaTileCfg<32, 32, 8>;
 
-template <class Cfg, class Epi>
-__global__ __launch_bounds__(256) void proj_dma_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
-                                                       int M, int H, int n_ct, Epi epi) {
+// KSPLIT = 2 (grids with fewer workgroups than CUs): 8 waves, two groups of
+// 4 each with its own ring taking one half of the k stages, so a CU keeps
+// twice the bytes in flight; group 1 hands its accumulators to group 0
+// through LDS before the epilogue.  The groups run the same number of steps
+// (a group with one stage fewer repeats its last copy and skips its MFMAs), so
+// every wave meets every barrier.
+template <class Cfg, class Epi, int KSPLIT>
+__global__ __launch_bounds__(256 * KSPLIT) void proj_dma_kernel(const uint16_t *__restrict__ A,
+                                                                const uint16_t *__restrict__ W, int M, int H,
+                                                                int n_ct, Epi epi) {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int NS = Cfg::NS, CPW = Cfg::CPW;
     int rt, ct;
     proj_tile_of(blockIdx.x, (M + Cfg::BM - 1) / Cfg::BM, n_ct, rt, ct);
     const int m0 = rt * Cfg::BM;
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1, n = lane & 15, q = lane >> 4;
-    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)smem;
-    // this lane's chunk of each of its copies: stage row (wave CPW + c) 8 + L / 8
+    const int lw = wave & 3, kg = wave >> 2;  // wave within its group, group
+    const int wm = lw >> 1, wn = lw & 1, n = lane & 15, q = lane >> 4;
+    uint8_t *ring = smem + (size_t)kg * NS * Cfg::STAGE;
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)ring;
+    // this lane's chunk of each of its copies: stage row (lw CPW + c) 8 + L / 8
     // (A rows, then W rows), chunk (L % 8) ^ (row % 8).  Rows past M or past
     // the projection read row 0; their outputs are never used.
     const uint8_t *src[CPW];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-        const int row = (wave * CPW + c) * 8 + (lane >> 3);
+        const int row = (lw * CPW + c) * 8 + (lane >> 3);
         const uint16_t *rp;
         if (row < Cfg::BM) {
             const int r = m0 + row;
@@ -293,10 +302,13 @@ __global__ __launch_bounds__(256) void proj_dma_kernel(const uint16_t *__restric
         src[c] = reinterpret_cast<const uint8_t *>(rp) + (((lane & 7) ^ (row & 7)) << 4);
     }
     const int nk = H / 64;
-    // stage s (the last one again past the end) into slot s % NS
+    const int nk0 = KSPLIT == 1 ? nk : nk / 2;                   // group 0's stages
+    const int k_begin = kg == 0 ? 0 : nk0, k_count = kg == 0 ? nk0 : nk - nk0;
+    const int steps = nk - nk0 > nk0 ? nk - nk0 : nk0;           // both groups
+    // local stage s (the group's last one again past its end) into slot s % NS
     auto issue = [&](int s) {
-        const size_t kb = (size_t)(s < nk ? s : nk - 1) * 128;
-        const uint32_t base = lds0 + (uint32_t)((s % NS) * Cfg::STAGE + wave * CPW * 1024);
+        const size_t kb = (size_t)(k_begin + (s < k_count ? s : k_count - 1)) * 128;
+        const uint32_t base = lds0 + (uint32_t)((s % NS) * Cfg::STAGE + lw * CPW * 1024);
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
             const uint8_t *p = src[c] + kb;
@@ -312,12 +324,13 @@ __global__ __launch_bounds__(256) void proj_dma_kernel(const uint16_t *__restric
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < NS - 1; ++s) issue(s);
-    for (int s = 0; s < nk; ++s) {
+    for (int s = 0; s < steps; ++s) {
         // stage s has landed (the NS - 2 after it may still fly) in every wave,
         // and every wave has finished reading stage s - 1, whose slot is refilled
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(CPW * (NS - 2)) : "memory");
         issue(s + NS - 1);
-        const uint8_t *st = smem + (s % NS) * Cfg::STAGE;
+        if (s >= k_count) continue;
+        const uint8_t *st = ring + (s % NS) * Cfg::STAGE;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int pos = ((ks * 4 + q) ^ (n & 7)) << 4;
@@ -336,7 +349,26 @@ __global__ __launch_bounds__(256) void proj_dma_kernel(const uint16_t *__restric
     }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     float *C = reinterpret_cast<float *>(smem);
-    tiled_store_c<Cfg>(C, acc);
+    if constexpr (KSPLIT == 2) {
+        // group 1's accumulators, lane by lane, over its idle ring
+        f32x4 *part = reinterpret_cast<f32x4 *>(smem + (size_t)NS * Cfg::STAGE) + (size_t)(lw * 64 + lane) * Cfg::TM * Cfg::TN;
+        if (kg == 1) {
+#pragma unroll
+            for (int a = 0; a < Cfg::TM; ++a)
+#pragma unroll
+                for (int b = 0; b < Cfg::TN; ++b) part[a * Cfg::TN + b] = acc[a][b];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int a = 0; a < Cfg::TM; ++a)
+#pragma unroll
+                for (int b = 0; b < Cfg::TN; ++b) acc[a][b] += part[a * Cfg::TN + b];
+            tiled_store_c<Cfg>(C, acc);
+        }
+    } else {
+        tiled_store_c<Cfg>(C, acc);
+    }
     __syncthreads();
     epi(C, Cfg::CSTRIDE, m0, min(Cfg::BM, M - m0), ct, Cfg::BN);
 }
@@ -346,14 +378,20 @@ __global__ __launch_bounds__(256) void proj_dma_kernel(const uint16_t *__restric
 template <class Cfg, class Epi>
 static hipError_t run_proj_dma(int64_t M, int H, int n_col_tiles, const void *A, const void *W, const Epi &epi,
                                hipStream_t stream) {
-    auto kern = proj_dma_kernel<Cfg, Epi>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-    if (e != hipSuccess) return e;
     const int n_rt = (int)((M + Cfg::BM - 1) / Cfg::BM);
-    hipLaunchKernelGGL(kern, dim3(n_rt * n_col_tiles), dim3(256), Cfg::LDS, stream, (const uint16_t *)A,
-                       (const uint16_t *)W, (int)M, H, n_col_tiles, epi);
-    return hipGetLastError();
+    auto go = [&](auto kern, int ksplit) -> hipError_t {
+        const int lds = ksplit * Cfg::NS * Cfg::STAGE > Cfg::LDS ? ksplit * Cfg::NS * Cfg::STAGE : Cfg::LDS;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(n_rt * n_col_tiles), dim3(256 * ksplit), lds, stream, (const uint16_t *)A,
+                           (const uint16_t *)W, (int)M, H, n_col_tiles, epi);
+        return hipGetLastError();
+    };
+    // fewer workgroups than CUs (one per CU): split k over two rings
+    if (n_rt * n_col_tiles < 256 && H / 64 >= 2 && 2 * Cfg::NS * Cfg::STAGE <= 160 * 1024)
+        return go(proj_dma_kernel<Cfg, Epi, 2>, 2);
+    return go(proj_dma_kernel<Cfg, Epi, 1>, 1);
 }
 
 // The larger tile once its grid covers half the chip: larger tiles read fewer
