@@ -149,7 +149,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
-              f"multi-GPU mode in this build", file=sys.stderr)
+              f"multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
