@@ -64,20 +64,20 @@ __device__ __forceinline__ void atomic_add(float *p, float v) { unsafeAtomicAdd(
 }  // namespace
 
 // ------------------------------------------------------------------ per-row kernel
-// Lane l holds elements 4 l + 256 c .. +3 of the rank dimension for chunk
-// c < NC (r <= 256 NC).  Lane k < K holds slot k's id, score and d.
+// One wave per row.  Lane l holds elements 4 l + 256 c .. +3 of the rank
+// dimension for chunk c < NC (r <= 256 NC).  Lane k < K holds slot k's id,
+// score and d.  dg goes to dg_row (float32 inputs) or to the wave's LDS row
+// dgs_row (bf16 inputs, packed by the workgroup afterwards).
 template <typename T, int NC>
-__global__ __launch_bounds__(256) void ce_grad_rows_kernel(
-    float *g, const T *__restrict__ A, const T *__restrict__ B, const int32_t *__restrict__ cand_ids,
+__device__ __forceinline__ void ce_grad_row(
+    long long n, float *g, const T *__restrict__ A, const T *__restrict__ B, const int32_t *__restrict__ cand_ids,
     const float *__restrict__ cand_vals, const int32_t *__restrict__ pred_ids,
     const int32_t *__restrict__ gold_ids, const uint8_t *__restrict__ force,
-    const float *__restrict__ gold_logit, const float *__restrict__ grad_ce, long long N, int V, int r, int K,
-    float *__restrict__ ag_out, float *__restrict__ dg, int32_t *__restrict__ tgt, float *__restrict__ wgt,
-    int32_t *__restrict__ counts, float *__restrict__ out_ce, uint8_t *__restrict__ out_valid,
-    uint32_t *__restrict__ status) {
+    const float *__restrict__ gold_logit, const float *__restrict__ grad_ce, int V, int r, int K,
+    float *__restrict__ ag_out, float *__restrict__ dg, float *dgs_row, int32_t *__restrict__ tgt,
+    float *__restrict__ wgt, int32_t *__restrict__ counts, float *__restrict__ out_ce,
+    uint8_t *__restrict__ out_valid, uint32_t *__restrict__ status) {
     const int lane = lane_id();
-    const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (n >= N) return;
     const size_t nk = (size_t)n * K, e0 = (size_t)n * (K + 1);
     int my_id = lane < K ? cand_ids[nk + lane] : 0;
     float my_u = lane < K ? cand_vals[nk + lane] : 0.f;
@@ -99,35 +99,9 @@ __global__ __launch_bounds__(256) void ce_grad_rows_kernel(
         }
     }
     float *dg_row = dg + (size_t)n * r;
-    // bf16: dg goes out as its truncated bf16 high part and the bf16 of the
-    // remainder, packed 8 rows deep: element (n, i) at ((n / 8) r + i) 8 + n % 8
-    // of each half (the last group's missing rows are zero)
-    uint16_t *dg_hi = reinterpret_cast<uint16_t *>(dg), *dg_lo = dg_hi + (size_t)(N + 7) / 8 * 8 * r;
     auto put_dg = [&](int e, f32x4 v) {
-        if constexpr (sizeof(T) == 2) {
-            const size_t base = ((size_t)(n >> 3) * r + e) * 8 + (n & 7);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t hb = __float_as_uint(v[i]) & 0xffff0000u;
-                dg_hi[base + 8 * i] = (uint16_t)(hb >> 16);
-                dg_lo[base + 8 * i] = (uint16_t)(__float_as_uint(v[i] - __uint_as_float(hb)) >> 16);
-            }
-        } else {
-            *reinterpret_cast<f32x4 *>(dg_row + e) = v;
-        }
+        *reinterpret_cast<f32x4 *>((sizeof(T) == 2 ? dgs_row : dg_row) + e) = v;
     };
-    if constexpr (sizeof(T) == 2) {
-        if (n == N - 1 && (N & 7) != 0) {
-            for (int e = 4 * lane; e < r; e += 256)
-                for (int p = (int)(N & 7); p < 8; ++p)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const size_t at = ((size_t)(n >> 3) * r + e + i) * 8 + p;
-                        dg_hi[at] = 0;
-                        dg_lo[at] = 0;
-                    }
-        }
-    }
     if (kg < 0) {  // excluded row: no CE, no gradient, no entries
         for (int e = 4 * lane; e < r; e += 256) put_dg(e, f32x4{0.f, 0.f, 0.f, 0.f});
         for (int j = lane; j <= K; j += 64) tgt[e0 + j] = -1;
@@ -201,6 +175,50 @@ __global__ __launch_bounds__(256) void ce_grad_rows_kernel(
         tgt[e0 + K] = V + p;
         wgt[e0 + K] = 1.f;
         atomicAdd(counts + V + p, 1);
+    }
+}
+
+// Eight rows per workgroup.  bf16: the rows' dg meet in LDS and go out as
+// their truncated bf16 high part and the bf16 of the remainder, packed 8 rows
+// deep (element (n, i) at ((n / 8) r + i) 8 + n % 8 of each half; rows past N
+// are zero), one 16-byte store per rank element and half.
+template <typename T, int NC>
+__global__ __launch_bounds__(512) void ce_grad_rows_kernel(
+    float *g, const T *__restrict__ A, const T *__restrict__ B, const int32_t *__restrict__ cand_ids,
+    const float *__restrict__ cand_vals, const int32_t *__restrict__ pred_ids,
+    const int32_t *__restrict__ gold_ids, const uint8_t *__restrict__ force,
+    const float *__restrict__ gold_logit, const float *__restrict__ grad_ce, long long N, int V, int r, int K,
+    float *__restrict__ ag_out, float *__restrict__ dg, int32_t *__restrict__ tgt, float *__restrict__ wgt,
+    int32_t *__restrict__ counts, float *__restrict__ out_ce, uint8_t *__restrict__ out_valid,
+    uint32_t *__restrict__ status) {
+    extern __shared__ __align__(16) float dgs[];  // bf16: [8][r]
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const long long n = (long long)blockIdx.x * 8 + wave;
+    float *my_dgs = dgs + (size_t)wave * r;
+    if (n < N) {
+        ce_grad_row<T, NC>(n, g, A, B, cand_ids, cand_vals, pred_ids, gold_ids, force, gold_logit, grad_ce, V, r,
+                           K, ag_out, dg, my_dgs, tgt, wgt, counts, out_ce, out_valid, status);
+    } else if constexpr (sizeof(T) == 2) {
+        for (int e = 4 * lane; e < r; e += 256) *reinterpret_cast<f32x4 *>(my_dgs + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (sizeof(T) == 2) {
+        __syncthreads();
+        uint16_t *dg_hi = reinterpret_cast<uint16_t *>(dg), *dg_lo = dg_hi + (size_t)(N + 7) / 8 * 8 * r;
+        for (int i = threadIdx.x; i < r; i += blockDim.x) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int p = 0; p < 8; p += 2) {
+                const float v0 = dgs[(size_t)p * r + i], v1 = dgs[(size_t)(p + 1) * r + i];
+                const uint32_t h0 = __float_as_uint(v0) & 0xffff0000u, h1 = __float_as_uint(v1) & 0xffff0000u;
+                const uint32_t l0 = __float_as_uint(v0 - __uint_as_float(h0)) & 0xffff0000u;
+                const uint32_t l1 = __float_as_uint(v1 - __uint_as_float(h1)) & 0xffff0000u;
+                hw[p / 2] = (h0 >> 16) | h1;
+                lw[p / 2] = (l0 >> 16) | l1;
+            }
+            const size_t at = ((size_t)blockIdx.x * r + i) * 8;
+            *reinterpret_cast<uint4 *>(dg_hi + at) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            *reinterpret_cast<uint4 *>(dg_lo + at) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
     }
 }
 
@@ -551,12 +569,16 @@ hipError_t launch_selector_ce_backward(int dtype, int64_t N, int H, int V, int r
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)zgrid), dim3(256), 0, stream, counts, (long long)C);
     hipError_t e = launch_context_proj(dtype, N, H, r, h, w_h, g, status, stream);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)((N + 3) / 4);
+    const unsigned grid = (unsigned)((N + 7) / 8);
     const int nc = (r + 255) / 256;
     auto rows = [&](const auto *Ap, const auto *Bp) -> hipError_t {
         using T = std::remove_cv_t<std::remove_pointer_t<decltype(Ap)>>;
+        const size_t lds = sizeof(T) == 2 ? (size_t)8 * r * 4 : 0;
         auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, g, Ap, Bp, cand_ids, cand_vals, pred_ids,
+            hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (err != hipSuccess) return err;
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(512), lds, stream, g, Ap, Bp, cand_ids, cand_vals, pred_ids,
                                gold_ids, force, gold_logit, grad_ce, (long long)N, V, r, K, ag, dg, tgt, wgt, counts,
                                out_ce, out_valid, status);
             return hipGetLastError();
