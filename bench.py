@@ -295,6 +295,22 @@ def main():
         _, best, _, _ = op_tf(ids, vals)
         replay_ok = bool(torch.equal(best.view(w.n_blocks, bs)[:, 1:], res[0][:, 1:]))
 
+    # achievable HBM rate on this device: a 1 GiB device-to-device copy (read
+    # plus write bytes over its event time, best of 5), beside the 8 TB/s peak
+    cs = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cd = torch.empty_like(cs)
+    cd.copy_(cs)
+    copy_ms = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cd.copy_(cs)
+        b.record()
+        torch.cuda.synchronize()
+        copy_ms.append(a.elapsed_time(b))
+    copy_gbs = 2.0 * (1 << 30) / (min(copy_ms) * 1e-3) / 1e9
+    del cs, cd
+
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -354,6 +370,7 @@ def main():
         "ce_backward": backward_report(w, bwd_ms) if tf_mode else None,
         "tf_replays_walk": replay_ok,
         "wall_s_timed": wall,
+        "copy_gbs": copy_gbs,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
