@@ -284,9 +284,12 @@ __global__ __launch_bounds__(256) void scan_tile_prefix_kernel(int32_t *__restri
     }
 }
 
+// own_prefix: tile_prefix holds the tile sums, and each workgroup adds up
+// those before its own tile (used for at most kScanOwnPrefixTiles tiles)
+constexpr int kScanOwnPrefixTiles = 1024;
 __global__ __launch_bounds__(256) void scan_apply_kernel(int32_t *__restrict__ counts, int C,
                                                          const int32_t *__restrict__ tile_prefix,
-                                                         int32_t *__restrict__ offsets) {
+                                                         int32_t *__restrict__ offsets, int own_prefix) {
     __shared__ int lds4[4];
     const long long base = (long long)blockIdx.x * kScanTile + threadIdx.x * kScanPer;
     int v[kScanPer], x = 0;
@@ -296,7 +299,17 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(int32_t *__restrict__ c
         x += v[i];
     }
     int total;
-    int run = block_exclusive_scan(x, lds4, total) + tile_prefix[blockIdx.x];
+    int prefix;
+    if (own_prefix) {
+        int part = 0;
+        for (int b = threadIdx.x; b < (int)blockIdx.x; b += kScanThreads) part += tile_prefix[b];
+        int all;
+        block_exclusive_scan(part, lds4, all);
+        prefix = all;
+    } else {
+        prefix = tile_prefix[blockIdx.x];
+    }
+    int run = block_exclusive_scan(x, lds4, total) + prefix;
 #pragma unroll
     for (int i = 0; i < kScanPer; ++i)
         if (base + i < C) {
@@ -593,8 +606,9 @@ hipError_t launch_selector_ce_backward(int dtype, int64_t N, int H, int V, int r
     if (e != hipSuccess) return e;
 
     hipLaunchKernelGGL(scan_tile_sums_kernel, dim3(n_tiles), dim3(256), 0, stream, counts, C, tiles);
-    hipLaunchKernelGGL(scan_tile_prefix_kernel, dim3(1), dim3(256), 0, stream, tiles, n_tiles);
-    hipLaunchKernelGGL(scan_apply_kernel, dim3(n_tiles), dim3(256), 0, stream, counts, C, tiles, offsets);
+    const int own = n_tiles <= kScanOwnPrefixTiles ? 1 : 0;
+    if (!own) hipLaunchKernelGGL(scan_tile_prefix_kernel, dim3(1), dim3(256), 0, stream, tiles, n_tiles);
+    hipLaunchKernelGGL(scan_apply_kernel, dim3(n_tiles), dim3(256), 0, stream, counts, C, tiles, offsets, own);
     hipLaunchKernelGGL(place_entries_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, stream, tgt, E,
                        offsets, counts, src);
     auto scatter = [&](auto kern) {

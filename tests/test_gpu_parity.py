@@ -462,6 +462,8 @@ CE_BWD_CASES = [
     (1, 256, 100, 16, 5, "bf16"), (1000, 320, 2000, 256, 16, "bf16"),
     # the rank limit; every vocabulary id a candidate of every row
     (16, 256, 500, 4096, 8, "bf16"), (9, 256, 64, 8, 64, "f32"),
+    # a vocabulary whose 2V + 1 counters span more than 1024 scan tiles
+    (50, 256, 2_200_000, 8, 4, "bf16"),
 ]
 
 
