@@ -464,6 +464,9 @@ CE_BWD_CASES = [
     (16, 256, 500, 4096, 8, "bf16"), (9, 256, 64, 8, 64, "f32"),
     # a vocabulary whose 2V + 1 counters span more than 1024 scan tiles
     (50, 256, 2_200_000, 8, 4, "bf16"),
+    # a 50-token vocabulary: every id is a candidate of ~64 rows, so many
+    # codebook rows gather more than one 64-entry chunk (chunks add atomically)
+    (200, 256, 50, 32, 16, "bf16"),
 ]
 
 
