@@ -131,7 +131,7 @@ struct EpiConv {
                 // loads every tap operand of IB items before any sum, so the
                 // loads overlap instead of each waiting out its latency; the
                 // sums keep the tap order of the scalar path below.
-                constexpr int IB = TMAX <= 2 ? 4 : TMAX <= 4 ? 2 : 1;
+                constexpr int IB = TMAX <= 2 ? 4 : TMAX <= 8 ? 2 : 1;
                 const int chunks = nc / 8, items = nrows * chunks, h0 = g0 * gs;
                 for (int i0 = threadIdx.x; i0 < items; i0 += IB * blockDim.x) {
                     uint4 xv[IB][TMAX], bv[IB][TMAX];
