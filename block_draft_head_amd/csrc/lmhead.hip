@@ -1301,6 +1301,83 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const uint64_t *__restr
     }
 }
 
+// Rows whose lists hold at most kMergeChunk keys in all: one wave per row,
+// four rows per workgroup (the workgroup-per-row kernel would leave seven of
+// its eight waves idle).  Same results as topk_merge_kernel: the same key
+// selection, gold dot product order aside (summed over the wave's lanes).
+template <typename T>
+__global__ __launch_bounds__(256) void topk_merge_rows_kernel(const uint64_t *__restrict__ partial, int M, int n_keys,
+                                                              int K, int V, int32_t *__restrict__ out_ids,
+                                                              float *__restrict__ out_vals,
+                                                              const int32_t *__restrict__ gold,
+                                                              float *__restrict__ gold_logit,
+                                                              uint32_t *__restrict__ status,
+                                                              const T *__restrict__ gold_h,
+                                                              const T *__restrict__ gold_w, int H, UnaryEpi ue,
+                                                              int n_lists, float *__restrict__ out_lse,
+                                                              float *__restrict__ out_prob,
+                                                              uint8_t *__restrict__ out_hit) {
+    __shared__ uint64_t scratch[4 * 128];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * 4 + wave;
+    if (row >= M) return;
+    const uint64_t *src = partial + (size_t)row * n_keys;
+    uint64_t k[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = lane * 8 + i < n_keys ? src[lane * 8 + i] : 0ull;
+    const uint64_t top = wave_topk<8>(k, K, scratch + wave * 128);
+    int32_t *oi = out_ids + (size_t)row * K;
+    if (lane < K) {
+        oi[lane] = top ? (int32_t)key_id(top) : -1;
+        out_vals[(size_t)row * K + lane] = top ? unary_transform(key_val(top), ue.mult, ue.cap) : -__builtin_inff();
+    }
+    float lse = 0.f;
+    if (ue.lse_part) {
+        float m = -__builtin_inff(), sm = 0.f;
+        for (int i = lane; i < n_lists; i += 64) {
+            const float2 ps = ue.lse_part[(size_t)row * n_lists + i];
+            lse_merge(m, sm, ps.x, ps.y);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) lse_merge(m, sm, __shfl_xor(m, o), __shfl_xor(sm, o));
+        lse = m + logf(sm);
+        if (out_lse && lane == 0) out_lse[row] = lse;
+    }
+    if (!gold) return;
+    const int g = gold[row];
+    const bool g_ok = g >= 0 && g < V;
+    if (out_hit) {
+        const bool hit = g_ok && lane < K && top && (int32_t)key_id(top) == g;
+        const unsigned long long b = __ballot(hit);
+        if (lane == 0) out_hit[row] = b ? 1 : 0;
+    }
+    float u = 0.f;
+    if (gold_h && g_ok) {
+        const T *x = gold_h + (size_t)row * H, *y = gold_w + (size_t)g * H;
+        float acc = 0.f;
+        for (int c = lane; c < H / 8; c += 64) {
+            float a[8], bb[8];
+            load8<T>(x + c * 8, a);
+            load8<T>(y + c * 8, bb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf(a[e], bb[e], acc);
+        }
+        u = wave_sum_f32(acc);
+    } else if (g_ok) {
+        u = gold_logit[row];  // written by the LM-head kernel
+    }
+    if (lane == 0) {
+        if (!g_ok) {
+            gold_logit[row] = __builtin_nanf("");
+            flag_status(status, kStatusIdRange);
+        } else {
+            u = unary_transform(u, ue.mult, ue.cap);
+            gold_logit[row] = u;
+            if (out_prob) out_prob[row] = __expf(u - lse);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- host side
 
 static int first_stage_keys(int n_keys, int K) {
@@ -1454,9 +1531,16 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
+    const int n_keys = p.n_lists * p.list_len;
+    if (n_keys <= kMergeChunk) {
+        hipLaunchKernelGGL(topk_merge_rows_kernel<T>, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, partial,
+                           (int)M, n_keys, K, V, out_ids, out_vals, gold, gold_logit, status,
+                           p.big ? (const T *)h : nullptr, p.big ? (const T *)w : nullptr, H, ue, p.n_lists, um.lse,
+                           um.gold_prob, um.hit);
+        return hipGetLastError();
+    }
     auto merge = topk_merge_kernel<T>;
     if ((e = set_lds(merge, p.merge_lds)) != hipSuccess) return e;
-    const int n_keys = p.n_lists * p.list_len;
     hipLaunchKernelGGL(merge, dim3((unsigned)M), dim3(512), p.merge_lds, stream, partial, (int)M, n_keys, K, V,
                        out_ids, out_vals, gold, gold_logit, status, first_stage_keys(n_keys, K),
                        p.big ? (const T *)h : nullptr, p.big ? (const T *)w : nullptr, H, ue, p.n_lists, um.lse,
