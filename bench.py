@@ -336,10 +336,10 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(w, w.name)
-    roof["kernel"] = ("lmhead_dma_kernel + topk_merge_kernel" if N <= 8 and w.dtype == "bf16" else
-                      "lmhead_stream_kernel + topk_merge_kernel" if N <= 8 else
-                      "lmhead_big_kernel + topk_merge_kernel" if w.dtype == "bf16" else
-                      "lmhead_tiled_kernel + topk_merge_kernel")
+    roof["kernel"] = ("lmhead_dma_kernel + top-K merge" if N <= 8 and w.dtype == "bf16" else
+                      "lmhead_stream_kernel + top-K merge" if N <= 8 else
+                      "lmhead_big_kernel + top-K merge" if w.dtype == "bf16" else
+                      "lmhead_tiled_kernel + top-K merge")
     roof["algorithmic_bytes"] = lm_bytes
     roof["avg_ms"] = lm_ms
 
