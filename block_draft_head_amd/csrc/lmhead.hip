@@ -1301,10 +1301,12 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const uint64_t *__restr
     }
 }
 
-// Rows whose lists hold at most kMergeChunk keys in all: one wave per row,
-// four rows per workgroup (the workgroup-per-row kernel would leave seven of
-// its eight waves idle).  Same results as topk_merge_kernel: the same key
-// selection, gold dot product order aside (summed over the wave's lanes).
+// Rows whose lists hold at most kMergeRowsKeys keys in all: one wave per row,
+// four rows per workgroup (the workgroup-per-row kernel would leave most of
+// its eight waves idle), the wave taking the row's keys kMergeChunk at a time
+// with its running top K beside them.  Same keys selected as
+// topk_merge_kernel; the gold dot product is summed in another order.
+constexpr int kMergeRowsKeys = 2 * kMergeChunk;
 template <typename T>
 __global__ __launch_bounds__(256) void topk_merge_rows_kernel(const uint64_t *__restrict__ partial, int M, int n_keys,
                                                               int K, int V, int32_t *__restrict__ out_ids,
@@ -1322,10 +1324,17 @@ __global__ __launch_bounds__(256) void topk_merge_rows_kernel(const uint64_t *__
     const int row = blockIdx.x * 4 + wave;
     if (row >= M) return;
     const uint64_t *src = partial + (size_t)row * n_keys;
-    uint64_t k[8];
+    uint64_t top = 0;  // lane j < K: the j-th best key so far
+    for (int base = 0; base < n_keys; base += kMergeChunk) {
+        uint64_t k[9];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) k[i] = lane * 8 + i < n_keys ? src[lane * 8 + i] : 0ull;
-    const uint64_t top = wave_topk<8>(k, K, scratch + wave * 128);
+        for (int i = 0; i < 8; ++i) {
+            const int idx = base + lane * 8 + i;
+            k[i] = idx < n_keys ? src[idx] : 0ull;
+        }
+        k[8] = top;
+        top = wave_topk<9>(k, K, scratch + wave * 128);
+    }
     int32_t *oi = out_ids + (size_t)row * K;
     if (lane < K) {
         oi[lane] = top ? (int32_t)key_id(top) : -1;
@@ -1532,7 +1541,7 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
     }
     if (e != hipSuccess) return e;
     const int n_keys = p.n_lists * p.list_len;
-    if (n_keys <= kMergeChunk) {
+    if (n_keys <= kMergeChunk || (n_keys <= kMergeRowsKeys && M >= 1024)) {
         hipLaunchKernelGGL(topk_merge_rows_kernel<T>, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, partial,
                            (int)M, n_keys, K, V, out_ids, out_vals, gold, gold_logit, status,
                            p.big ? (const T *)h : nullptr, p.big ? (const T *)w : nullptr, H, ue, p.n_lists, um.lse,

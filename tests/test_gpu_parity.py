@@ -111,6 +111,8 @@ TOPK_CASES = [
     # bf16, N <= 8, H a multiple of 512: weights streamed through LDS; several
     # ring turns per tile and several tiles per wave, ragged per-wave ranges
     (8, 4096, 30011, 16, "bf16"), (1, 4096, 5003, 64, "bf16"), (3, 2048, 70001, 5, "bf16"),
+    # many rows whose 32 lists of 32 keys (1024) one wave merges in two chunks
+    (1800, 256, 9000, 20, "bf16"),
 ]
 
 
