@@ -45,7 +45,8 @@ __device__ __forceinline__ void split_bf16x8(const float (&v)[8], uint4 &hi, uin
 // candidate cid (row l % 16) and predecessor pid (column l % 16); a negative
 // id is a zero row/column.  r is a multiple of 8; grow is the context row (r
 // floats, global memory or LDS).  The rank index is visited 32 at a time (8
-// per lane group).  pair_tiles forms NJ such tiles over the same
+// per lane group); B rows sit bstride elements apart (r in global memory,
+// padded in LDS).  pair_tiles forms NJ such tiles over the same
 // predecessors (tile j from candidates cid[j]): the predecessor rows and the
 // context are loaded and multiplied once for all of them, and a batch of
 // steps (as many as keep its operands within about 128 registers) has all of
@@ -60,7 +61,7 @@ __device__ __forceinline__ void split_bf16x8(const float (&v)[8], uint4 &hi, uin
 // P[j][i] of lane l is tile j's P[4 * (l / 16) + i][l % 16].
 template <typename T, int NJ>
 __device__ __forceinline__ void pair_tiles(const T *__restrict__ A, const T *__restrict__ B, const float *grow,
-                                           int pid, const int (&cid)[NJ], int r, f32x4 (&P)[NJ]) {
+                                           int pid, const int (&cid)[NJ], int r, int bstride, f32x4 (&P)[NJ]) {
     constexpr int W = kWords8<T>;
     constexpr int PER = 4 * W * (1 + NJ) + 8;  // registers of one step's operands
     constexpr int S = 128 / PER >= 8 ? 8 : 128 / PER >= 4 ? 4 : 128 / PER >= 2 ? 2 : 1;
@@ -68,7 +69,7 @@ __device__ __forceinline__ void pair_tiles(const T *__restrict__ A, const T *__r
     const T *arow = pid >= 0 ? A + (size_t)pid * r : nullptr;
     const T *brow[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) brow[j] = cid[j] >= 0 ? B + (size_t)cid[j] * r : nullptr;
+    for (int j = 0; j < NJ; ++j) brow[j] = cid[j] >= 0 ? B + (size_t)cid[j] * bstride : nullptr;
     f32x4 acc[NJ][4];
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -128,7 +129,7 @@ __device__ __forceinline__ f32x4 pair_tile(const T *__restrict__ A, const T *__r
                                            int pid, int cid, int r) {
     const int c[1] = {cid};
     f32x4 P[1];
-    pair_tiles<T, 1>(A, B, grow, pid, c, r, P);
+    pair_tiles<T, 1>(A, B, grow, pid, c, r, r, P);
     return P[0];
 }
 
@@ -241,7 +242,7 @@ __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *_
             if (!cok[jt]) cid[jt] = -1;
         }
         f32x4 P[NJ];
-        pair_tiles<T, NJ>(A, B, g + n * r, pid, cid, r, P);
+        pair_tiles<T, NJ>(A, B, g + n * r, pid, cid, r, r, P);
         // noise of this lane's slots
         float gn[NJ][4];
         if constexpr (SAMPLE) {
@@ -339,6 +340,152 @@ __global__ __launch_bounds__(512) void selector_walk_kernel(
     extern __shared__ __align__(16) uint8_t wsm[];
     walk_block<T, NJ, SAMPLE>(blockIdx.x, wsm, g, A, B, cand_ids, cand_vals, anchors, bs, V, r, K, path,
                               path_score, status, temperature, k0, k1);
+}
+
+// ------------------------------------------------------------------ walk, one pick at a time
+// With many blocks the pair walk is bound by its gathers: at every position
+// it fetches the A rows of all K slots of C_{t-1}, though the path follows
+// only one of them.  This greedy variant (bf16 codebooks) scores one step at
+// a time.  For position t the workgroup copies the K successor rows of B, the
+// context row and the single A row of the previous pick straight into LDS
+// (global_load_lds, 1 KB per wave instruction): one round trip to memory per
+// step and about half the pair walk's bytes.  Wave w then scores successor
+// tile w with the predecessor in column 0 of pair_tiles, as teacher forcing
+// does, so every score equals the pair walk's bit for bit and so does the path.
+// LDS layout (ChaseLayout): candidate ids [bs][K] int; B rows, each r + 8
+// elements apart when r is a multiple of 512 (the 16 rows a wave reads at one
+// rank offset then fall in 16 different bank groups), else packed r apart in
+// whole 1 KB copies (lanes past the last row fetch row 0's first chunk into
+// the slack); the context row [r] float and the A row [r] bf16, each in whole
+// 1 KB copies; the waves' best keys.
+typedef __attribute__((address_space(3))) void chase_lds_t;
+constexpr int kChaseThreads = 256;
+constexpr int kChaseMinBlocks = 128;
+constexpr size_t kChaseMaxLds = 96 * 1024;
+struct ChaseLayout {
+    int padded, bstride, b_copies, g_copies, a_copies;
+    size_t b_off, g_off, a_off, key_off, total;
+};
+static ChaseLayout chase_layout(int bs, int K, int r) {
+    ChaseLayout L;
+    L.padded = r % 512 == 0;
+    L.bstride = L.padded ? r + 8 : r;
+    const size_t rowbytes = (size_t)r * 2;
+    L.b_copies = L.padded ? K * (r / 512) : (int)(((size_t)K * rowbytes + 1023) / 1024);
+    L.g_copies = (r + 255) / 256;
+    L.a_copies = (r + 511) / 512;
+    L.b_off = ((size_t)bs * K * 4 + 255) / 256 * 256;
+    L.g_off = L.b_off + (L.padded ? (size_t)K * (rowbytes + 16) : (size_t)L.b_copies * 1024);
+    L.g_off = (L.g_off + 255) / 256 * 256;
+    L.a_off = L.g_off + (size_t)L.g_copies * 1024;
+    L.key_off = L.a_off + (size_t)L.a_copies * 1024;
+    L.total = L.key_off + 4 * 8;
+    return L;
+}
+
+__global__ __launch_bounds__(kChaseThreads) void selector_chase_kernel(
+    const float *__restrict__ g, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const int32_t *__restrict__ cand_ids, const float *__restrict__ cand_vals, const int32_t *__restrict__ anchors,
+    int bs, int V, int r, int K, ChaseLayout L, int32_t *__restrict__ path, float *__restrict__ path_score,
+    uint32_t *__restrict__ status) {
+    extern __shared__ __align__(16) uint8_t csm[];
+    int32_t *ids = reinterpret_cast<int32_t *>(csm);
+    uint8_t *bsm = csm + L.b_off, *gsm = csm + L.g_off, *asm_ = csm + L.a_off;
+    uint64_t *keys = reinterpret_cast<uint64_t *>(csm + L.key_off);
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int q = lane >> 4, c = lane & 15;
+    const int blk = blockIdx.x, n_it = (K + 15) >> 4, rc = r >> 3;
+    const size_t row0 = (size_t)blk * bs;
+    const int anchor = anchors[blk];
+    const bool anchor_ok = anchor >= 0 && anchor < V;
+    if (!anchor_ok && tid == 0) flag_status(status, kStatusIdRange);
+    for (int i = tid; i < bs * K; i += kChaseThreads) {
+        const int id = cand_ids[row0 * K + i];
+        const bool ok = id >= 0 && id < V;
+        if (i >= K && !ok) flag_status(status, kStatusIdRange);  // positions 1.. are scored
+        ids[i] = ok ? id : -1;
+    }
+    if (tid == 0) {
+        path[row0] = anchor_ok ? anchor : -1;
+        if (path_score) path_score[row0] = 0.f;
+    }
+    __syncthreads();
+    int pid = anchor_ok ? anchor : -1;  // the previous pick (workgroup-uniform); -1 once the path has ended
+    for (int t = 1; t < bs; ++t) {
+        const size_t n = row0 + t;
+        if (pid < 0) {
+            if (tid == 0) {
+                path[n] = -1;
+                if (path_score) path_score[n] = __builtin_nanf("");
+            }
+            continue;
+        }
+        const int32_t *idt = ids + t * K;
+        for (int k = wave; k < L.b_copies; k += kChaseThreads / 64) {
+            int j, ch;
+            uint8_t *dst;
+            if (L.padded) {
+                const int bpr = r / 512;
+                j = k / bpr;
+                ch = (k - j * bpr) * 64 + lane;
+                dst = bsm + (size_t)j * (r * 2 + 16) + (size_t)(k - j * bpr) * 1024;
+            } else {
+                const int f = k * 64 + lane;
+                j = f / rc;
+                ch = f - j * rc;
+                dst = bsm + (size_t)k * 1024;
+            }
+            int id = j < K ? idt[j] : -1;
+            if (id < 0) id = 0, ch = 0;  // slack or an invalid slot: an in-bounds chunk that is never read
+            __builtin_amdgcn_global_load_lds(B + (size_t)id * r + ch * 8, (chase_lds_t *)dst, 16, 0, 0);
+        }
+        for (int k = wave; k < L.g_copies; k += kChaseThreads / 64) {
+            const int f = k * 64 + lane, ch = f < (r >> 2) ? f : 0;
+            __builtin_amdgcn_global_load_lds(g + n * r + ch * 4, (chase_lds_t *)(gsm + k * 1024), 16, 0, 0);
+        }
+        for (int k = wave; k < L.a_copies; k += kChaseThreads / 64) {
+            const int f = k * 64 + lane, ch = f < rc ? f : 0;
+            __builtin_amdgcn_global_load_lds(A + (size_t)pid * r + ch * 8, (chase_lds_t *)(asm_ + k * 1024), 16, 0,
+                                             0);
+        }
+        float uv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int jj = wave * 16 + 4 * q + i;
+            uv[i] = (wave < n_it && jj < K) ? cand_vals[n * K + jj] : 0.f;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (wave < n_it) {
+            const int j = wave * 16 + c;
+            const int cid[1] = {(j < K && idt[j] >= 0) ? j : -1};
+            f32x4 P[1];
+            pair_tiles<uint16_t, 1>(reinterpret_cast<const uint16_t *>(asm_), reinterpret_cast<const uint16_t *>(bsm),
+                                    reinterpret_cast<const float *>(gsm), c == 0 ? 0 : -1, cid, r, L.bstride, P);
+            uint64_t local = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int jj = wave * 16 + 4 * q + i;
+                const bool ok = c == 0 && jj < K && idt[jj] >= 0;
+                const float s = jj < K ? uv[i] + P[0][i] : 0.f;
+                const uint64_t key = ok ? make_key(s, (uint32_t)jj) : 0ull;
+                local = key > local ? key : local;
+            }
+            uint64_t o = shfl_xor_u64(local, 16);
+            local = o > local ? o : local;
+            o = shfl_xor_u64(local, 32);
+            local = o > local ? o : local;
+            if (lane == 0) keys[wave] = local;
+        }
+        __syncthreads();
+        uint64_t key = 0;
+        for (int w = 0; w < n_it; ++w) key = keys[w] > key ? keys[w] : key;
+        pid = key ? idt[key_id(key)] : -1;
+        if (tid == 0) {
+            path[n] = pid;
+            if (path_score) path_score[n] = key ? key_val(key) : __builtin_nanf("");
+        }
+    }
 }
 
 // ------------------------------------------------------------------ teacher forcing
@@ -454,6 +601,16 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
         return sample ? pick(Ap, Bp, std::true_type{}) : pick(Ap, Bp, std::false_type{});
     };
     if (dtype == 0) return mode((const float *)A, (const float *)B);
+    const ChaseLayout L = chase_layout(bs, K, r);
+    if (!sample && n_blocks >= kChaseMinBlocks && bs >= 2 && L.total <= kChaseMaxLds) {
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(selector_chase_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(selector_chase_kernel, dim3(n_blocks), dim3(kChaseThreads), L.total, stream, g,
+                           (const uint16_t *)A, (const uint16_t *)B, cand_ids, cand_vals, anchors, bs, V, r, K, L,
+                           path, path_score, status);
+        return hipGetLastError();
+    }
     return mode((const uint16_t *)A, (const uint16_t *)B);
 }
 

@@ -276,6 +276,10 @@ WALK_CASES = [
     (1, 8, 256, 1000, 32, 16, "f32"), (3, 8, 256, 1000, 256, 16, "bf16"), (16, 8, 256, 4096, 32, 16, "f32"),
     (5, 16, 256, 3000, 40, 20, "bf16"), (4, 16, 512, 5000, 512, 64, "bf16"), (7, 2, 256, 500, 64, 1, "bf16"),
     (2, 3, 256, 800, 256, 33, "bf16"), (64, 8, 256, 2000, 256, 16, "bf16"),
+    # 128 blocks or more (bf16): the walk that follows one pick at a time, with
+    # padded LDS rows (r a multiple of 512) and packed ones, ragged K
+    (128, 8, 256, 3000, 512, 20, "bf16"), (130, 4, 256, 2000, 40, 64, "bf16"), (200, 2, 256, 500, 256, 1, "bf16"),
+    (129, 16, 256, 4000, 1024, 33, "bf16"),
 ]
 
 
@@ -454,6 +458,37 @@ def test_out_of_range_ids_are_flagged_not_read(D):
                                         to_dev(vals), to_dev(pred), workspace=ws3)
     assert D.read_device_status(ws3) == 8 and int(best[5]) == -1 and int(best[4]) >= 0
 
+
+
+@pytest.mark.parametrize("nb,bs,r,K", [(160, 8, 512, 16), (140, 6, 96, 24)])
+def test_chased_walk_equals_pair_walk(D, nb, bs, r, K):
+    """With 128 blocks or more (bf16) the walk follows one pick at a time;
+    below that every adjacent pair is scored.  The first 127 blocks, walked
+    alone, take the pair walk: both must give the same paths and bit-equal
+    scores, also with candidate and anchor ids out of range."""
+    H, V = 256, 2500
+    log(f"chase vs pair nb={nb} bs={bs} r={r} K={K}")
+    w = wl(n_blocks=nb, block_size=bs, hidden=H, vocab=V, rank=r, top_k=K, dtype="bf16")
+    inp = make_inputs(w, seed=21, fields=["h", "w_h", "cb_pred", "cb_succ", "anchors"])
+    rng = np.random.default_rng(nb + K)
+    N = nb * bs
+    ids, vals = rand_cands(rng, N, V, K)
+    ids[bs + 2, 3] = V + 1  # invalid candidates in block 1 and block 130
+    ids[130 * bs + 1, 0] = -4
+    anchors = inp["anchors"].copy()
+    anchors[5] = -2
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    outs = []
+    for m in (nb, 127):
+        ws = D.make_workspace(D.OP_SELECTOR_WALK, m * bs, H, V, r, K, "cuda")
+        path, ps = D.selector_walk(dev["h"][:m * bs], dev["w_h"], dev["cb_pred"], dev["cb_succ"],
+                                   to_dev(ids[:m * bs]), to_dev(vals[:m * bs]), to_dev(anchors[:m]), bs, workspace=ws)
+        assert D.read_device_status(ws) == 8
+        outs.append((to_np(path), to_np(ps)))
+    (p_all, s_all), (p_pair, s_pair) = outs
+    assert np.all(p_all[5] == -1) and np.all(np.isnan(s_all[5, 1:]))
+    assert np.array_equal(p_all[:127], p_pair)
+    assert np.array_equal(s_all[:127].view(np.uint32), s_pair.view(np.uint32))
 
 # -------------------------------------------------------- selector CE backward
 
