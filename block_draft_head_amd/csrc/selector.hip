@@ -5,9 +5,11 @@
 // candidates on the rows and predecessors on the columns, the rank index
 // visited in the same order.  The greedy walk scores every adjacent pair of a
 // block at once and reduces each predecessor's row to its best successor;
-// only the final pointer chase is sequential.  Teacher forcing places its one
-// predecessor in column 0 of the same routine, so replaying a walk's own
-// predecessors reproduces the walk's scores bit for bit.
+// only the final pointer chase is sequential; with many blocks (bf16) the
+// walk instead follows the path, one position at a time against the previous
+// pick only, with that pick in column 0 (selector_chase_kernel).  Teacher
+// forcing places its one predecessor in column 0 of the same routine, so
+// replaying a walk's own predecessors reproduces the walk's scores bit for bit.
 #include <type_traits>
 
 #include "common.hpp"

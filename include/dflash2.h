@@ -186,8 +186,11 @@ dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, 
  *   S_t(a, b) = cand_vals[n, slot(b)] + sum_r cb_pred[a, r] * g[n, r] * cb_succ[b, r]
  * with n = blk*bs + t.  path[blk, 0] = anchor_ids[blk]; for t = 1..bs-1 the
  * candidate of row n with the highest S_t(path[blk, t-1], .) is taken (lowest
- * slot on an exact tie).  Every adjacent pair is scored in parallel; only the
- * final pointer chase is sequential.
+ * slot on an exact tie).  With float32 codebooks or fewer than 128 blocks,
+ * every adjacent pair is scored in parallel and only the final pointer chase
+ * is sequential; with bf16 codebooks and 128 blocks or more the walk follows
+ * the path, scoring each position against the previous pick only (about half
+ * the gathered bytes).  The scores, and so the path, are the same either way.
  *
  *   n_blocks, block_size (<= 64), hidden H, vocab V, rank r (multiple of 8, <= 4096),
  *   top_k K (<= 64)
