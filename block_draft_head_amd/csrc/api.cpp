@@ -13,6 +13,8 @@
 
 using namespace dflash2;
 
+static_assert(DFLASH2_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "header and library agree on the array size");
+
 namespace {
 
 size_t elem_size(int dtype) { return dtype == DFLASH2_F32 ? 4 : 2; }
@@ -206,6 +208,30 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
     return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
                                          cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
                                          out_path_score, workspace, (hipStream_t)stream, nullptr));
+}
+
+dflash2_status dflash2_selector_walk_noalloc(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,
+                                             int32_t vocab, int32_t rank, int32_t top_k, const void *h,
+                                             const void *w_h, const void *cb_pred, const void *cb_succ,
+                                             const int32_t *cand_ids, const float *cand_vals,
+                                             const int32_t *anchor_ids, int32_t *out_path, float *out_path_score,
+                                             void *stream) {
+    if (n_blocks < 1 || block_size < 1) return dtype_ok(dtype) ? DFLASH2_ERR_SHAPE : DFLASH2_ERR_DTYPE;
+    const int64_t N = (int64_t)n_blocks * block_size;
+    dflash2_status s = check_selector(dtype, N, hidden, vocab, rank, top_k);
+    if (s != DFLASH2_OK) return s;
+    if (block_size > DFLASH2_MAX_BLOCK_SIZE) return DFLASH2_ERR_UNSUPPORTED;
+    if (dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k) > kNoAllocScratchBytes)
+        return DFLASH2_ERR_UNSUPPORTED;
+    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path)
+        return DFLASH2_ERR_NULL;
+    const size_t np = (size_t)N * 4;
+    if (out_path_score && overlaps(out_path_score, np, out_path, np)) return DFLASH2_ERR_ALIAS;
+    void *scratch = nullptr;
+    if (noalloc_scratch(&scratch) != hipSuccess) return DFLASH2_ERR_LAUNCH;
+    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
+                                         cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
+                                         out_path_score, scratch, (hipStream_t)stream, nullptr));
 }
 
 dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,

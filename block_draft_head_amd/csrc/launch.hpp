@@ -91,6 +91,12 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
                                 const int32_t *cand_ids, const float *cand_vals,
                                 const int32_t *anchors, int32_t *path, float *path_score,
                                 void *workspace, hipStream_t stream, const SampleParams *sample);
+// Walk without a caller workspace: the status word and the context rows live
+// in a file-scope device array of this many bytes (one copy per GPU).
+constexpr size_t kNoAllocScratchBytes = ((size_t)8 << 20) + kStatusBytes;
+// Device address of that array on the current device (looked up once per device).
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
                               const void *w_h, const void *A, const void *B, const int32_t *cand_ids,
                               const float *cand_vals, const int32_t *pred_ids,

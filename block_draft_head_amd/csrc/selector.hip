@@ -10,6 +10,7 @@
 // pick only, with that pick in column 0 (selector_chase_kernel).  Teacher
 // forcing places its one predecessor in column 0 of the same routine, so
 // replaying a walk's own predecessors reproduces the walk's scores bit for bit.
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -614,6 +615,33 @@ hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, i
         return hipGetLastError();
     }
     return mode((const uint16_t *)A, (const uint16_t *)B);
+}
+
+// ------------------------------------------------------------------ walk without a caller workspace
+// The walk's workspace (status word, then the context rows g [N, r] float32)
+// in a file-scope device array, for callers that cannot allocate.  Each GPU
+// holds its own copy at its own address; host code never uses the array's
+// name as a device address, only the address looked up here once per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex lock;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(lock);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,

@@ -24,9 +24,10 @@ STATUS = {
 OP_UNARY_TOPK, OP_SELECTOR_WALK, OP_SELECTOR_TF, OP_SELECTOR_CE_BACKWARD = 0, 1, 2, 3
 F32, BF16 = 0, 1
 MAX_TOP_K, MAX_TAPS, MAX_BLOCK_SIZE, MAX_RANK = 64, 16, 64, 4096
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024 + 256
 
 EXPORTS = ["dflash2_conv_prepare", "dflash2_conv_finish", "dflash2_unary_topk", "dflash2_unary_topk_ex",
-           "dflash2_selector_walk", "dflash2_selector_sample", "dflash2_selector_score_tf",
+           "dflash2_selector_walk", "dflash2_selector_walk_noalloc", "dflash2_selector_sample", "dflash2_selector_score_tf",
            "dflash2_selector_ce_backward", "dflash2_workspace_bytes",
            "dflash2_status_str", "dflash2_read_device_status", "dflash2_version"]
 
@@ -49,6 +50,7 @@ def _load() -> ctypes.CDLL:
         "dflash2_unary_topk_ex": [ctypes.c_int, I64, I32, I32, I32, P, P, P, ctypes.c_float, ctypes.c_float,
                                   P, P, P, P, P, P, P, SZ, P],
         "dflash2_selector_walk": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "dflash2_selector_walk_noalloc": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P],
         "dflash2_selector_sample": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P,
                                     ctypes.c_float, ctypes.c_uint64, P, P, P, SZ, P],
         "dflash2_selector_score_tf": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -235,6 +237,32 @@ def selector_walk(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, blo
                                     _ptr(ps), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "dflash2_selector_walk")
     return path, ps
+
+
+def selector_walk_noalloc(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, block_size: int,
+                          path: Optional[torch.Tensor] = None, path_score: Optional[torch.Tensor] = None,
+                          want_scores: bool = True):
+    """selector_walk without a workspace (the library's own device array; see
+    dflash2_selector_walk_noalloc).  Outputs may be passed in, so that a
+    caller that cannot allocate allocates nothing here either.
+    -> (path [n_blocks, bs] int32, path_score [n_blocks, bs] float32 or None)."""
+    _same_dtype(h, w_h, cb_pred, cb_succ)
+    _ids(cand_ids, "cand_ids")
+    _ids(anchor_ids, "anchor_ids")
+    N, H = h.shape
+    V, r = cb_pred.shape
+    K = cand_ids.shape[1]
+    nb = anchor_ids.shape[0]
+    dev = h.device
+    if path is None:
+        path = torch.empty((nb, block_size), dtype=torch.int32, device=dev)
+    if path_score is None and want_scores:
+        path_score = torch.empty((nb, block_size), dtype=torch.float32, device=dev)
+    st = _lib.dflash2_selector_walk_noalloc(_dtype_code(h), nb, block_size, H, V, r, K, _ptr(h), _ptr(w_h),
+                                            _ptr(cb_pred), _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals),
+                                            _ptr(anchor_ids), _ptr(path), _ptr(path_score), _stream(dev))
+    _check(st, "dflash2_selector_walk_noalloc")
+    return path, path_score
 
 
 def selector_sample(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, block_size: int,

@@ -20,8 +20,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every pointer is a DEVICE pointer owned by the caller, except where noted.
- *   The library never allocates, never frees and keeps no state between calls.
- *   Calls are re-entrant; concurrent calls must use distinct workspaces.
+ *   The library never allocates, never frees and keeps no state between calls
+ *   (dflash2_selector_walk_noalloc alone works in a library-owned device
+ *   array, see there).  Calls are re-entrant; concurrent calls must use
+ *   distinct workspaces.
  * - All work is enqueued on `stream` (a hipStream_t; NULL is the default
  *   stream).  No entry point synchronises, except dflash2_read_device_status.
  * - Matrices are row-major.  Weights follow the [out, in] layout of a linear
@@ -207,6 +209,28 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
                                      const float *cand_vals, const int32_t *anchor_ids,
                                      int32_t *out_path, float *out_path_score, void *workspace,
                                      size_t workspace_bytes, void *stream);
+
+/*
+ * dflash2_selector_walk for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that forbid allocation): the same
+ * inputs, outputs and kernels, without a workspace argument.  The status word
+ * and the context rows live in a library-owned device array of
+ * DFLASH2_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; its
+ * address on a device is looked up on the first call there.  Nothing is
+ * allocated.  Sizes whose walk workspace (dflash2_workspace_bytes with
+ * DFLASH2_OP_SELECTOR_WALK) exceeds that array return DFLASH2_ERR_UNSUPPORTED.
+ * Every call on one GPU shares the array and overwrites what the last call
+ * left there: calls that overlap on one GPU (other streams, other threads)
+ * race and must not be issued.  The status word cannot be read back;
+ * out-of-range ids show in the outputs (path -1, score NaN).
+ */
+#define DFLASH2_NOALLOC_SCRATCH_BYTES (8u * 1024u * 1024u + 256u)
+dflash2_status dflash2_selector_walk_noalloc(int dtype, int32_t n_blocks, int32_t block_size,
+                                             int32_t hidden, int32_t vocab, int32_t rank, int32_t top_k,
+                                             const void *h, const void *w_h, const void *cb_pred,
+                                             const void *cb_succ, const int32_t *cand_ids,
+                                             const float *cand_vals, const int32_t *anchor_ids,
+                                             int32_t *out_path, float *out_path_score, void *stream);
 
 /*
  * Sampled selector walk per anchor block ([Explainer] "Problem 1", the

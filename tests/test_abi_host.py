@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert sorted(D.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -147,6 +147,25 @@ def test_selector_walk_rules():
     assert walk(path=None) == NULL and walk(anchors=None) == NULL and walk(ws=None) == NULL
     assert walk(wsb=100) == WS
     assert walk(ps=fake(7)) == ALIAS
+
+
+def walk_na(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, path=fake(10), ps=None, anchors=fake(6)):
+    return L.dflash2_selector_walk_noalloc(dtype, nb, bs, h, v, r, k, fake(0), fake(1), fake(2), fake(3), fake(4),
+                                           fake(5), anchors, path, ps, None)
+
+
+@no_gpu
+def test_selector_walk_noalloc_rules():
+    # the walk's rules, with the library's array in place of a workspace
+    assert walk_na(k=0) == SHAPE and walk_na(nb=0) == SHAPE and walk_na(r=0) == SHAPE
+    assert walk_na(k=65) == UNSUP and walk_na(bs=65) == UNSUP and walk_na(r=12) == UNSUP
+    assert walk_na(dtype=5) == DTYPE
+    # the status word and the float32 context rows must fit the array
+    cap = D.NOALLOC_SCRATCH_BYTES
+    assert D.workspace_bytes(D.OP_SELECTOR_WALK, 256 * 16, 5120, 248320, 512, 64) <= cap  # the wide walk fits
+    assert walk_na(nb=257, bs=16, h=5120, v=248320, r=512, k=64) == UNSUP                 # one block more does not
+    assert walk_na(path=None) == NULL and walk_na(anchors=None) == NULL
+    assert walk_na(ps=fake(10)) == ALIAS
 
 
 def sample(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, temp=1.0, path=fake(10), ps=None, anchors=fake(6),
