@@ -95,6 +95,9 @@ size_t dflash2_workspace_bytes(int op, int64_t n_rows, int32_t hidden, int32_t v
         case DFLASH2_OP_SELECTOR_CE_BACKWARD:
             if (rank < 1 || vocab < 1 || top_k < 1) return 0;
             return ce_bwd_layout(n_rows, vocab, rank, top_k).total;
+        case DFLASH2_OP_DECODE_HEAD:
+            if (hidden < 1 || vocab < 1 || rank < 0 || top_k < 1 || top_k > DFLASH2_MAX_TOP_K) return 0;
+            return decode_layout(n_rows, hidden, vocab, rank, top_k).total;
         default: return 0;
     }
 }
@@ -260,6 +263,45 @@ dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t bloc
     return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
                                          cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
                                          out_path_score, workspace, (hipStream_t)stream, &sp));
+}
+
+dflash2_status dflash2_decode_head(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden, int32_t vocab,
+                                   int32_t rank, int32_t top_k, const void *h, const void *w_lm, const void *w_h,
+                                   const void *cb_pred, const void *cb_succ, const int32_t *anchor_ids,
+                                   int32_t *out_ids, float *out_vals, int32_t *out_path, float *out_path_score,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    if (!dtype_ok(dtype)) return DFLASH2_ERR_DTYPE;
+    if (n_blocks < 1 || block_size < 1 || hidden < 1 || vocab < 1) return DFLASH2_ERR_SHAPE;
+    if (top_k < 1 || top_k > vocab) return DFLASH2_ERR_SHAPE;
+    const bool sel = w_h || cb_pred || cb_succ || anchor_ids || out_path || out_path_score;
+    if (sel) {
+        if (rank < 1) return DFLASH2_ERR_SHAPE;
+        if (rank % 8 != 0 || rank > DFLASH2_MAX_RANK) return DFLASH2_ERR_UNSUPPORTED;
+    }
+    const int64_t N = (int64_t)n_blocks * block_size;
+    const int r = sel ? rank : 0;
+    if (dtype != DFLASH2_BF16 || block_size > DFLASH2_MAX_BLOCK_SIZE || !hidden_supported(hidden) ||
+        !decode_head_supported(N, hidden, vocab, r, top_k))
+        return DFLASH2_ERR_UNSUPPORTED;
+    if (!h || !w_lm || !out_ids || !out_vals || !workspace) return DFLASH2_ERR_NULL;
+    if (sel && (!w_h || !cb_pred || !cb_succ || !anchor_ids || !out_path)) return DFLASH2_ERR_NULL;
+    if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_DECODE_HEAD, N, hidden, vocab, r, top_k))
+        return DFLASH2_ERR_WORKSPACE;
+    const size_t nk = (size_t)N * top_k * 4, np = (size_t)N * 4;
+    struct Span { const void *p; size_t b; };
+    const Span outs[] = {{out_ids, nk}, {out_vals, nk}, {out_path, out_path ? np : 0},
+                         {out_path_score, out_path_score ? np : 0}, {workspace, workspace_bytes}};
+    const Span ins[] = {{h, (size_t)N * hidden * 2}, {anchor_ids, anchor_ids ? (size_t)n_blocks * 4 : 0}};
+    constexpr size_t no = sizeof(outs) / sizeof(outs[0]);
+    for (size_t i = 0; i < no; ++i) {
+        for (size_t j = i + 1; j < no; ++j)
+            if (overlaps(outs[i].p, outs[i].b, outs[j].p, outs[j].b)) return DFLASH2_ERR_ALIAS;
+        for (const Span &in : ins)
+            if (overlaps(outs[i].p, outs[i].b, in.p, in.b)) return DFLASH2_ERR_ALIAS;
+    }
+    return launched(launch_decode_head(N, hidden, vocab, top_k, h, w_lm, r, sel ? w_h : nullptr, cb_pred, cb_succ,
+                                       anchor_ids, block_size, out_ids, out_vals, out_path, out_path_score,
+                                       workspace, (hipStream_t)stream));
 }
 
 dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,

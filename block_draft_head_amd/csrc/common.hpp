@@ -180,6 +180,18 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// A wave-uniform pointer read from the first active lane, so that it can sit
+// in scalar registers.  readfirstlane returns a signed int: each half is
+// widened as unsigned, or a low word with bit 31 set would sign-extend into
+// the high word.
+template <typename P>
+__device__ __forceinline__ P *readfirstlane_ptr(P *p) {
+    const uint64_t b = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    return reinterpret_cast<P *>(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));

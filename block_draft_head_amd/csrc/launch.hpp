@@ -84,6 +84,19 @@ hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const vo
                              const int32_t *gold, int32_t *out_ids, float *out_vals,
                              float *gold_logit, void *workspace, hipStream_t stream,
                              const UnaryMetrics *metrics = nullptr);
+// Decode head (bf16, at most 8 rows): the LM-head kernel with the context
+// projection's rows streamed after the vocabulary's, then one workgroup that
+// merges the candidate lists and walks every block.  Workspace: status word,
+// the workgroups' partial lists, the context rows g [M, r].
+struct DecodeLayout {
+    int grid;
+    size_t partial, g, total;
+};
+DecodeLayout decode_layout(int64_t M, int H, int V, int r, int K);  // r = 0: no context rows
+bool decode_head_supported(int64_t M, int H, int V, int r, int K);
+hipError_t launch_decode_head(int64_t M, int H, int V, int K, const void *h, const void *w, int r, const void *w_h,
+                              const void *A, const void *B, const int32_t *anchors, int bs, int32_t *out_ids,
+                              float *out_vals, int32_t *path, float *path_score, void *workspace, hipStream_t stream);
 hipError_t launch_context_proj(int dtype, int64_t N, int H, int r, const void *h, const void *w_h,
                                float *g, uint32_t *status, hipStream_t stream);
 hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, int r, int K,

@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "gemm.hpp"
 #include "launch.hpp"
+#include "selector.hpp"
 
 namespace dflash2 {
 
@@ -368,11 +369,20 @@ __device__ void load_afrag_shares(uint4 *afrag, const uint16_t *__restrict__ A, 
     }
 }
 
-template <int KS, bool LSE>
+// The decode head: the context projection's rows stream after the
+// vocabulary's through the same kernel (their tiles write g instead of
+// candidates), so the selector adds no pass over h of its own.
+struct DecodeFuse {
+    const uint16_t *wh;  // [r, H], or null: no context projection
+    int r;
+    float *g;            // [M, r] float32 context rows
+};
+
+template <int KS, bool LSE, bool FUSED>
 __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K,
     const int32_t *__restrict__ gold, float *__restrict__ gold_logit, uint64_t *__restrict__ partial,
-    uint32_t *__restrict__ status, UnaryEpi ue) {
+    uint32_t *__restrict__ status, UnaryEpi ue, DecodeFuse fu) {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int NW = kDmaWaves, NB = kDmaRing, CAP = kDmaCandCap, AH = kDmaAhead, LD = kDmaLead;
     constexpr int G = NW / KS;   // wave groups
@@ -395,9 +405,17 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     load_afrag_shares(afrag, h, M, H, Q);
     __syncthreads();
 
-    const int r0 = (int)((long long)blockIdx.x * V / gridDim.x);
-    const int r1 = (int)((long long)(blockIdx.x + 1) * V / gridDim.x);
-    const int ntile = (r1 - r0 + 15) / 16;
+    // workgroup b owns 16-row tiles [t0, t1) of the vocabulary's tiles, then
+    // (fused decode head) the context projection's tiles
+    // (the fused head's fields as scalars: read through the struct, which the
+    // lambdas below would capture by address, they would count as divergent)
+    const uint16_t *const wh = FUSED ? fu.wh : nullptr;
+    const int rk = FUSED && wh ? fu.r : 0;
+    float *const gout = FUSED ? fu.g : nullptr;
+    const int tiles_v = (V + 15) / 16;
+    const int n_all = tiles_v + (rk + 15) / 16;
+    const int t0 = (int)((long long)blockIdx.x * n_all / gridDim.x);
+    const int ntile = (int)((long long)(blockIdx.x + 1) * n_all / gridDim.x) - t0;
     // group gi takes tiles gi, gi + G, ...; with a K split every wave runs the
     // same number of iterations (they meet at barriers), a group with one
     // tile fewer repeating its last tile with no row valid
@@ -438,15 +456,21 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     const uint32_t ring_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)ring;
     const int crow = lane >> 3, cpos = lane & 7;
     // byte offsets of this lane's chunk of its two copy rows in the tile of
-    // iteration `it`, first block of the wave's K share
-    auto tile_rows = [&](int it, uint32_t (&ro)[2]) {
-        const int ti = min(it * G + gi, ntile - 1);
+    // iteration `it`, first block of the wave's K share; returns the matrix
+    // the tile's rows belong to (w_lm, or w_h past the vocabulary's tiles)
+    auto tile_rows = [&](int it, uint32_t (&ro)[2]) -> const uint16_t * {
+        const int gt = t0 + min(it * G + gi, ntile - 1);
+        const bool ht = FUSED && gt >= tiles_v;
+        const int row0 = ht ? (gt - tiles_v) * 16 : gt * 16, lim = ht ? rk : V;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int row = 8 * j + crow, vrow = r0 + ti * 16 + row;
+            const int row = 8 * j + crow, vrow = row0 + row;
             ro[j] = (uint32_t)((cpos ^ (row & 7)) * 16 + kp * Q * 128) +
-                    (vrow < r1 ? (uint32_t)vrow * (uint32_t)H * 2u : 0u);
+                    (vrow < lim ? (uint32_t)vrow * (uint32_t)H * 2u : 0u);
         }
+        // (wave-uniform; read from the first lane so that the copies can take
+        // it as their scalar base whatever the compiler proves about it)
+        return readfirstlane_ptr(ht ? wh : w);
     };
     // block `src` + I of the rows `ro` into ring slot I.  The instruction's
     // immediate offset moves the LDS destination as well as the global
@@ -455,8 +479,12 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     // inline assembly).  `held` are the B fragments last
     // read from the slot: naming them as inputs makes the compiler wait for
     // those reads before the copy overwrites it.
-    auto copy_block = [&](const uint32_t (&ro)[2], const uint16_t *src, auto slotc, const uint4 (&held)[2]) {
+    auto copy_block = [&](const uint32_t (&ro)[2], const uint16_t *src_in, auto slotc, const uint4 (&held)[2]) {
         constexpr int I = decltype(slotc)::value;
+        // with two matrices in the stream the base is chosen per tile; it is
+        // wave-uniform, and read from the first lane again here so that the
+        // copy can take it as its scalar base whatever the compiler proves
+        const uint16_t *src = FUSED ? readfirstlane_ptr(src_in) : src_in;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t dst = ring_lds + (uint32_t)(I * (2048 - 128) + j * 1024);
@@ -488,11 +516,11 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
         // block g + I + LD into its slot, whose previous block has been
         // multiplied by then.
         uint32_t cur[2], nxt[2];
-        tile_rows(0, cur);
-        tile_rows(nit > 1 ? 1 : 0, nxt);
+        const uint16_t *cbase = tile_rows(0, cur);
+        const uint16_t *nbase = tile_rows(nit > 1 ? 1 : 0, nxt);
         uint4 fb[4][2], fa[4][2];
         const uint4 none[2] = {};
-        static_for<LD>([&](auto ic) { copy_block(cur, w, ic, none); });
+        static_for<LD>([&](auto ic) { copy_block(cur, cbase, ic, none); });
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (LD - AH)) : "memory");  // blocks 0 .. AH-1 have landed
         static_for<AH>([&](auto ic) {
             constexpr int I = decltype(ic)::value;
@@ -519,7 +547,7 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
                 mma16<uint16_t>(acc, fa[I % 4][1], fb[I % 4][1]);
                 if constexpr (MODE != 2 || !wrap) {
                     constexpr bool next_tile = MODE == 1 && wrap;
-                    const uint16_t *src = w + (next_tile ? 0 : (size_t)(g + (wrap ? NB : 0)) * 64);
+                    const uint16_t *src = next_tile ? nbase : cbase + (size_t)(g + (wrap ? NB : 0)) * 64;
                     // with LD == NB the slot is the one just multiplied from
                     copy_block(next_tile ? nxt : cur, src, std::integral_constant<int, S>{},
                                LD == NB ? fb[I % 4] : none);
@@ -548,8 +576,26 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
                 for (int p = 1; p < KS; ++p) acc += set[(gi * KS + p) * 64 + lane];
             }
             const int ti = it * G + gi;
-            const int v = r0 + ti * 16 + n;
-            const bool vok = ti < ntile && v < r1;
+            const int gt = t0 + ti;
+            if (FUSED && gt >= tiles_v) {
+                // a tile of the context projection: g[row, rho] (every tile
+                // row that is a real row of w_h)
+                const int rho = (gt - tiles_v) * 16 + n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (e % KS != kp) continue;
+                    const int row = 4 * q + e;
+                    if (ti < ntile && rho < rk && row < M) gout[(size_t)row * rk + rho] = acc[e];
+                }
+                if (last) break;
+                cur[0] = nxt[0];
+                cur[1] = nxt[1];
+                cbase = nbase;
+                nbase = tile_rows(it + 2 < nit ? it + 2 : it + 1, nxt);
+                continue;
+            }
+            const int v = gt * 16 + n;
+            const bool vok = ti < ntile && v < V;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if (e % KS != kp) continue;
@@ -589,7 +635,8 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
             if (last) break;
             cur[0] = nxt[0];
             cur[1] = nxt[1];
-            tile_rows(it + 2 < nit ? it + 2 : it + 1, nxt);
+            cbase = nbase;
+            nbase = tile_rows(it + 2 < nit ? it + 2 : it + 1, nxt);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -1387,6 +1434,146 @@ __global__ __launch_bounds__(256) void topk_merge_rows_kernel(const uint64_t *__
     }
 }
 
+// ---------------------------------------------------------------- decode head tail
+// One workgroup of 8 waves after the LM-head kernel of at most 8 rows: wave w
+// merges row w's partial lists (n_lists <= 256 sorted lists of K keys), then
+// the workgroup walks every block on the merged lattice.
+//
+// The merge reads list heads first.  With v the largest value such that at
+// least K heads have a high word (the order image of the logit) >= v, any key
+// whose high word is below v has K larger keys and is not among the row's K
+// best; so only lists whose head reaches v, and only their keys that do,
+// remain.  Those survivors (usually K to 2K of them) are sorted by a bitonic
+// network of 128 keys; when more than 128 survive (massive ties) every key
+// of the qualifying lists is ranked by wave_topk instead.  Two dependent
+// loads (the heads, then those lists) and no serial ranking loop.  The walk's
+// anchors and context rows are copied to LDS while the heads load.
+constexpr int kTailWaves = 8;
+constexpr int kTailChunk = 512;      // keys a wave scans per step (8 per lane)
+constexpr int kTailCtxFloats = 8192; // context rows held in LDS (else read from global memory)
+
+// Largest v such that at least K of the wave's keys have a high word >= v
+// (0 when fewer than K keys are set).
+template <int R>
+__device__ __forceinline__ uint32_t high_word_bound(const uint64_t (&k)[R], int K) {
+    uint32_t v = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t t = v | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < R; ++i) cnt += __popcll(__ballot((uint32_t)(k[i] >> 32) >= t));
+        if (cnt >= K) v = t;
+    }
+    return v;
+}
+
+template <int NJ, bool WALK>
+__global__ __launch_bounds__(64 * kTailWaves) void decode_tail_kernel(
+    const uint64_t *__restrict__ partial, int M, int n_lists, int K, int V, int32_t *__restrict__ out_ids,
+    float *__restrict__ out_vals, const float *__restrict__ g, const uint16_t *__restrict__ A,
+    const uint16_t *__restrict__ B, const int32_t *__restrict__ anchors, int bs, int r, int32_t *__restrict__ path,
+    float *__restrict__ path_score, uint32_t *__restrict__ status) {
+    __shared__ uint64_t cand[kTailWaves][128];     // per row: survivors, then the sorted top
+    __shared__ uint64_t scratch[kTailWaves * 128];  // wave_topk (many ties)
+    __shared__ int sel[kTailWaves][256];            // per row: the lists that reach the bound
+    __shared__ int32_t ids_sm[kStreamMaxRows * DFLASH2_MAX_TOP_K];
+    __shared__ float vals_sm[kStreamMaxRows * DFLASH2_MAX_TOP_K];
+    __shared__ int32_t anchors_sm[kStreamMaxRows];
+    __shared__ __align__(16) float g_sm[WALK ? kTailCtxFloats : 1];
+    __shared__ __align__(16) uint8_t wsm[kStreamMaxRows * DFLASH2_MAX_TOP_K * 20];  // walk_lds_bytes(bs <= 8, K <= 64)
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int row = wave;
+    const uint64_t *rl = partial + (size_t)row * n_lists * K;
+    uint64_t hk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int li = lane + 64 * i;
+        hk[i] = (row < M && li < n_lists) ? rl[(size_t)li * K] : 0ull;
+    }
+    const bool g_in_lds = WALK && M * r <= kTailCtxFloats;
+    if constexpr (WALK) {
+        // issued after the heads, so both loads are in flight together
+        if ((int)threadIdx.x < M / bs) anchors_sm[threadIdx.x] = anchors[threadIdx.x];
+        if (g_in_lds)
+            for (int i = threadIdx.x; i < M * r / 4; i += blockDim.x)
+                reinterpret_cast<float4 *>(g_sm)[i] = reinterpret_cast<const float4 *>(g)[i];
+    }
+    if (row < M) {
+        const uint32_t v = high_word_bound<4>(hk, K);
+        const uint64_t lb = (uint64_t)v << 32;
+        int C = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool q = hk[i] != 0ull && hk[i] >= lb;
+            const unsigned long long m = __ballot(q);
+            if (q) sel[wave][C + lanes_below(m)] = lane + 64 * i;
+            C += __popcll(m);
+        }
+        wave_lds_fence();
+        // the survivors: keys of those lists at or above the bound
+        const int n = C * K;
+        int S = 0;
+        for (int base = 0; base < n; base += kTailChunk) {
+            uint64_t k[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = base + lane + 64 * i;
+                k[i] = e < n ? rl[(size_t)sel[wave][e / K] * K + e % K] : 0ull;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool keep = k[i] != 0ull && k[i] >= lb;
+                const unsigned long long m = __ballot(keep);
+                const int pos = S + lanes_below(m);
+                if (keep && pos < 128) cand[wave][pos] = k[i];
+                S += __popcll(m);
+            }
+        }
+        wave_lds_fence();
+        uint64_t top;
+        if (S <= 128) {
+            uint64_t x0 = 2 * lane < S ? cand[wave][2 * lane] : 0ull;
+            uint64_t x1 = 2 * lane + 1 < S ? cand[wave][2 * lane + 1] : 0ull;
+            bitonic128_desc(x0, x1);  // element 2 l + h: the (2 l + h)-th largest
+            wave_lds_fence();
+            cand[wave][2 * lane] = x0;
+            cand[wave][2 * lane + 1] = x1;
+            wave_lds_fence();
+            top = lane < K ? cand[wave][lane] : 0ull;
+        } else {
+            // more than 128 keys tie at the bound: rank every key of the lists
+            top = 0ull;
+            for (int base = 0; base < n; base += kTailChunk) {
+                uint64_t k[9];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int e = base + lane + 64 * i;
+                    k[i] = e < n ? rl[(size_t)sel[wave][e / K] * K + e % K] : 0ull;
+                }
+                k[8] = top;
+                top = wave_topk<9>(k, K, scratch + wave * 128);
+            }
+        }
+        if (lane < K) {
+            const int32_t id = top ? (int32_t)key_id(top) : -1;
+            const float val = top ? key_val(top) : -__builtin_inff();
+            out_ids[(size_t)row * K + lane] = id;
+            out_vals[(size_t)row * K + lane] = val;
+            ids_sm[row * K + lane] = id;
+            vals_sm[row * K + lane] = val;
+        }
+    }
+    if constexpr (WALK) {
+        __syncthreads();
+        const float *gw = g_in_lds ? g_sm : g;
+        for (int blk = 0; blk < M / bs; ++blk) {
+            walk_block<uint16_t, NJ, false>(blk, wsm, gw, A, B, ids_sm, vals_sm, anchors_sm, bs, V, r, K, path,
+                                            path_score, status, 1.f, 0u, 0u);
+            __syncthreads();
+        }
+    }
+}
+
 // ---------------------------------------------------------------- host side
 
 static int first_stage_keys(int n_keys, int K) {
@@ -1498,12 +1685,13 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
                 hipError_t err = set_lds(kern, p.lds);
                 if (err != hipSuccess) return err;
                 hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(64 * kDmaWaves), p.lds, stream, (const uint16_t *)h,
-                                   (const uint16_t *)w, (int)M, H, V, K, gold, gold_logit, partial, status, ue);
+                                   (const uint16_t *)w, (int)M, H, V, K, gold, gold_logit, partial, status, ue,
+                                   DecodeFuse{});
                 return hipGetLastError();
             };
-            e = p.ksplit == 4 ? launch(lmhead_dma_kernel<4, LSE>)
-                : p.ksplit == 2 ? launch(lmhead_dma_kernel<2, LSE>)
-                                : launch(lmhead_dma_kernel<1, LSE>);
+            e = p.ksplit == 4 ? launch(lmhead_dma_kernel<4, LSE, false>)
+                : p.ksplit == 2 ? launch(lmhead_dma_kernel<2, LSE, false>)
+                                : launch(lmhead_dma_kernel<1, LSE, false>);
         } else {
             return hipErrorInvalidValue;
         }
@@ -1555,6 +1743,63 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
                        p.big ? (const T *)h : nullptr, p.big ? (const T *)w : nullptr, H, ue, p.n_lists, um.lse,
                        um.gold_prob, um.hit);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- decode head, host side
+
+DecodeLayout decode_layout(int64_t M, int H, int V, int r, int K) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    DecodeLayout L{};
+    const int tiles = (V + 15) / 16 + (r > 0 ? (r + 15) / 16 : 0);
+    L.grid = tiles < kStreamWGs ? tiles : kStreamWGs;
+    L.partial = kStatusBytes;
+    L.g = L.partial + up((size_t)M * L.grid * K * 8);
+    L.total = L.g + up((size_t)M * (r > 0 ? r : 0) * 4);
+    return L;
+}
+
+bool decode_head_supported(int64_t M, int H, int V, int r, int K) {
+    const int ks = dma_ksplit(H);
+    return M >= 1 && M <= kStreamMaxRows && ks > 0 && dma_lds_bytes(H, ks) <= 160 * 1024 && K >= 1 &&
+           K <= DFLASH2_MAX_TOP_K && (uint64_t)V * H * 2 < (1ull << 32) && (uint64_t)(r > 0 ? r : 0) * H * 2 < (1ull << 32);
+}
+
+hipError_t launch_decode_head(int64_t M, int H, int V, int K, const void *h, const void *w, int r, const void *w_h,
+                              const void *A, const void *B, const int32_t *anchors, int bs, int32_t *out_ids,
+                              float *out_vals, int32_t *path, float *path_score, void *workspace, hipStream_t stream) {
+    const bool walk = w_h != nullptr;
+    const DecodeLayout L = decode_layout(M, H, V, walk ? r : 0, K);
+    uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+    uint32_t *status = reinterpret_cast<uint32_t *>(ws);
+    uint64_t *partial = reinterpret_cast<uint64_t *>(ws + L.partial);
+    float *g = reinterpret_cast<float *>(ws + L.g);
+    const DecodeFuse fu{(const uint16_t *)w_h, walk ? r : 0, g};
+    const int ks = dma_ksplit(H);
+    const size_t lds = dma_lds_bytes(H, ks);
+    auto stream_kernel = [&](auto kern) -> hipError_t {
+        hipError_t err = set_lds(kern, lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3(L.grid), dim3(64 * kDmaWaves), lds, stream, (const uint16_t *)h,
+                           (const uint16_t *)w, (int)M, H, V, K, nullptr, nullptr, partial, status,
+                           UnaryEpi{1.f, 0.f, nullptr}, fu);
+        return hipGetLastError();
+    };
+    hipError_t e = ks == 4 ? stream_kernel(lmhead_dma_kernel<4, false, true>)
+                   : ks == 2 ? stream_kernel(lmhead_dma_kernel<2, false, true>)
+                             : stream_kernel(lmhead_dma_kernel<1, false, true>);
+    if (e != hipSuccess) return e;
+    auto tail = [&](auto kern) -> hipError_t {
+        hipLaunchKernelGGL(kern, dim3(1), dim3(64 * kTailWaves), 0, stream, partial, (int)M, L.grid, K, V, out_ids,
+                           out_vals, g, (const uint16_t *)A, (const uint16_t *)B, anchors, bs, walk ? r : 0, path,
+                           path_score, status);
+        return hipGetLastError();
+    };
+    if (!walk) return tail(decode_tail_kernel<1, false>);
+    const int nj = (K + 15) >> 4;
+    return nj == 1 ? tail(decode_tail_kernel<1, true>)
+           : nj == 2 ? tail(decode_tail_kernel<2, true>)
+           : nj == 3 ? tail(decode_tail_kernel<3, true>)
+                     : tail(decode_tail_kernel<4, true>);
 }
 
 hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const void *h, const void *w,

@@ -21,14 +21,14 @@ STATUS = {
     4: "DFLASH2_ERR_UNSUPPORTED", 5: "DFLASH2_ERR_ALIAS", 6: "DFLASH2_ERR_WORKSPACE",
     7: "DFLASH2_ERR_LAUNCH", 8: "DFLASH2_ERR_DEVICE_ID_RANGE",
 }
-OP_UNARY_TOPK, OP_SELECTOR_WALK, OP_SELECTOR_TF, OP_SELECTOR_CE_BACKWARD = 0, 1, 2, 3
+OP_UNARY_TOPK, OP_SELECTOR_WALK, OP_SELECTOR_TF, OP_SELECTOR_CE_BACKWARD, OP_DECODE_HEAD = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 MAX_TOP_K, MAX_TAPS, MAX_BLOCK_SIZE, MAX_RANK = 64, 16, 64, 4096
 NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024 + 256
 
 EXPORTS = ["dflash2_conv_prepare", "dflash2_conv_finish", "dflash2_unary_topk", "dflash2_unary_topk_ex",
            "dflash2_selector_walk", "dflash2_selector_walk_noalloc", "dflash2_selector_sample", "dflash2_selector_score_tf",
-           "dflash2_selector_ce_backward", "dflash2_workspace_bytes",
+           "dflash2_selector_ce_backward", "dflash2_decode_head", "dflash2_workspace_bytes",
            "dflash2_status_str", "dflash2_read_device_status", "dflash2_version"]
 
 
@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
                                     ctypes.c_float, ctypes.c_uint64, P, P, P, SZ, P],
         "dflash2_selector_score_tf": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "dflash2_selector_ce_backward": [ctypes.c_int, I64, I32, I32, I32, I32] + [P] * 16 + [P, SZ, P],
+        "dflash2_decode_head": [ctypes.c_int, I32, I32, I32, I32, I32, I32] + [P] * 10 + [P, SZ, P],
         "dflash2_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "dflash2_status_str": [ctypes.c_int],
         "dflash2_read_device_status": [P, P],
@@ -288,6 +289,42 @@ def selector_sample(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, b
                                       _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "dflash2_selector_sample")
     return path, ps
+
+
+def decode_head(h, w_lm, top_k: int, w_h=None, cb_pred=None, cb_succ=None, anchor_ids=None,
+                block_size: Optional[int] = None, workspace: Optional[torch.Tensor] = None, want_scores: bool = True,
+                out=None):
+    """The decode step in one launch: h [N, H] (N <= 8, bf16), w_lm [V, H] -> (ids [N, K], vals [N, K],
+    path [n_blocks, bs] or None, path_score or None).  With w_h, cb_pred, cb_succ and anchor_ids the greedy
+    walk of every block (block_size = N / n_blocks) runs in the same launch; without them only the lattice
+    is formed.  `out` may pass (ids, vals, path, path_score) to write into."""
+    _same_dtype(h, w_lm)
+    N, H = h.shape
+    V = w_lm.shape[0]
+    dev = h.device
+    sel = w_h is not None
+    r = 0
+    nb, bs = 1, N
+    if sel:
+        _same_dtype(h, w_h, cb_pred, cb_succ)
+        _ids(anchor_ids, "anchor_ids")
+        r = cb_pred.shape[1]
+        nb = anchor_ids.shape[0]
+        bs = block_size if block_size is not None else N // max(nb, 1)
+    if out is not None:
+        ids, vals, path, ps = out
+    else:
+        ids = torch.empty((N, top_k), dtype=torch.int32, device=dev)
+        vals = torch.empty((N, top_k), dtype=torch.float32, device=dev)
+        path = torch.empty((nb, bs), dtype=torch.int32, device=dev) if sel else None
+        ps = torch.empty((nb, bs), dtype=torch.float32, device=dev) if sel and want_scores else None
+    if workspace is None:
+        workspace = make_workspace(OP_DECODE_HEAD, N, H, V, r, top_k, dev)
+    st = _lib.dflash2_decode_head(_dtype_code(h), nb, bs, H, V, r, top_k, _ptr(h), _ptr(w_lm), _ptr(w_h),
+                                  _ptr(cb_pred), _ptr(cb_succ), _ptr(anchor_ids), _ptr(ids), _ptr(vals), _ptr(path),
+                                  _ptr(ps), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "dflash2_decode_head")
+    return ids, vals, path, ps
 
 
 def selector_score_tf(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, pred_ids, gold_ids=None, force=None,

@@ -77,7 +77,8 @@ typedef enum {
     DFLASH2_OP_UNARY_TOPK = 0,
     DFLASH2_OP_SELECTOR_WALK = 1,
     DFLASH2_OP_SELECTOR_TF = 2,
-    DFLASH2_OP_SELECTOR_CE_BACKWARD = 3
+    DFLASH2_OP_SELECTOR_CE_BACKWARD = 3,
+    DFLASH2_OP_DECODE_HEAD = 4
 } dflash2_op;
 
 /* Kernel limits (sizes beyond them return DFLASH2_ERR_UNSUPPORTED). */
@@ -256,6 +257,38 @@ dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t bloc
                                        float temperature, uint64_t seed, int32_t *out_path,
                                        float *out_path_score, void *workspace,
                                        size_t workspace_bytes, void *stream);
+
+/*
+ * Decode step of the draft head in two launches: the unary top-K lattice of
+ * dflash2_unary_topk and the greedy walk of dflash2_selector_walk, for at most
+ * 8 rows ([Explainer] "One Cycle, Step by Step": the lattice from the draft's
+ * hidden states, then one path per block from the last verified token;
+ * [Speculators] "Candidate Selector").  The context projection's weight rows
+ * w_h stream through the LM-head kernel after the vocabulary's, so the
+ * selector adds no pass over h of its own; one workgroup then merges the
+ * candidate lists and walks every block.
+ *   out_ids / out_vals: as dflash2_unary_topk (no gold ids);
+ *   out_path / out_path_score: as dflash2_selector_walk on that lattice.
+ * With w_h NULL (and cb_pred, cb_succ, anchor_ids, out_path, out_path_score
+ * NULL) only the lattice is formed; giving some of the selector's arguments
+ * but not all of w_h, cb_pred, cb_succ, anchor_ids and out_path returns
+ * DFLASH2_ERR_NULL.
+ *   dtype must be DFLASH2_BF16; N = n_blocks * block_size <= 8; hidden a
+ *   multiple of 512 (DFLASH2_ERR_UNSUPPORTED otherwise); rank as
+ *   dflash2_selector_walk (pass 0 without the selector); top_k in
+ *   [1, min(V, 64)].
+ *   h [N, H], w_lm [V, H], w_h [r, H], cb_pred / cb_succ [V, r]: bf16;
+ *   anchor_ids [n_blocks] int32; out_ids [N, K] int32; out_vals [N, K] float32;
+ *   out_path [n_blocks, bs] int32; out_path_score [n_blocks, bs] float32 or NULL.
+ *   workspace: at least dflash2_workspace_bytes(DFLASH2_OP_DECODE_HEAD, N,
+ *   hidden, vocab, rank (0 without the selector), top_k) bytes, any contents.
+ */
+dflash2_status dflash2_decode_head(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,
+                                   int32_t vocab, int32_t rank, int32_t top_k, const void *h,
+                                   const void *w_lm, const void *w_h, const void *cb_pred,
+                                   const void *cb_succ, const int32_t *anchor_ids, int32_t *out_ids,
+                                   float *out_vals, int32_t *out_path, float *out_path_score,
+                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Teacher-forced selector scoring of every row at once ([verl PR] "Selector

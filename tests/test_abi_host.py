@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert sorted(D.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -166,6 +166,34 @@ def test_selector_walk_noalloc_rules():
     assert walk_na(nb=257, bs=16, h=5120, v=248320, r=512, k=64) == UNSUP                 # one block more does not
     assert walk_na(path=None) == NULL and walk_na(anchors=None) == NULL
     assert walk_na(ps=fake(10)) == ALIAS
+
+
+def dhead(dtype=1, nb=1, bs=8, h=512, v=1000, r=32, k=16, wh=fake(2), A=fake(3), B=fake(4), anchors=fake(5),
+          ids=fake(10), vals=fake(11), path=fake(12), ps=None, ws=fake(20), wsb=None):
+    if wsb is None:
+        wsb = D.workspace_bytes(D.OP_DECODE_HEAD, max(nb * bs, 1), h, v, r if wh else 0, k) or 1 << 20
+    return L.dflash2_decode_head(dtype, nb, bs, h, v, r, k, fake(0), fake(1), wh, A, B, anchors, ids, vals, path, ps,
+                                 ws, wsb, None)
+
+
+@no_gpu
+def test_decode_head_rules():
+    assert dhead(k=0) == SHAPE and dhead(k=1001) == SHAPE and dhead(nb=0) == SHAPE and dhead(r=0) == SHAPE
+    assert dhead(dtype=0) == UNSUP                 # bf16 only
+    assert dhead(nb=2, bs=8) == UNSUP              # at most 8 rows
+    assert dhead(h=256) == UNSUP                   # hidden a multiple of 512
+    assert dhead(k=65) == UNSUP and dhead(r=12) == UNSUP
+    assert dhead(dtype=7) == DTYPE
+    # the selector's arguments come all together or not at all
+    assert dhead(A=None) == NULL and dhead(anchors=None) == NULL and dhead(path=None) == NULL
+    assert dhead(wh=None) == NULL                  # others given without w_h
+    assert dhead(ids=None) == NULL and dhead(ws=None) == NULL
+    assert dhead(wsb=100) == WS
+    assert dhead(vals=fake(10)) == ALIAS and dhead(path=fake(20)) == ALIAS and dhead(ps=fake(12)) == ALIAS
+    assert dhead(ids=fake(0)) == ALIAS             # an output over h
+    # without the selector the workspace holds no context rows
+    assert (D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 0, 16)
+            < D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16))
 
 
 def sample(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, temp=1.0, path=fake(10), ps=None, anchors=fake(6),
