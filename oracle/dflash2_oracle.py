@@ -39,18 +39,24 @@ import numpy as np
 
 DTYPES = ("f32", "bf16")
 
+# Precision the storage arrays are widened to, and so of every sum.  float64
+# is the oracle.  The benchmark's second CPU line times the same steps with
+# float32 sums by setting this to np.float32 around its calls; no pin and no
+# parity test ever runs with anything but float64.
+ACC = np.float64
+
 
 # --------------------------------------------------------------------------
 # storage formats
 # --------------------------------------------------------------------------
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage array -> float64, exactly.  bf16 is the high half of a float32."""
+    """Storage array -> float64 (ACC), exactly.  bf16 is the high half of a float32."""
     if dtype == "f32":
-        return np.asarray(a, dtype=np.float32).astype(np.float64)
+        return np.asarray(a, dtype=np.float32).astype(ACC)
     if dtype == "bf16":
         u = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-        return u.view(np.float32).astype(np.float64)
+        return u.view(np.float32).astype(ACC)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
