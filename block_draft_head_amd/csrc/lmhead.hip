@@ -1498,6 +1498,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void decode_tail_kernel(
             for (int i = threadIdx.x; i < M * r / 4; i += blockDim.x)
                 reinterpret_cast<float4 *>(g_sm)[i] = reinterpret_cast<const float4 *>(g)[i];
     }
+    uint64_t top = 0ull;
     if (row < M) {
         const uint32_t v = high_word_bound<4>(hk, K);
         const uint64_t lb = (uint64_t)v << 32;
@@ -1530,7 +1531,6 @@ __global__ __launch_bounds__(64 * kTailWaves) void decode_tail_kernel(
             }
         }
         wave_lds_fence();
-        uint64_t top;
         if (S <= 128) {
             uint64_t x0 = 2 * lane < S ? cand[wave][2 * lane] : 0ull;
             uint64_t x1 = 2 * lane + 1 < S ? cand[wave][2 * lane + 1] : 0ull;
@@ -1554,6 +1554,8 @@ __global__ __launch_bounds__(64 * kTailWaves) void decode_tail_kernel(
                 top = wave_topk<9>(k, K, scratch + wave * 128);
             }
         }
+    }
+    if (row < M) {
         if (lane < K) {
             const int32_t id = top ? (int32_t)key_id(top) : -1;
             const float val = top ? key_val(top) : -__builtin_inff();

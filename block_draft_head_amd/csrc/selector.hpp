@@ -299,24 +299,31 @@ __device__ __forceinline__ void walk_block(int blk, uint8_t *wsm, const float *_
         bool alive = anchor_ok;
         int slot = 0;  // wave-uniform
         for (int t0 = 1; t0 < bs; t0 += 8) {
+            // 8 positions' keys, scores and ids in registers (lane = slot), so
+            // each step of the chase is a handful of register reads
             uint64_t kk[8];
             float ks[8];
+            int ci[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int t = t0 + u;
-                kk[u] = (t < bs && lane < K) ? best[t * K + lane] : 0ull;
-                ks[u] = (t < bs && lane < K) ? best_s[t * K + lane] : 0.f;
+                const bool in = t < bs && lane < K;
+                kk[u] = in ? best[t * K + lane] : 0ull;
+                ks[u] = in ? best_s[t * K + lane] : 0.f;
+                ci[u] = in ? cids[t * K + lane] : -1;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int t = t0 + u;
                 if (t >= bs) break;
                 const uint64_t key = alive ? readlane_u64(kk[u], slot) : 0ull;
-                const float sc = __shfl(ks[u], slot);  // S of the pick (the key holds the noisy score when sampling)
+                // S of the pick (the key holds the noisy score when sampling)
+                const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ks[u]), slot));
                 if (key == 0) alive = false;
                 else slot = (int)key_id(key);
+                const int pick = __builtin_amdgcn_readlane(ci[u], slot);
                 if (lane == 0) {
-                    path[p0 + t] = alive ? cids[t * K + slot] : -1;
+                    path[p0 + t] = alive ? pick : -1;
                     if (path_score) path_score[p0 + t] = alive ? (SAMPLE ? sc : key_val(key)) : __builtin_nanf("");
                 }
             }

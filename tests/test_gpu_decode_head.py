@@ -114,3 +114,38 @@ def test_decode_head_flags_an_out_of_range_anchor(D):
     D.decode_head(dev["h"], dev["w_lm"], K, dev["w_h"], dev["cb_pred"], dev["cb_succ"], dev["anchors"], bs,
                   workspace=ws)
     assert D.read_device_status(ws) == 0
+
+
+@pytest.mark.parametrize("kind", ["clustered", "tied", "one_list"])
+def test_decode_head_merge_fallbacks(D, kind):
+    # lattices that defeat the fast merge: the top-K inside one workgroup's
+    # slice (a list whose prefix all reaches the bound), or every logit of a
+    # row tied (more survivors than the sort holds); the exact paths must give
+    # the plain top-K bit for bit
+    nb, bs, H, V, r, K = 1, 8, 512, 6000, 32, 16
+    inp = inputs(nb, bs, H, V, r, K, 21, 1)
+    w = O.widen(inp["w_lm"], "bf16")
+    hh = O.widen(inp["h"], "bf16")
+    if kind == "clustered":
+        w[2000:2040] = hh[0] / np.linalg.norm(hh[0]) * np.linspace(1.0, 2.0, 40)[:, None]
+    elif kind == "tied":
+        w[:] = w[7]
+    else:
+        w[:] = 0.0
+        w[3000:3020] = hh[:1] * 0.01
+    inp["w_lm"] = O.round_bf16(w)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    ids, vals, path, ps = D.decode_head(dev["h"], dev["w_lm"], K, dev["w_h"], dev["cb_pred"], dev["cb_succ"],
+                                        dev["anchors"], bs)
+    ref_ids, ref_vals, _ = D.unary_topk(dev["h"], dev["w_lm"], K)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ref_ids) and torch.equal(vals, ref_vals)
+    U = O.lm_logits(inp["h"], inp["w_lm"], "bf16")
+    fails, _, msgs = compare_topk(to_np(ids), to_np(vals), U, K)
+    assert fails == 0, msgs
+    gids = to_np(ids)
+    u64 = U[np.arange(U.shape[0])[:, None], gids]
+    g64 = O.context_projection(inp["h"], inp["w_h"], "bf16")
+    fails, _, _, msgs = compare_walk(to_np(path), to_np(ps), g64, inp["cb_pred"], inp["cb_succ"], gids, u64,
+                                     inp["anchors"], bs, "bf16")
+    assert fails == 0, msgs
