@@ -65,6 +65,48 @@ def build(jobs: int = 8, verbose: bool = True) -> str:
     return LIB
 
 
+# Host code instrumented by AddressSanitizer and UndefinedBehaviorSanitizer;
+# device code left alone (each flag goes to the host compilation only).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
+
+
+def asan_runtime() -> str:
+    """The compiler's shared AddressSanitizer runtime (LD_PRELOAD it into a
+    process that loads the sanitized library)."""
+    clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang++")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime was not found")
+    return path
+
+
+def build_host_sanitized(out_dir: str, jobs: int = 8) -> str:
+    """The same sources as build(), at -O1, with the host side sanitized: a
+    library for the ABI tests' host validation on a machine without a GPU.
+    Its kernels are never launched.  Returns the library path."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-fno-omit-frame-pointer", *SANITIZE]
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), "-x", "hip", *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libdflash2.so")
+    rt_dir = os.path.dirname(asan_runtime())
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *SANITIZE, f"-Wl,-rpath,{rt_dir}", "-o", lib, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))

@@ -5,7 +5,9 @@
 #include <cmath>
 #include <hip/hip_runtime.h>
 
+#include <array>
 #include <climits>
+#include <iterator>
 #include <cstdint>
 
 #include "../../include/dflash2.h"
@@ -25,6 +27,28 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return na && nb && x < y + nb && y < x + na;
 }
+
+// A byte range of a call's argument (an empty range when the pointer is NULL).
+struct Span {
+    const void *p;
+    size_t b;
+};
+
+// true when two outputs share a byte, or an output shares one with an input
+template <class O, class I>
+bool aliased(const O &outs, const I &ins) {
+    const size_t no = std::size(outs), ni = std::size(ins);
+    for (size_t i = 0; i < no; ++i) {
+        for (size_t j = i + 1; j < no; ++j)
+            if (overlaps(outs[i].p, outs[i].b, outs[j].p, outs[j].b)) return true;
+        for (size_t j = 0; j < ni; ++j)
+            if (overlaps(outs[i].p, outs[i].b, ins[j].p, ins[j].b)) return true;
+    }
+    return false;
+}
+
+// The bytes of an optional argument: 0 when it is NULL.
+size_t opt(const void *p, size_t b) { return p ? b : 0; }
 
 dflash2_status launched(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : DFLASH2_ERR_LAUNCH; }
 
@@ -54,11 +78,29 @@ dflash2_status check_selector(int dtype, int64_t n_rows, int32_t hidden, int32_t
     return DFLASH2_OK;
 }
 
+// The walk's and sampler's outputs (the workspace among them) and inputs.
+std::array<Span, 3> walk_outputs(int64_t N, const void *path, const void *score, const void *ws, size_t ws_bytes) {
+    return {Span{path, (size_t)N * 4}, Span{score, opt(score, (size_t)N * 4)}, Span{ws, ws_bytes}};
+}
+std::array<Span, 7> walk_inputs(int dtype, int32_t n_blocks, int64_t N, int32_t hidden, int32_t vocab, int32_t rank,
+                                int32_t top_k, const void *h, const void *w_h, const void *A, const void *B,
+                                const void *cand_ids, const void *cand_vals, const void *anchors) {
+    const size_t es = elem_size(dtype), nk = (size_t)N * top_k * 4, cb = (size_t)vocab * rank * es;
+    return {Span{h, (size_t)N * hidden * es}, Span{w_h, (size_t)rank * hidden * es}, Span{A, cb}, Span{B, cb},
+            Span{cand_ids, nk}, Span{cand_vals, nk}, Span{anchors, (size_t)n_blocks * 4}};
+}
+
 }  // namespace
 
 extern "C" {
 
 const char *dflash2_version(void) { return "dflash2-gfx950 0.1.0"; }
+
+dflash2_status dflash2_debug_force_slabs(int32_t n_slabs) {
+    if (n_slabs < 0 || n_slabs > 4096) return DFLASH2_ERR_SHAPE;
+    set_forced_slabs(n_slabs);
+    return DFLASH2_OK;
+}
 
 const char *dflash2_status_str(int s) {
     switch (s) {
@@ -112,8 +154,10 @@ dflash2_status dflash2_conv_prepare(int dtype, int64_t n_tokens, int32_t block_s
     const size_t es = elem_size(dtype);
     const size_t act = (size_t)n_tokens * hidden * es;
     const size_t kp = (size_t)n_tokens * taps * (hidden / group_size) * 4;
-    if (overlaps(x_out, act, x, act) || overlaps(k_post, kp, x, act) || overlaps(k_post, kp, x_out, act))
-        return DFLASH2_ERR_ALIAS;
+    const size_t G = (size_t)(hidden / group_size);
+    const Span outs[] = {{x_out, act}, {k_post, kp}};
+    const Span ins[] = {{x, act}, {w_proj, 2 * (size_t)taps * G * hidden * es}, {base, 2 * (size_t)taps * hidden * es}};
+    if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
     return launched(launch_conv_prepare(dtype, n_tokens, block_size, hidden, taps, group_size, x,
                                         w_proj, base, x_out, k_post, (hipStream_t)stream));
 }
@@ -128,7 +172,9 @@ dflash2_status dflash2_conv_finish(int dtype, int64_t n_tokens, int32_t block_si
     const size_t es = elem_size(dtype);
     const size_t act = (size_t)n_tokens * hidden * es;
     const size_t kp = (size_t)n_tokens * taps * (hidden / group_size) * 4;
-    if (overlaps(y_out, act, y, act) || overlaps(y_out, act, k_post, kp)) return DFLASH2_ERR_ALIAS;
+    const Span outs[] = {{y_out, act}};
+    const Span ins[] = {{y, act}, {k_post, kp}, {base, 2 * (size_t)taps * hidden * es}};
+    if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
     return launched(launch_conv_finish(dtype, n_tokens, block_size, hidden, taps, group_size, y,
                                        k_post, base, y_out, (hipStream_t)stream));
 }
@@ -147,10 +193,11 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
     if (gold_ids && !out_gold_logit) return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_UNARY_TOPK, n_rows, hidden, vocab, 0, top_k))
         return DFLASH2_ERR_WORKSPACE;
-    const size_t nk = (size_t)n_rows * top_k;
-    if (overlaps(out_ids, nk * 4, out_vals, nk * 4) || overlaps(out_ids, nk * 4, workspace, workspace_bytes) ||
-        overlaps(out_vals, nk * 4, workspace, workspace_bytes))
-        return DFLASH2_ERR_ALIAS;
+    const size_t nk = (size_t)n_rows * top_k, n = (size_t)n_rows, es = elem_size(dtype);
+    const Span outs[] = {{out_ids, nk * 4}, {out_vals, nk * 4}, {out_gold_logit, opt(out_gold_logit, n * 4)},
+                         {workspace, workspace_bytes}};
+    const Span ins[] = {{h, n * hidden * es}, {w_lm, (size_t)vocab * hidden * es}, {gold_ids, opt(gold_ids, n * 4)}};
+    if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
     return launched(launch_unary_topk(dtype, n_rows, hidden, vocab, top_k, h, w_lm, gold_ids, out_ids,
                                       out_vals, out_gold_logit, workspace, (hipStream_t)stream));
 }
@@ -173,15 +220,12 @@ dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, 
     if ((out_gold_prob || out_gold_hit) && !gold_ids) return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_UNARY_TOPK, n_rows, hidden, vocab, 0, top_k))
         return DFLASH2_ERR_WORKSPACE;
-    const size_t nk = (size_t)n_rows * top_k, n = (size_t)n_rows;
-    struct Span { const void *p; size_t b; };
-    const Span outs[] = {{out_ids, nk * 4}, {out_vals, nk * 4}, {out_gold_logit, out_gold_logit ? n * 4 : 0},
-                         {out_lse, out_lse ? n * 4 : 0}, {out_gold_prob, out_gold_prob ? n * 4 : 0},
-                         {out_gold_hit, out_gold_hit ? n : 0}, {workspace, workspace_bytes}};
-    constexpr size_t no = sizeof(outs) / sizeof(outs[0]);
-    for (size_t i = 0; i < no; ++i)
-        for (size_t j = i + 1; j < no; ++j)
-            if (overlaps(outs[i].p, outs[i].b, outs[j].p, outs[j].b)) return DFLASH2_ERR_ALIAS;
+    const size_t nk = (size_t)n_rows * top_k, n = (size_t)n_rows, es = elem_size(dtype);
+    const Span outs[] = {{out_ids, nk * 4}, {out_vals, nk * 4}, {out_gold_logit, opt(out_gold_logit, n * 4)},
+                         {out_lse, opt(out_lse, n * 4)}, {out_gold_prob, opt(out_gold_prob, n * 4)},
+                         {out_gold_hit, opt(out_gold_hit, n)}, {workspace, workspace_bytes}};
+    const Span ins[] = {{h, n * hidden * es}, {w_lm, (size_t)vocab * hidden * es}, {gold_ids, opt(gold_ids, n * 4)}};
+    if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
     const UnaryMetrics um{output_multiplier, final_logit_softcapping, out_lse, out_gold_prob, out_gold_hit};
     return launched(launch_unary_topk(dtype, n_rows, hidden, vocab, top_k, h, w_lm, gold_ids, out_ids, out_vals,
                                       out_gold_logit, workspace, (hipStream_t)stream, &um));
@@ -203,10 +247,9 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
         return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
-    const size_t np = (size_t)N * 4;
-    if (overlaps(out_path, np, workspace, workspace_bytes) ||
-        (out_path_score && (overlaps(out_path_score, np, workspace, workspace_bytes) ||
-                            overlaps(out_path_score, np, out_path, np))))
+    if (aliased(walk_outputs(N, out_path, out_path_score, workspace, workspace_bytes),
+                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, cb_pred, cb_succ, cand_ids,
+                            cand_vals, anchor_ids)))
         return DFLASH2_ERR_ALIAS;
     return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
                                          cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
@@ -228,8 +271,10 @@ dflash2_status dflash2_selector_walk_noalloc(int dtype, int32_t n_blocks, int32_
         return DFLASH2_ERR_UNSUPPORTED;
     if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path)
         return DFLASH2_ERR_NULL;
-    const size_t np = (size_t)N * 4;
-    if (out_path_score && overlaps(out_path_score, np, out_path, np)) return DFLASH2_ERR_ALIAS;
+    if (aliased(walk_outputs(N, out_path, out_path_score, nullptr, 0),
+                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, cb_pred, cb_succ, cand_ids,
+                            cand_vals, anchor_ids)))
+        return DFLASH2_ERR_ALIAS;
     void *scratch = nullptr;
     if (noalloc_scratch(&scratch) != hipSuccess) return DFLASH2_ERR_LAUNCH;
     return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
@@ -254,10 +299,9 @@ dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t bloc
         return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
-    const size_t np = (size_t)N * 4;
-    if (overlaps(out_path, np, workspace, workspace_bytes) ||
-        (out_path_score && (overlaps(out_path_score, np, workspace, workspace_bytes) ||
-                            overlaps(out_path_score, np, out_path, np))))
+    if (aliased(walk_outputs(N, out_path, out_path_score, workspace, workspace_bytes),
+                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, cb_pred, cb_succ, cand_ids,
+                            cand_vals, anchor_ids)))
         return DFLASH2_ERR_ALIAS;
     const SampleParams sp{temperature, seed};
     return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
@@ -287,18 +331,13 @@ dflash2_status dflash2_decode_head(int dtype, int32_t n_blocks, int32_t block_si
     if (sel && (!w_h || !cb_pred || !cb_succ || !anchor_ids || !out_path)) return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_DECODE_HEAD, N, hidden, vocab, r, top_k))
         return DFLASH2_ERR_WORKSPACE;
-    const size_t nk = (size_t)N * top_k * 4, np = (size_t)N * 4;
-    struct Span { const void *p; size_t b; };
-    const Span outs[] = {{out_ids, nk}, {out_vals, nk}, {out_path, out_path ? np : 0},
-                         {out_path_score, out_path_score ? np : 0}, {workspace, workspace_bytes}};
-    const Span ins[] = {{h, (size_t)N * hidden * 2}, {anchor_ids, anchor_ids ? (size_t)n_blocks * 4 : 0}};
-    constexpr size_t no = sizeof(outs) / sizeof(outs[0]);
-    for (size_t i = 0; i < no; ++i) {
-        for (size_t j = i + 1; j < no; ++j)
-            if (overlaps(outs[i].p, outs[i].b, outs[j].p, outs[j].b)) return DFLASH2_ERR_ALIAS;
-        for (const Span &in : ins)
-            if (overlaps(outs[i].p, outs[i].b, in.p, in.b)) return DFLASH2_ERR_ALIAS;
-    }
+    const size_t nk = (size_t)N * top_k * 4, np = (size_t)N * 4, cb = (size_t)vocab * r * 2;
+    const Span outs[] = {{out_ids, nk}, {out_vals, nk}, {out_path, opt(out_path, np)},
+                         {out_path_score, opt(out_path_score, np)}, {workspace, workspace_bytes}};
+    const Span ins[] = {{h, (size_t)N * hidden * 2}, {w_lm, (size_t)vocab * hidden * 2},
+                        {w_h, opt(w_h, (size_t)r * hidden * 2)}, {cb_pred, opt(cb_pred, cb)},
+                        {cb_succ, opt(cb_succ, cb)}, {anchor_ids, opt(anchor_ids, (size_t)n_blocks * 4)}};
+    if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
     return launched(launch_decode_head(N, hidden, vocab, top_k, h, w_lm, r, sel ? w_h : nullptr, cb_pred, cb_succ,
                                        anchor_ids, block_size, out_ids, out_vals, out_path, out_path_score,
                                        workspace, (hipStream_t)stream));
@@ -323,10 +362,14 @@ dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidd
     if (gold_ids && (!out_ce || !out_valid)) return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_TF, n_rows, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
-    const size_t nk = (size_t)n_rows * top_k * 4;
-    if (overlaps(out_scores, nk, workspace, workspace_bytes) || overlaps(out_best_ids, (size_t)n_rows * 4, workspace, workspace_bytes) ||
-        overlaps(out_scores, nk, out_best_ids, (size_t)n_rows * 4))
-        return DFLASH2_ERR_ALIAS;
+    const size_t nk = (size_t)n_rows * top_k * 4, n = (size_t)n_rows, es = elem_size(dtype);
+    const size_t cb = (size_t)vocab * rank * es;
+    const Span outs[] = {{out_scores, nk}, {out_best_ids, n * 4}, {out_ce, opt(out_ce, n * 4)},
+                         {out_valid, opt(out_valid, n)}, {workspace, workspace_bytes}};
+    const Span ins[] = {{h, n * hidden * es}, {w_h, (size_t)rank * hidden * es}, {cb_pred, cb}, {cb_succ, cb},
+                        {cand_ids, nk}, {cand_vals, nk}, {pred_ids, n * 4}, {gold_ids, opt(gold_ids, n * 4)},
+                        {force, opt(force, n)}, {gold_logit, opt(gold_logit, n * 4)}};
+    if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
     return launched(launch_selector_tf(dtype, n_rows, hidden, vocab, rank, top_k, h, w_h, cb_pred,
                                        cb_succ, cand_ids, cand_vals, pred_ids, gold_ids, force,
                                        gold_logit, out_scores, out_best_ids, out_ce, out_valid,
@@ -356,20 +399,14 @@ dflash2_status dflash2_selector_ce_backward(int dtype, int64_t n_rows, int32_t h
     const size_t es = elem_size(dtype);
     const size_t cb = (size_t)vocab * rank * 4, wh = (size_t)rank * hidden * 4;
     const size_t n = (size_t)n_rows, nk = n * top_k;
-    struct Span { const void *p; size_t b; };
-    const Span outs[] = {{grad_pred, cb}, {grad_succ, cb}, {grad_wh, wh}, {out_ce, out_ce ? n * 4 : 0},
-                         {out_valid, out_valid ? n : 0}};
+    const Span outs[] = {{grad_pred, cb}, {grad_succ, cb}, {grad_wh, wh}, {out_ce, opt(out_ce, n * 4)},
+                         {out_valid, opt(out_valid, n)}};
     const Span ins[] = {{h, n * hidden * es}, {w_h, (size_t)rank * hidden * es},
                         {cb_pred, (size_t)vocab * rank * es}, {cb_succ, (size_t)vocab * rank * es},
                         {cand_ids, nk * 4}, {cand_vals, nk * 4}, {pred_ids, n * 4}, {gold_ids, n * 4},
-                        {force, force ? n : 0}, {gold_logit, gold_logit ? n * 4 : 0}, {grad_ce, n * 4},
+                        {force, opt(force, n)}, {gold_logit, opt(gold_logit, n * 4)}, {grad_ce, n * 4},
                         {workspace, workspace_bytes}};
-    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
-        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
-            if (overlaps(outs[i].p, outs[i].b, outs[j].p, outs[j].b)) return DFLASH2_ERR_ALIAS;
-        for (const Span &in : ins)
-            if (overlaps(outs[i].p, outs[i].b, in.p, in.b)) return DFLASH2_ERR_ALIAS;
-    }
+    if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
     return launched(launch_selector_ce_backward(dtype, n_rows, hidden, vocab, rank, top_k, h, w_h, cb_pred,
                                                 cb_succ, cand_ids, cand_vals, pred_ids, gold_ids, force,
                                                 gold_logit, grad_ce, grad_pred, grad_succ, grad_wh, out_ce,

@@ -29,6 +29,8 @@ struct LmheadPlan {
     size_t lse_offset;    // byte offset of the per-list log-sum-exp partials (float2 [M][n_lists])
 };
 LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K);
+// Forces the number of vocabulary slabs of every later plan (0 = automatic).
+void set_forced_slabs(int n);
 
 // LDS of one walk workgroup: the block's best-successor keys, their scores,
 // the candidate ids and (sampling) the noise.

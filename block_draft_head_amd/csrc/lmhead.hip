@@ -6,6 +6,7 @@
 // vocabulary, and topk_merge_kernel merges the slices.  A key orders
 // candidates by value, then by lower id (see make_key), so the result does not
 // depend on how the vocabulary was split.
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -1578,6 +1579,21 @@ __global__ __launch_bounds__(64 * kTailWaves) void decode_tail_kernel(
 
 // ---------------------------------------------------------------- host side
 
+// Debug knob: a fixed number of vocabulary slabs (partial top-K lists per
+// row), 0 = the automatic choice.  Each logit is formed the same way whatever
+// the split, and the merge orders keys totally, so the merged lists must not
+// depend on it; the determinism tests change it and compare.
+static std::atomic<int> g_forced_slabs{0};
+
+void set_forced_slabs(int n) { g_forced_slabs.store(n, std::memory_order_relaxed); }
+
+// The slab count: `automatic`, or the forced count, within [1, limit].
+static int slab_count(int automatic, int limit) {
+    const int f = g_forced_slabs.load(std::memory_order_relaxed);
+    const int n = f > 0 ? f : automatic;
+    return n < 1 ? 1 : n > limit ? limit : n;
+}
+
 static int first_stage_keys(int n_keys, int K) {
     return (n_keys + kMergeChunk - 1) / kMergeChunk * K;
 }
@@ -1598,7 +1614,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.dma = true;
         p.ksplit = ks;
         p.n_tiles = (V + 15) / 16;
-        p.grid_x = p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs;
+        p.grid_x = slab_count(kStreamWGs, p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs);
         p.grid_y = 1;
         p.n_lists = p.grid_x;
         p.lds = dma_lds_bytes(H, ks);
@@ -1606,7 +1622,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.streaming = true;
         p.nw = nw;
         p.n_tiles = (V + 15) / 16;
-        p.grid_x = p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs;
+        p.grid_x = slab_count(kStreamWGs, p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs);
         p.grid_y = 1;
         p.n_lists = p.grid_x;
         p.lds = stream_lds;
@@ -1616,8 +1632,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.big = true;
         p.n_mt = (int)((M + big::BM - 1) / big::BM);
         p.n_tiles = (V + big::BN - 1) / big::BN;
-        int slabs = (256 + p.n_mt - 1) / p.n_mt;
-        slabs = slabs < 1 ? 1 : slabs > p.n_tiles ? p.n_tiles : slabs;
+        const int slabs = slab_count((256 + p.n_mt - 1) / p.n_mt, p.n_tiles);
         p.grid_x = p.n_mt * slabs;
         p.grid_y = 1;
         p.n_lists = slabs;
@@ -1627,10 +1642,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.streaming = false;
         const int n_mt = (int)((M + 127) / 128);
         const int n_vt = (V + 127) / 128;
-        int slabs = (512 + n_mt - 1) / n_mt;
-        slabs = slabs < 1 ? 1 : slabs;
-        slabs = slabs > n_vt ? n_vt : slabs;
-        slabs = slabs > 1024 ? 1024 : slabs;
+        const int slabs = slab_count((512 + n_mt - 1) / n_mt, n_vt < 1024 ? n_vt : 1024);
         p.grid_x = slabs;
         p.grid_y = n_mt;
         p.n_lists = slabs;
@@ -1753,7 +1765,7 @@ DecodeLayout decode_layout(int64_t M, int H, int V, int r, int K) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     DecodeLayout L{};
     const int tiles = (V + 15) / 16 + (r > 0 ? (r + 15) / 16 : 0);
-    L.grid = tiles < kStreamWGs ? tiles : kStreamWGs;
+    L.grid = slab_count(kStreamWGs, tiles < kStreamWGs ? tiles : kStreamWGs);
     L.partial = kStatusBytes;
     L.g = L.partial + up((size_t)M * L.grid * K * 8);
     L.total = L.g + up((size_t)M * (r > 0 ? r : 0) * 4);

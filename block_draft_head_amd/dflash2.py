@@ -14,7 +14,10 @@ from typing import Optional, Tuple
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash2.so")
+# DFLASH2_LIBRARY names another build of the same ABI (the host-only,
+# sanitizer-instrumented build the ABI tests load); default: the in-tree one.
+_LIB_PATH = os.environ.get("DFLASH2_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libdflash2.so")
 
 STATUS = {
     0: "DFLASH2_OK", 1: "DFLASH2_ERR_NULL", 2: "DFLASH2_ERR_SHAPE", 3: "DFLASH2_ERR_DTYPE",
@@ -29,7 +32,7 @@ NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024 + 256
 EXPORTS = ["dflash2_conv_prepare", "dflash2_conv_finish", "dflash2_unary_topk", "dflash2_unary_topk_ex",
            "dflash2_selector_walk", "dflash2_selector_walk_noalloc", "dflash2_selector_sample", "dflash2_selector_score_tf",
            "dflash2_selector_ce_backward", "dflash2_decode_head", "dflash2_workspace_bytes",
-           "dflash2_status_str", "dflash2_read_device_status", "dflash2_version"]
+           "dflash2_status_str", "dflash2_read_device_status", "dflash2_debug_force_slabs", "dflash2_version"]
 
 
 class DFlash2Error(RuntimeError):
@@ -59,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "dflash2_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "dflash2_status_str": [ctypes.c_int],
         "dflash2_read_device_status": [P, P],
+        "dflash2_debug_force_slabs": [I32],
         "dflash2_version": [],
     }
     for name, args in sig.items():
@@ -84,6 +88,12 @@ def version() -> str:
 
 def status_str(status: int) -> str:
     return _lib.dflash2_status_str(int(status)).decode()
+
+
+def debug_force_slabs(n_slabs: int) -> None:
+    """Fixes the LM-head kernels' vocabulary slab count (0 = automatic); a
+    determinism knob.  Size workspaces after changing it."""
+    _check(_lib.dflash2_debug_force_slabs(int(n_slabs)), "dflash2_debug_force_slabs")
 
 
 def workspace_bytes(op: int, n_rows: int, hidden: int = 0, vocab: int = 0, rank: int = 0, top_k: int = 0) -> int:

@@ -336,9 +336,14 @@ dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidd
  *   the loss weight over the number of valid rows)
  *   grad_pred [V, r], grad_succ [V, r], grad_wh [r, H]: float32, accumulated
  *   into (zero them for a fresh gradient); distinct, and overlapping no input
- *   and not the workspace.  The adds are float atomics: the summation order,
- *   and so the last bits, may differ from call to call.  They must be
- *   ordinary device memory (not host-mapped).
+ *   and not the workspace; ordinary device memory (not host-mapped).
+ *   The (row, slot) contributions are counting-sorted by target codebook row
+ *   and each row's contributions are summed in chunks of 64 and added with
+ *   one read-modify-write per chunk (a row with more than 64 contributions
+ *   adds its chunks with float atomics).  The placement inside a row's
+ *   segment follows atomic counters, so the summation order of grad_pred and
+ *   grad_succ, and with it their last bits, may differ from call to call;
+ *   grad_wh is summed in a fixed order.
  *   out_ce [N] float32, out_valid [N] uint8: optional (NULL to skip), as in
  *   dflash2_selector_score_tf
  *   workspace: at least dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_CE_BACKWARD, ...)
@@ -372,6 +377,20 @@ const char *dflash2_status_str(int status);
  * (DFLASH2_ERR_LAUNCH if the read itself fails).
  */
 dflash2_status dflash2_read_device_status(const void *workspace, void *stream);
+
+/*
+ * Debug knob for determinism tests (host only, process-wide).  Fixes how many
+ * vocabulary slabs (partial top-K lists per row) the LM-head kernels of
+ * dflash2_unary_topk(_ex) and dflash2_decode_head split the vocabulary into,
+ * clamped to each kernel's own limit; 0 restores the automatic choice.  Every
+ * logit is formed the same way whatever the split and keys merge in one total
+ * order, so the ids and values returned must not change with it (the
+ * log-sum-exp outputs may differ in the last bits).  It changes
+ * dflash2_workspace_bytes for those operations: size workspaces after setting
+ * it.  Not synchronised with calls running on other host threads.
+ * n_slabs in [0, 4096] (DFLASH2_ERR_SHAPE otherwise).
+ */
+dflash2_status dflash2_debug_force_slabs(int32_t n_slabs);
 
 /* Library version, e.g. "dflash2-gfx950 0.1.0" (static string). */
 const char *dflash2_version(void);

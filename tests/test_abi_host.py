@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert sorted(D.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -54,7 +54,9 @@ def test_status_strings_and_version():
 
 
 def fake(i):
-    return P(0x100000 * (i + 1))
+    """Fake device pointer i: 64 MiB apart, so only the overlaps a test
+    plants exist."""
+    return P(0x4000000 * (i + 1))
 
 
 def prep(dtype=1, n=16, bs=8, h=256, t=2, gs=16, x=fake(0), w=fake(1), b=fake(2), xo=fake(3), kp=fake(4)):
@@ -82,8 +84,13 @@ def test_conv_pointer_and_alias_rules():
     assert prep(x=None) == NULL and prep(kp=None) == NULL and prep(w=None) == NULL
     assert fin(yo=None) == NULL and fin(kp=None) == NULL
     assert prep(xo=fake(0)) == ALIAS     # output on the input
-    assert prep(xo=P(0x100000 + 64)) == ALIAS  # partial overlap
+    assert prep(xo=P(0x4000000 + 64)) == ALIAS  # partial overlap
+    assert prep(xo=fake(2)) == ALIAS     # output on base
+    assert prep(kp=fake(1)) == ALIAS     # k_post on the projection weight
+    assert prep(kp=fake(3)) == ALIAS     # k_post on x_out
     assert fin(yo=fake(0)) == ALIAS
+    assert fin(yo=fake(2)) == ALIAS      # output on base
+    assert fin(yo=fake(1)) == ALIAS      # output on k_post
 
 
 def topk(dtype=1, n=8, h=256, v=4096, k=16, hp=fake(0), w=fake(1), gold=None, ids=fake(2), vals=fake(3),
@@ -102,6 +109,10 @@ def test_unary_topk_rules():
     assert topk(gold=fake(5), gl=None) == NULL
     assert topk(wsb=16) == WS
     assert topk(ids=fake(3)) == ALIAS    # ids on vals
+    assert topk(ids=fake(0)) == ALIAS and topk(vals=fake(1)) == ALIAS  # outputs on h, on the LM head
+    assert topk(gold=fake(5), gl=fake(5)) == ALIAS  # the gold logit over the gold ids
+    assert topk(gold=fake(5), gl=fake(4)) == ALIAS  # and over the workspace
+    assert topk(ws=fake(1)) == ALIAS     # the workspace over the LM head
 
 
 def topk_ex(dtype=1, n=8, h=256, v=4096, k=16, hp=fake(0), w=fake(1), gold=None, mult=1.0, cap=0.0, ids=fake(2),
@@ -128,6 +139,7 @@ def test_unary_topk_ex_rules():
     # outputs overlap neither each other nor the workspace
     assert topk_ex(lse=fake(3)) == ALIAS and topk_ex(gold=fake(5), gl=fake(6), hit=fake(6)) == ALIAS
     assert topk_ex(lse=fake(4)) == ALIAS
+    assert topk_ex(lse=fake(0)) == ALIAS and topk_ex(gold=fake(5), gl=fake(6), prob=fake(5)) == ALIAS
 
 
 def walk(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, ws=fake(9), wsb=None, path=fake(7), anchors=fake(6), ps=None):
@@ -147,6 +159,9 @@ def test_selector_walk_rules():
     assert walk(path=None) == NULL and walk(anchors=None) == NULL and walk(ws=None) == NULL
     assert walk(wsb=100) == WS
     assert walk(ps=fake(7)) == ALIAS
+    # outputs and workspace overlap no input: candidate ids, values, anchors, codebooks
+    assert walk(path=fake(4)) == ALIAS and walk(ps=fake(5)) == ALIAS
+    assert walk(path=fake(6)) == ALIAS and walk(ws=fake(2)) == ALIAS and walk(ps=fake(0)) == ALIAS
 
 
 def walk_na(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, path=fake(10), ps=None, anchors=fake(6)):
@@ -166,6 +181,7 @@ def test_selector_walk_noalloc_rules():
     assert walk_na(nb=257, bs=16, h=5120, v=248320, r=512, k=64) == UNSUP                 # one block more does not
     assert walk_na(path=None) == NULL and walk_na(anchors=None) == NULL
     assert walk_na(ps=fake(10)) == ALIAS
+    assert walk_na(path=fake(4)) == ALIAS and walk_na(ps=fake(6)) == ALIAS and walk_na(path=fake(3)) == ALIAS
 
 
 def dhead(dtype=1, nb=1, bs=8, h=512, v=1000, r=32, k=16, wh=fake(2), A=fake(3), B=fake(4), anchors=fake(5),
@@ -191,6 +207,8 @@ def test_decode_head_rules():
     assert dhead(wsb=100) == WS
     assert dhead(vals=fake(10)) == ALIAS and dhead(path=fake(20)) == ALIAS and dhead(ps=fake(12)) == ALIAS
     assert dhead(ids=fake(0)) == ALIAS             # an output over h
+    assert dhead(vals=fake(1)) == ALIAS and dhead(path=fake(5)) == ALIAS and dhead(ps=fake(3)) == ALIAS
+    assert dhead(ws=fake(2)) == ALIAS              # the workspace over W_H
     # without the selector the workspace holds no context rows
     assert (D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 0, 16)
             < D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16))
@@ -214,6 +232,7 @@ def test_selector_sample_rules():
     assert sample(path=None) == NULL and sample(anchors=None) == NULL and sample(ws=None) == NULL
     assert sample(wsb=100) == WS
     assert sample(ps=fake(10)) == ALIAS
+    assert sample(path=fake(5)) == ALIAS and sample(ps=fake(4)) == ALIAS and sample(ws=fake(6)) == ALIAS
 
 
 def tf(dtype=1, n=16, h=256, v=1000, r=32, k=16, gold=None, force=None, gl=None, ce=None, valid=None, ws=fake(12),
@@ -234,6 +253,11 @@ def test_selector_tf_rules():
     assert tf(scores=None) == NULL and tf(ws=None) == NULL
     assert tf(wsb=8) == WS
     assert tf(scores=fake(14)) == ALIAS
+    assert tf(scores=fake(4)) == ALIAS and tf(best=fake(6)) == ALIAS and tf(ws=fake(5)) == ALIAS
+    full = dict(gold=fake(7), force=fake(8), gl=fake(9), ce=fake(10), valid=fake(11))
+    assert tf(**{**full, "valid": fake(8)}) == ALIAS   # valid over force
+    assert tf(**{**full, "ce": fake(9)}) == ALIAS      # ce over the gold logits
+    assert tf(**{**full, "ce": fake(7)}) == ALIAS      # ce over the gold ids
 
 
 def bwd(dtype=1, n=16, h=256, v=1000, r=32, k=16, gold=fake(7), force=None, gl=None, gce=fake(9), gp=fake(20),
@@ -262,6 +286,26 @@ def test_selector_ce_backward_rules():
     assert bwd(gw=fake(0)) == ALIAS              # dW on h
     assert bwd(gs=fake(12)) == ALIAS             # dB on the workspace
     assert bwd(ce=fake(9)) == ALIAS              # ce on grad_ce
+
+
+def test_debug_slab_knob_changes_the_lm_head_workspace():
+    assert L.dflash2_debug_force_slabs(-1) == SHAPE and L.dflash2_debug_force_slabs(4097) == SHAPE
+    auto_dma = D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16)
+    auto_big = D.workspace_bytes(D.OP_UNARY_TOPK, 4096, 4096, 151936, 0, 16)
+    auto_dh = D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16)
+    try:
+        D.debug_force_slabs(7)
+        # 8 rows: 7 lists of 16 keys per row instead of 256 (plus the status
+        # header, the log-sum-exp partials and the context rows)
+        assert D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16) < auto_dma
+        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh - 8 * (256 - 7) * 16 * 8
+        assert D.workspace_bytes(D.OP_UNARY_TOPK, 4096, 4096, 151936, 0, 16) < auto_big
+        D.debug_force_slabs(100000 // 100)  # clamped to each kernel's limit
+        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh
+    finally:
+        D.debug_force_slabs(0)
+    assert D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16) == auto_dma
+    assert D.workspace_bytes(D.OP_UNARY_TOPK, 4096, 4096, 151936, 0, 16) == auto_big
 
 
 def test_workspace_sizes():

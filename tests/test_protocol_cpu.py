@@ -3,7 +3,7 @@ import numpy as np
 
 from oracle import dflash2_oracle as O
 from block_draft_head_amd.inputs import WORKLOADS, make_inputs
-from tests.helpers import act_ok, bf16_bracketed, compare_topk, conv_term_scale
+from tests.helpers import CORR_ULPS, act_ok, bf16_bracketed, compare_topk, conv_delta, corr_abs
 
 
 def test_bf16_bracket_accepts_both_neighbours_and_nothing_else():
@@ -32,15 +32,12 @@ def test_topk_comparison_flags_near_ties_and_fails_real_errors():
     assert compare_topk(np.array([[0, 1, 2]]), np.array([[5.0, 4.0, 3.1]]), U, 3)[:2] == (1, 0)
 
 
-def test_conv_rule_accepts_a_float32_sum_and_rejects_a_wrong_ulp():
-    """A float32 evaluation of the conv (float32 projection, float32 taps, one
-    rounding) passes the conv rule everywhere, including where the taps nearly
-    cancel; moving any output one bf16 step further from the exact value fails
-    it wherever the output is not near cancellation."""
-    w = WORKLOADS["serve_64x8_h5120_v248320"]
+def _float32_prepare(w, blocks):
+    """A float32 evaluation of conv prepare (float32 projection, float32 taps,
+    one rounding) on the given blocks, beside the exact value and the rule's delta."""
     inp = make_inputs(w, fields=["h", "w_proj", "base"])
     bs, T, gs = w.block_size, w.taps, w.group_size
-    rows = np.concatenate([np.arange(b * bs, (b + 1) * bs) for b in (0, 24, 62, 63)])
+    rows = np.concatenate([np.arange(b * bs, (b + 1) * bs) for b in blocks])
     h = inp["h"][rows]
     _, _, ex = O.conv_prepare(h, inp["w_proj"], inp["base"], bs, T, gs, "bf16")
     c64 = O.conv_projection(h, inp["w_proj"], T, gs, "bf16")
@@ -52,13 +49,59 @@ def test_conv_rule_accepts_a_float32_sum_and_rejects_a_wrong_ulp():
     for n in range(len(rows)):
         for j in range(min(T - 1, n % bs) + 1):
             f32[n] = f32[n] + (b32[0, j] + c32[n, 0, j, gh]) * x32[n - j]
-    got = O.round_bf16(f32.astype(np.float64))
-    scale = conv_term_scale(h, c64[:, 0], inp["base"][0], bs, gs, "bf16")
-    assert not bf16_bracketed(got, ex).all()  # the strict bracket alone rejects a correct float32 sum here
-    assert act_ok(got, ex, "bf16", scale).all()
-    # one step further out from the exact value, away from cancellation
-    g = O.widen(got, "bf16")
-    away = np.where((g >= ex) == (g >= 0), 1, -1)  # +1 grows the magnitude
-    worse = (got.astype(np.int64) + away).astype(np.uint16)
-    far = np.abs(ex) > np.ldexp(scale, -6)
-    assert not act_ok(worse, ex, "bf16", scale)[far & (g != ex)].any()
+    A = corr_abs(h, inp["w_proj"], T, gs, "bf16")
+    delta = conv_delta(h, c64[:, 0], inp["base"][0], bs, gs, "bf16", A[:, 0])
+    S = conv_delta(h, c64[:, 0], inp["base"][0], bs, gs, "bf16") * 2.0 ** 24 / (2 * T + 1)
+    return O.round_bf16(f32.astype(np.float64)), ex, delta, S, (c32, c64, A)
+
+
+def test_conv_rule_accepts_a_float32_sum_and_rejects_a_wrong_ulp():
+    """The float32 evaluation passes the conv rule everywhere, including where
+    the taps nearly cancel; moving any output one bf16 step further from the
+    exact value fails it wherever the float32 error bound is below half a bf16
+    step; the float32 projection stays within the rule's ulps of its terms;
+    and the rule is tighter than 2^-16 of the terms' magnitudes away from
+    cancellation."""
+    for name, blocks in (("serve_64x8_h5120_v248320", (0, 24, 62, 63)),
+                         ("wide_256x16_h5120_v248320_t8_k64", (0, 100, 255))):
+        w = WORKLOADS[name]
+        got, ex, delta, S, (c32, c64, A) = _float32_prepare(w, blocks)
+        assert np.all(np.abs(c32 - c64) <= CORR_ULPS * 2.0 ** -24 * A)
+        assert not bf16_bracketed(got, ex).all()  # the strict bracket alone rejects a correct float32 sum here
+        assert act_ok(got, ex, "bf16", delta).all()
+        # one step further out from the exact value
+        g = O.widen(got, "bf16")
+        away = np.where((g >= ex) == (g >= 0), 1, -1)  # +1 grows the magnitude
+        worse = (got.astype(np.int64) + away).astype(np.uint16)
+        far = delta < np.abs(ex) * 2.0 ** -10
+        assert far.mean() > 0.98
+        assert not act_ok(worse, ex, "bf16", delta)[far & (g != ex)].any()
+        # away from cancellation the bound is below 2^-16 S (2.6x at two taps)
+        big = np.abs(ex) > 0.25 * S
+        assert np.median(delta[big] / (2.0 ** -16 * S[big])) < (0.5 if w.taps == 2 else 1.0)
+
+
+def test_conv_rule_fails_a_shifted_tap():
+    """A planted mistake in the float32 evaluation (tap 1 reads the row after,
+    not the row before, and so is missing at the block's last position) fails
+    the rule on most rows past a block's first; the first rows still pass."""
+    w = WORKLOADS["serve_64x8_h5120_v248320"]
+    inp = make_inputs(w, fields=["h", "w_proj", "base"])
+    bs, T, gs = w.block_size, w.taps, w.group_size
+    h = inp["h"][: 2 * bs]
+    _, _, ex = O.conv_prepare(h, inp["w_proj"], inp["base"], bs, T, gs, "bf16")
+    c64 = O.conv_projection(h, inp["w_proj"], T, gs, "bf16")
+    x = O.widen(h, "bf16")
+    b = O.widen(inp["base"], "bf16")
+    gh = np.arange(w.hidden) // gs
+    bad = np.zeros_like(x)
+    for n in range(2 * bs):
+        p = n % bs
+        bad[n] = (b[0, 0] + c64[n, 0, 0, gh]) * x[n]
+        if 1 <= p < bs - 1:
+            bad[n] += (b[0, 1] + c64[n, 0, 1, gh]) * x[n + 1]
+    A = corr_abs(h, inp["w_proj"], T, gs, "bf16")
+    delta = conv_delta(h, c64[:, 0], inp["base"][0], bs, gs, "bf16", A[:, 0])
+    ok = act_ok(O.round_bf16(bad), ex, "bf16", delta)
+    tapped = np.array([n % bs >= 1 for n in range(2 * bs)])
+    assert (~ok[tapped]).mean() > 0.9 and ok[~tapped].all()
