@@ -100,6 +100,31 @@ def lmhead_work(w):
     return bytes_, flops
 
 
+def small_op_floors(w, ops, launch_floor_us, path):
+    """Conv and selector against their floors at decode size: each launch
+    costs at least the measured back-to-back launch floor, and each byte
+    moves at the HBM peak.  The conv wrapper is two launches (prepare before
+    the sublayer, finish after it); it reads W_k, x, y and k_post and writes
+    x_out, y_out and k_post.  The fused decode head runs the selector in the
+    LM-head launches (W_H streams with W_lm, the walk in the merge launch), so
+    its floor is bytes only: W_H plus the gathered codebook rows."""
+    es = 4 if w.dtype == "f32" else 2
+    N, H, T, G, r, K, bs = w.n_rows, w.hidden, w.taps, w.groups, w.rank, w.top_k, w.block_size
+    conv_bytes = 2 * T * G * H * es + 4 * N * H * es + 2 * N * T * G * 4
+    sel_bytes = r * H * es + 2 * (bs - 1) * K * r * es + N * r * 4
+    sel_launches = 0 if path == "decode_head" else 2
+    conv_floor = (2 * launch_floor_us + conv_bytes / (HBM_PEAK_GBS * 1e3)) * 1e-3
+    sel_floor = (sel_launches * launch_floor_us + sel_bytes / (HBM_PEAK_GBS * 1e3)) * 1e-3
+    lm = ops["lmhead"]
+    return {"launch_floor_us": launch_floor_us,
+            "conv": {"ms": ops["conv"], "launches": 2, "bytes": conv_bytes, "floor_ms": conv_floor,
+                     "gap_ms": ops["conv"] - conv_floor},
+            "selector": {"ms": ops["selector"], "launches": sel_launches, "bytes": sel_bytes, "floor_ms": sel_floor,
+                         "gap_ms": ops["selector"] - sel_floor},
+            "ratio_at_floors": (conv_floor + sel_floor) / lm if lm > 0 else None,
+            "target_ratio": 0.05}
+
+
 def traffic_for(key):
     """HBM bytes per launch from committed rocprofv3 counters, or None when
     they are missing or were taken on a different kernel source."""
@@ -512,11 +537,16 @@ def main():
     for k in ("roofline_target_frac", "tf_coverage", "ce_backward", "unary_metrics"):
         if k in head:
             out[k] = head[k]
+    out["timing"]["median_ms_flushed_steps"] = head["attribution_ms"]["full"]
+    if w.n_rows <= 8:
+        out["small_op_floors"] = small_op_floors(w, ops, launch_floor, head["path"])
 
     if not args.no_workloads:
         wl = {}
-        budget = {"tiny_fp32_16x8_h256_v4096": (50, 10, 50), "serve_64x8_h5120_v248320": (30, 5, 30),
-                  "packed_tf_512x8_h4096_v151936": (15, 3, 15), "wide_256x16_h5120_v248320_t8_k64": (10, 3, 10),
+        # (timed steps, warmup, steps per attribution variant): the attribution
+        # differences are small against the LM head, so they get more steps
+        budget = {"tiny_fp32_16x8_h256_v4096": (50, 10, 50), "serve_64x8_h5120_v248320": (30, 5, 100),
+                  "packed_tf_512x8_h4096_v151936": (15, 3, 40), "wide_256x16_h5120_v248320_t8_k64": (10, 3, 20),
                   "decode_1x8_h4096_v151936": (50, 10, 200)}
         sub = argparse.Namespace(**{**vars(args), "train": False, "metrics": False, "output_multiplier": 1.0,
                                     "softcap": 0.0, "selector": "greedy"})
