@@ -4,8 +4,8 @@
 // terms sum_r B[cand, r] * (A[pred, r] * g[n, r]) on the float32 MFMA units,
 // candidates on the rows and predecessors on the columns, the rank index
 // visited in the same order.  The greedy walk scores every adjacent pair of a
-// block at once and reduces each predecessor's row to its best successor;
-// only the final pointer chase is sequential; with many blocks (bf16) the
+// block at once and reduces each predecessor's row to its best successor, then
+// one wave chases those pointers from the anchor; with many blocks (bf16) the
 // walk instead follows the path, one position at a time against the previous
 // pick only, with that pick in column 0 (selector_chase_kernel).  Teacher
 // forcing places its one predecessor in column 0 of the same routine, so

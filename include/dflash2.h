@@ -190,8 +190,9 @@ dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, 
  * with n = blk*bs + t.  path[blk, 0] = anchor_ids[blk]; for t = 1..bs-1 the
  * candidate of row n with the highest S_t(path[blk, t-1], .) is taken (lowest
  * slot on an exact tie).  With float32 codebooks or fewer than 128 blocks,
- * every adjacent pair is scored in parallel and only the final pointer chase
- * is sequential; with bf16 codebooks and 128 blocks or more the walk follows
+ * every adjacent pair is scored at once, each predecessor keeps its best
+ * successor, and one wave follows those links from the anchor; with bf16
+ * codebooks and 128 blocks or more the walk follows
  * the path, scoring each position against the previous pick only (about half
  * the gathered bytes).  The scores, and so the path, are the same either way.
  *
