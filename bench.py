@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--metrics", action="store_true",
                     help="the LM head also forms the full-vocabulary log-sum-exp and, on teacher-forced "
                          "workloads, the gold's probability and top-K hit (recall@K, target mass, coverage)")
+    ap.add_argument("--context-rows", choices=("lmhead", "selector"), default="lmhead",
+                    help="where the selector's context rows h W_H^T are formed outside the decode head: in the "
+                         "LM head's call (W_H tiles on its weight stream), or by the selector call itself")
     ap.add_argument("--output-multiplier", type=float, default=1.0)
     ap.add_argument("--softcap", type=float, default=0.0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of each CPU-oracle sample")
@@ -89,14 +92,16 @@ def lmhead_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def lmhead_work(w):
+def lmhead_work(w, ctx=False):
     """Algorithmic bytes and FLOPs of one LM-head + top-K op: the weights
     stream once, activations are read once, ids and values are written once;
-    logits never leave the chip."""
+    logits never leave the chip.  With ctx the op also forms the context rows
+    h W_H^T: W_H streams once more and g [N, r] float32 is written."""
     es = 4 if w.dtype == "f32" else 2
     N = w.n_rows
-    bytes_ = w.vocab * w.hidden * es + N * w.hidden * es + N * w.top_k * 8
-    flops = 2.0 * N * w.vocab * w.hidden
+    rows = w.vocab + (w.rank if ctx else 0)
+    bytes_ = rows * w.hidden * es + N * w.hidden * es + N * w.top_k * 8 + (N * w.rank * 4 if ctx else 0)
+    flops = 2.0 * N * rows * w.hidden
     return bytes_, flops
 
 
@@ -287,6 +292,9 @@ class Path:
                              torch.empty((N, K), dtype=torch.float32, device="cuda"),
                              torch.empty((w.n_blocks, bs), dtype=torch.int32, device="cuda"),
                              torch.empty((w.n_blocks, bs), dtype=torch.float32, device="cuda"))
+        # outside the decode head, the context rows ride on the LM head's call
+        self.ctx = not self.fused and args.context_rows == "lmhead"
+        self.g = torch.empty((N, r), dtype=torch.float32, device="cuda") if self.ctx else None
         self.ws_topk = mk(D.OP_UNARY_TOPK, 0)
         self.ws_sel = mk(D.OP_SELECTOR_TF if self.tf else D.OP_SELECTOR_WALK, r)
         if self.tf:
@@ -312,25 +320,28 @@ class Path:
             ids, vals, _, _ = self.D.decode_head(d["h"], d["w_lm"], K, workspace=self.ws_lat,
                                                  out=(self.head_out[0], self.head_out[1], None, None))
             return ids, vals, None
-        if not self.transformed:
+        if not self.transformed and not self.ctx:
             return self.D.unary_topk(d["h"], d["w_lm"], K, gold_ids=self.gold, workspace=self.ws_topk)
         ids, vals, gl, lse, prob, hit = self.D.unary_topk_ex(d["h"], d["w_lm"], K, gold_ids=self.gold,
                                                              output_multiplier=a.output_multiplier,
                                                              softcap=a.softcap, want_lse=a.metrics,
-                                                             want_metrics=a.metrics, workspace=self.ws_topk)
+                                                             want_metrics=a.metrics, workspace=self.ws_topk,
+                                                             w_h=d["w_h"] if self.ctx else None, g=self.g)
         self.metrics_out.update(lse=lse, prob=prob, hit=hit)
         return ids, vals, gl
 
     def selector(self, ids, vals, gl):
         d, w, D = self.dev, self.w, self.D
+        # with the context rows formed by the LM head, h and W_H are not passed
+        h, wh = (None, None) if self.ctx else (d["h"], d["w_h"])
         if self.tf:
-            return D.selector_score_tf(d["h"], d["w_h"], d["cb_pred"], d["cb_succ"], ids, vals, d["pred"],
-                                       gold_ids=self.gold, force=d["force"], gold_logit=gl, workspace=self.ws_sel)
+            return D.selector_score_tf(h, wh, d["cb_pred"], d["cb_succ"], ids, vals, d["pred"], gold_ids=self.gold,
+                                       force=d["force"], gold_logit=gl, workspace=self.ws_sel, g=self.g)
         if self.args.selector == "sample":
-            return D.selector_sample(d["h"], d["w_h"], d["cb_pred"], d["cb_succ"], ids, vals, d["anchors"],
-                                     w.block_size, temperature=1.0, seed=0x5EED, workspace=self.ws_sel)
-        return D.selector_walk(d["h"], d["w_h"], d["cb_pred"], d["cb_succ"], ids, vals, d["anchors"],
-                               w.block_size, workspace=self.ws_sel)
+            return D.selector_sample(h, wh, d["cb_pred"], d["cb_succ"], ids, vals, d["anchors"], w.block_size,
+                                     temperature=1.0, seed=0x5EED, workspace=self.ws_sel, g=self.g)
+        return D.selector_walk(h, wh, d["cb_pred"], d["cb_succ"], ids, vals, d["anchors"], w.block_size,
+                               workspace=self.ws_sel, g=self.g)
 
     def backward(self, ids, vals, gl):
         d = self.dev
@@ -382,8 +393,8 @@ class Path:
         return float((path[:, 1:] != first).float().mean())
 
 
-def roofline(w, lm_ms, key):
-    lm_bytes, lm_flops = lmhead_work(w)
+def roofline(w, lm_ms, key, ctx=False):
+    lm_bytes, lm_flops = lmhead_work(w, ctx)
     mfma_bound = lm_flops / lm_bytes > (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) and w.dtype == "bf16"
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": lm_flops / (lm_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
@@ -418,7 +429,10 @@ def measure(D, torch, timer, w, dev, args, steps, warmup, attr_steps):
             "lmhead_dma_kernel + top-K merge" if w.n_rows <= 8 and w.dtype == "bf16" else
             "lmhead_stream_kernel + top-K merge" if w.n_rows <= 8 else
             "lmhead_big_kernel + top-K merge" if w.dtype == "bf16" else "lmhead_tiled_kernel + top-K merge")
-    roof = roofline(w, lm_b2b, w.name)
+    if p.ctx:
+        kern += (" (W_H tiles in the stream)" if w.dtype == "bf16" and w.n_rows > 8 else
+                 " + context projection")
+    roof = roofline(w, lm_b2b, w.name, p.ctx)
     roof["kernel"] = kern
     out = {
         "ms_per_step": statistics.median(per), "ms_per_step_mean": statistics.fmean(per),
@@ -427,6 +441,7 @@ def measure(D, torch, timer, w, dev, args, steps, warmup, attr_steps):
         "selector_plus_conv_over_lmhead": (conv + sel) / lm if lm > 0 else None,
         "attribution_ms": {k: v for k, v in med.items()}, "attribution_steps_per_variant": n_attr,
         "roofline": roof, "teeth": teeth, "path": "decode_head" if p.fused else "unary_topk + selector",
+        "context_rows": "decode head" if p.fused else "lm head" if p.ctx else "selector",
     }
     if w.name in TARGETS:
         out["roofline_target_frac"] = TARGETS[w.name]

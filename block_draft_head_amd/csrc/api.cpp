@@ -82,12 +82,13 @@ dflash2_status check_selector(int dtype, int64_t n_rows, int32_t hidden, int32_t
 std::array<Span, 3> walk_outputs(int64_t N, const void *path, const void *score, const void *ws, size_t ws_bytes) {
     return {Span{path, (size_t)N * 4}, Span{score, opt(score, (size_t)N * 4)}, Span{ws, ws_bytes}};
 }
-std::array<Span, 7> walk_inputs(int dtype, int32_t n_blocks, int64_t N, int32_t hidden, int32_t vocab, int32_t rank,
-                                int32_t top_k, const void *h, const void *w_h, const void *A, const void *B,
-                                const void *cand_ids, const void *cand_vals, const void *anchors) {
+std::array<Span, 8> walk_inputs(int dtype, int32_t n_blocks, int64_t N, int32_t hidden, int32_t vocab, int32_t rank,
+                                int32_t top_k, const void *h, const void *w_h, const float *g, const void *A,
+                                const void *B, const void *cand_ids, const void *cand_vals, const void *anchors) {
     const size_t es = elem_size(dtype), nk = (size_t)N * top_k * 4, cb = (size_t)vocab * rank * es;
-    return {Span{h, (size_t)N * hidden * es}, Span{w_h, (size_t)rank * hidden * es}, Span{A, cb}, Span{B, cb},
-            Span{cand_ids, nk}, Span{cand_vals, nk}, Span{anchors, (size_t)n_blocks * 4}};
+    return {Span{h, opt(h, (size_t)N * hidden * es)}, Span{w_h, opt(w_h, (size_t)rank * hidden * es)},
+            Span{g, opt(g, (size_t)N * rank * 4)}, Span{A, cb}, Span{B, cb}, Span{cand_ids, nk}, Span{cand_vals, nk},
+            Span{anchors, (size_t)n_blocks * 4}};
 }
 
 }  // namespace
@@ -204,10 +205,10 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
 
 dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab, int32_t top_k,
                                      const void *h, const void *w_lm, const int32_t *gold_ids,
-                                     float output_multiplier, float final_logit_softcapping, int32_t *out_ids,
-                                     float *out_vals, float *out_gold_logit, float *out_lse, float *out_gold_prob,
-                                     uint8_t *out_gold_hit, void *workspace, size_t workspace_bytes,
-                                     void *stream) {
+                                     float output_multiplier, float final_logit_softcapping, const void *w_h,
+                                     int32_t rank, int32_t *out_ids, float *out_vals, float *out_gold_logit,
+                                     float *out_lse, float *out_gold_prob, uint8_t *out_gold_hit, float *out_g,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
     if (!dtype_ok(dtype)) return DFLASH2_ERR_DTYPE;
     if (n_rows < 1 || hidden < 1 || vocab < 1) return DFLASH2_ERR_SHAPE;
     if (top_k < 1 || top_k > vocab) return DFLASH2_ERR_SHAPE;
@@ -218,22 +219,29 @@ dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, 
     if (!h || !w_lm || !out_ids || !out_vals || !workspace) return DFLASH2_ERR_NULL;
     if (gold_ids && !out_gold_logit) return DFLASH2_ERR_NULL;
     if ((out_gold_prob || out_gold_hit) && !gold_ids) return DFLASH2_ERR_NULL;
+    if (!w_h != !out_g) return DFLASH2_ERR_NULL;  // the context projection takes both
+    if (out_g) {
+        if (rank < 1) return DFLASH2_ERR_SHAPE;
+        if (rank % 8 != 0 || rank > DFLASH2_MAX_RANK) return DFLASH2_ERR_UNSUPPORTED;
+    }
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_UNARY_TOPK, n_rows, hidden, vocab, 0, top_k))
         return DFLASH2_ERR_WORKSPACE;
     const size_t nk = (size_t)n_rows * top_k, n = (size_t)n_rows, es = elem_size(dtype);
+    const size_t r = out_g ? (size_t)rank : 0;
     const Span outs[] = {{out_ids, nk * 4}, {out_vals, nk * 4}, {out_gold_logit, opt(out_gold_logit, n * 4)},
                          {out_lse, opt(out_lse, n * 4)}, {out_gold_prob, opt(out_gold_prob, n * 4)},
-                         {out_gold_hit, opt(out_gold_hit, n)}, {workspace, workspace_bytes}};
-    const Span ins[] = {{h, n * hidden * es}, {w_lm, (size_t)vocab * hidden * es}, {gold_ids, opt(gold_ids, n * 4)}};
+                         {out_gold_hit, opt(out_gold_hit, n)}, {out_g, n * r * 4}, {workspace, workspace_bytes}};
+    const Span ins[] = {{h, n * hidden * es}, {w_lm, (size_t)vocab * hidden * es}, {gold_ids, opt(gold_ids, n * 4)},
+                        {w_h, r * hidden * es}};
     if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
     const UnaryMetrics um{output_multiplier, final_logit_softcapping, out_lse, out_gold_prob, out_gold_hit};
     return launched(launch_unary_topk(dtype, n_rows, hidden, vocab, top_k, h, w_lm, gold_ids, out_ids, out_vals,
-                                      out_gold_logit, workspace, (hipStream_t)stream, &um));
+                                      out_gold_logit, workspace, (hipStream_t)stream, &um, w_h, (int)r, out_g));
 }
 
 dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,
                                      int32_t vocab, int32_t rank, int32_t top_k, const void *h,
-                                     const void *w_h, const void *cb_pred, const void *cb_succ,
+                                     const void *w_h, const float *g, const void *cb_pred, const void *cb_succ,
                                      const int32_t *cand_ids, const float *cand_vals,
                                      const int32_t *anchor_ids, int32_t *out_path,
                                      float *out_path_score, void *workspace,
@@ -243,22 +251,24 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
     dflash2_status s = check_selector(dtype, N, hidden, vocab, rank, top_k);
     if (s != DFLASH2_OK) return s;
     if (block_size > DFLASH2_MAX_BLOCK_SIZE) return DFLASH2_ERR_UNSUPPORTED;
-    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path || !workspace)
+    if (!(g || (h && w_h)) || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path ||
+        !workspace)
         return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
     if (aliased(walk_outputs(N, out_path, out_path_score, workspace, workspace_bytes),
-                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, cb_pred, cb_succ, cand_ids,
+                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, g, cb_pred, cb_succ, cand_ids,
                             cand_vals, anchor_ids)))
         return DFLASH2_ERR_ALIAS;
-    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
+    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h, g,
                                          cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
                                          out_path_score, workspace, (hipStream_t)stream, nullptr));
 }
 
 dflash2_status dflash2_selector_walk_noalloc(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,
                                              int32_t vocab, int32_t rank, int32_t top_k, const void *h,
-                                             const void *w_h, const void *cb_pred, const void *cb_succ,
+                                             const void *w_h, const float *g, const void *cb_pred,
+                                             const void *cb_succ,
                                              const int32_t *cand_ids, const float *cand_vals,
                                              const int32_t *anchor_ids, int32_t *out_path, float *out_path_score,
                                              void *stream) {
@@ -269,22 +279,22 @@ dflash2_status dflash2_selector_walk_noalloc(int dtype, int32_t n_blocks, int32_
     if (block_size > DFLASH2_MAX_BLOCK_SIZE) return DFLASH2_ERR_UNSUPPORTED;
     if (dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k) > kNoAllocScratchBytes)
         return DFLASH2_ERR_UNSUPPORTED;
-    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path)
+    if (!(g || (h && w_h)) || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path)
         return DFLASH2_ERR_NULL;
     if (aliased(walk_outputs(N, out_path, out_path_score, nullptr, 0),
-                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, cb_pred, cb_succ, cand_ids,
+                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, g, cb_pred, cb_succ, cand_ids,
                             cand_vals, anchor_ids)))
         return DFLASH2_ERR_ALIAS;
     void *scratch = nullptr;
     if (noalloc_scratch(&scratch) != hipSuccess) return DFLASH2_ERR_LAUNCH;
-    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
+    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h, g,
                                          cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
                                          out_path_score, scratch, (hipStream_t)stream, nullptr));
 }
 
 dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t block_size, int32_t hidden,
                                        int32_t vocab, int32_t rank, int32_t top_k, const void *h,
-                                       const void *w_h, const void *cb_pred, const void *cb_succ,
+                                       const void *w_h, const float *g, const void *cb_pred, const void *cb_succ,
                                        const int32_t *cand_ids, const float *cand_vals,
                                        const int32_t *anchor_ids, float temperature, uint64_t seed,
                                        int32_t *out_path, float *out_path_score, void *workspace,
@@ -295,16 +305,17 @@ dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t bloc
     if (s != DFLASH2_OK) return s;
     if (!(temperature > 0.0f) || !std::isfinite(temperature)) return DFLASH2_ERR_SHAPE;
     if (block_size > DFLASH2_MAX_BLOCK_SIZE) return DFLASH2_ERR_UNSUPPORTED;
-    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path || !workspace)
+    if (!(g || (h && w_h)) || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path ||
+        !workspace)
         return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
     if (aliased(walk_outputs(N, out_path, out_path_score, workspace, workspace_bytes),
-                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, cb_pred, cb_succ, cand_ids,
+                walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, g, cb_pred, cb_succ, cand_ids,
                             cand_vals, anchor_ids)))
         return DFLASH2_ERR_ALIAS;
     const SampleParams sp{temperature, seed};
-    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h,
+    return launched(launch_selector_walk(dtype, n_blocks, block_size, hidden, vocab, rank, top_k, h, w_h, g,
                                          cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, out_path,
                                          out_path_score, workspace, (hipStream_t)stream, &sp));
 }
@@ -345,7 +356,7 @@ dflash2_status dflash2_decode_head(int dtype, int32_t n_blocks, int32_t block_si
 
 dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab,
                                          int32_t rank, int32_t top_k, const void *h, const void *w_h,
-                                         const void *cb_pred, const void *cb_succ,
+                                         const float *g, const void *cb_pred, const void *cb_succ,
                                          const int32_t *cand_ids, const float *cand_vals,
                                          const int32_t *pred_ids, const int32_t *gold_ids,
                                          const uint8_t *force, const float *gold_logit,
@@ -354,7 +365,7 @@ dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidd
                                          size_t workspace_bytes, void *stream) {
     dflash2_status s = check_selector(dtype, n_rows, hidden, vocab, rank, top_k);
     if (s != DFLASH2_OK) return s;
-    if (!h || !w_h || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !pred_ids || !out_scores ||
+    if (!(g || (h && w_h)) || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !pred_ids || !out_scores ||
         !out_best_ids || !workspace)
         return DFLASH2_ERR_NULL;
     if (force && !gold_ids) return DFLASH2_ERR_NULL;
@@ -366,11 +377,12 @@ dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidd
     const size_t cb = (size_t)vocab * rank * es;
     const Span outs[] = {{out_scores, nk}, {out_best_ids, n * 4}, {out_ce, opt(out_ce, n * 4)},
                          {out_valid, opt(out_valid, n)}, {workspace, workspace_bytes}};
-    const Span ins[] = {{h, n * hidden * es}, {w_h, (size_t)rank * hidden * es}, {cb_pred, cb}, {cb_succ, cb},
-                        {cand_ids, nk}, {cand_vals, nk}, {pred_ids, n * 4}, {gold_ids, opt(gold_ids, n * 4)},
-                        {force, opt(force, n)}, {gold_logit, opt(gold_logit, n * 4)}};
+    const Span ins[] = {{h, opt(h, n * hidden * es)}, {w_h, opt(w_h, (size_t)rank * hidden * es)},
+                        {g, opt(g, n * rank * 4)}, {cb_pred, cb}, {cb_succ, cb}, {cand_ids, nk}, {cand_vals, nk},
+                        {pred_ids, n * 4}, {gold_ids, opt(gold_ids, n * 4)}, {force, opt(force, n)},
+                        {gold_logit, opt(gold_logit, n * 4)}};
     if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
-    return launched(launch_selector_tf(dtype, n_rows, hidden, vocab, rank, top_k, h, w_h, cb_pred,
+    return launched(launch_selector_tf(dtype, n_rows, hidden, vocab, rank, top_k, h, w_h, g, cb_pred,
                                        cb_succ, cand_ids, cand_vals, pred_ids, gold_ids, force,
                                        gold_logit, out_scores, out_best_ids, out_ce, out_valid,
                                        workspace, (hipStream_t)stream));

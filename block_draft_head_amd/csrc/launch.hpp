@@ -82,10 +82,14 @@ struct UnaryMetrics {
     float *gold_prob;  // [M] softmax probability of the gold id, or null
     uint8_t *hit;      // [M] gold id among the top K, or null
 };
+// With g (and w_h, r > 0) the call also writes the context projection
+// g = h W_Hᵀ, float32 [M, r]: on the many-row bf16 path as extra tiles of the
+// LM-head kernel's weight stream, else by its own launch.
 hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const void *h, const void *w,
                              const int32_t *gold, int32_t *out_ids, float *out_vals,
                              float *gold_logit, void *workspace, hipStream_t stream,
-                             const UnaryMetrics *metrics = nullptr);
+                             const UnaryMetrics *metrics = nullptr, const void *w_h = nullptr, int r = 0,
+                             float *g = nullptr);
 // Decode head (bf16, at most 8 rows): the LM-head kernel with the context
 // projection's rows streamed after the vocabulary's, then one workgroup that
 // merges the candidate lists and walks every block.  Workspace: status word,
@@ -101,8 +105,10 @@ hipError_t launch_decode_head(int64_t M, int H, int V, int K, const void *h, con
                               float *out_vals, int32_t *path, float *path_score, void *workspace, hipStream_t stream);
 hipError_t launch_context_proj(int dtype, int64_t N, int H, int r, const void *h, const void *w_h,
                                float *g, uint32_t *status, hipStream_t stream);
+// g_in: the context rows g = h W_Hᵀ computed beforehand (float32 [N, r]), or
+// null to form them here from h and w_h into the workspace.
 hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, int r, int K,
-                                const void *h, const void *w_h, const void *A, const void *B,
+                                const void *h, const void *w_h, const float *g_in, const void *A, const void *B,
                                 const int32_t *cand_ids, const float *cand_vals,
                                 const int32_t *anchors, int32_t *path, float *path_score,
                                 void *workspace, hipStream_t stream, const SampleParams *sample);
@@ -113,7 +119,8 @@ constexpr size_t kNoAllocScratchBytes = ((size_t)8 << 20) + kStatusBytes;
 hipError_t noalloc_scratch(void **ptr);
 
 hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
-                              const void *w_h, const void *A, const void *B, const int32_t *cand_ids,
+                              const void *w_h, const float *g_in, const void *A, const void *B,
+                              const int32_t *cand_ids,
                               const float *cand_vals, const int32_t *pred_ids,
                               const int32_t *gold_ids, const uint8_t *force,
                               const float *gold_logit, float *out_scores, int32_t *out_best,

@@ -1069,7 +1069,7 @@ template <int KL, bool LSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_big_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int n_mt, int n_slabs,
     int n_vt, uint64_t *__restrict__ partial, float *__restrict__ tiles, uint32_t *__restrict__ status,
-    UnaryEpi ue) {
+    UnaryEpi ue, DecodeFuse ctx) {
     using namespace big;
     __shared__ __align__(16) uint8_t st0[STAGE];
     __shared__ __align__(16) uint8_t st1[STAGE];
@@ -1085,7 +1085,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     big_tile_of(blockIdx.x, gridDim.x, n_mt, n_slabs, mt, slab);
     const int m0 = mt * BM;
     if (blockIdx.x == 0 && t == 0 && status) *status = 0u;
-    const int vt0 = (int)((long long)slab * n_vt / n_slabs), vt1 = (int)((long long)(slab + 1) * n_vt / n_slabs);
+    // the slabs split the vocabulary's tiles and then the context
+    // projection's (W_H rows, ctx.r > 0) as one sequence, so the extra tiles
+    // land at the ends of the last slabs without unbalancing them
+    const int n_ct = ctx.r > 0 ? (ctx.r + BN - 1) / BN : 0, n_all = n_vt + n_ct;
+    const int vt0 = (int)((long long)slab * n_all / n_slabs), vt1 = (int)((long long)(slab + 1) * n_all / n_slabs);
+    const int vt1v = vt1 < n_vt ? vt1 : n_vt;  // end of this slab's vocabulary tiles
     const bool my_ok = m0 + t < M;
     uint64_t *my_list = partial + ((size_t)(my_ok ? m0 + t : 0) * n_slabs + slab) * KL;
     float *tile = tiles + (size_t)blockIdx.x * kBigTileFloats;  // exact path: [256 rows][256 cols]
@@ -1111,7 +1116,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < (kRegList ? KL : 1); ++j) RL[j] = 0ull;
     bool prefilled = false;
+    if (vt0 >= n_vt) {
+        // a slab of context tiles only: its lists stay empty
+        if constexpr (!kRegList) {
+            if (my_ok)
+                for (int j = 0; j < KL; ++j) my_list[j] = 0ull;
+        }
+    }
     for (int vt = vt0; vt < vt1; ++pass) {
+        if (vt >= n_vt) {
+            // a context projection tile: g[m0 + row][c0 + col] = <h row, W_H row c0 + col>,
+            // the accumulators stored as they are (rows past M or r dropped)
+            const int c0 = (vt - n_vt) * BN;
+            f32x16 acc[4][4];
+            mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, ctx.wh + (size_t)c0 * H, ctx.r - c0, H, false);
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int row = m0 + acc_row(wm, tm, i, lane), col = c0 + wn * 128 + tn * 32 + (lane & 31);
+                        const float v = agpr_read(acc[tm][tn][i]);
+                        if (row < M && col < ctx.r) ctx.g[(size_t)row * ctx.r + col] = v;
+                    }
+            __syncthreads();  // every wave is done with the stage buffers
+            ++vt;
+            continue;
+        }
         const int v0 = vt * BN, par = pass & 1;
         const bool fresh = vt == vt0;
         // The tile with the vocabulary's tail takes the exact path too (the
@@ -1161,7 +1193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (!over) lse_s[t] += lse_t[t];
                 lse_t[t] = 0.f;
             }
-            if (!over && vt + 1 < vt1) {
+            if (!over && vt + 1 < vt1v) {
                 // the next tile's first k-slice loads under the list insertion (the
                 // barrier above ended the scan's use of st0)
                 const int v1 = v0 + BN;
@@ -1691,7 +1723,7 @@ template <typename T, bool LSE>
 static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K, const void *h,
                              const void *w, const int32_t *gold, int32_t *out_ids, float *out_vals,
                              float *gold_logit, uint64_t *partial, uint32_t *status, const UnaryEpi &ue,
-                             const UnaryMetrics &um, hipStream_t stream) {
+                             const UnaryMetrics &um, const DecodeFuse &ctx, hipStream_t stream) {
     hipError_t e;
     if (p.dma) {
         if constexpr (sizeof(T) == 2) {
@@ -1728,7 +1760,7 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
             float *tiles = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(partial) + p.tiles_offset);
             hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(big::NT), p.lds, stream, (const uint16_t *)h,
                                (const uint16_t *)w, (int)M, H, V, p.n_mt, p.n_lists, p.n_tiles, partial, tiles,
-                               status, ue);
+                               status, ue, ctx);
             e = hipGetLastError();
         } else {
             return hipErrorInvalidValue;
@@ -1818,7 +1850,8 @@ hipError_t launch_decode_head(int64_t M, int H, int V, int K, const void *h, con
 
 hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const void *h, const void *w,
                              const int32_t *gold, int32_t *out_ids, float *out_vals,
-                             float *gold_logit, void *workspace, hipStream_t stream, const UnaryMetrics *metrics) {
+                             float *gold_logit, void *workspace, hipStream_t stream, const UnaryMetrics *metrics,
+                             const void *w_h, int r, float *g) {
     const LmheadPlan p = plan_lmhead(dtype, M, H, V, K);
     uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
     uint64_t *partial = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
@@ -1826,15 +1859,26 @@ hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const vo
     const bool lse = um.lse || um.gold_prob;
     UnaryEpi ue{um.mult, um.cap,
                 lse ? reinterpret_cast<float2 *>(reinterpret_cast<uint8_t *>(partial) + p.lse_offset) : nullptr};
+    // the context projection: extra tiles of the many-row kernel's stream,
+    // else its own launch ahead of the LM head
+    DecodeFuse ctx{};
+    if (g && r > 0) {
+        if (p.big) {
+            ctx = DecodeFuse{(const uint16_t *)w_h, r, g};
+        } else {
+            hipError_t e = launch_context_proj(dtype, M, H, r, h, w_h, g, nullptr, stream);
+            if (e != hipSuccess) return e;
+        }
+    }
     if (dtype == 0)
         return lse ? run_lmhead<float, true>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial,
-                                             status, ue, um, stream)
+                                             status, ue, um, ctx, stream)
                    : run_lmhead<float, false>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial,
-                                              status, ue, um, stream);
+                                              status, ue, um, ctx, stream);
     return lse ? run_lmhead<uint16_t, true>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial,
-                                            status, ue, um, stream)
+                                            status, ue, um, ctx, stream)
                : run_lmhead<uint16_t, false>(p, M, H, V, K, h, w, gold, out_ids, out_vals, gold_logit, partial,
-                                             status, ue, um, stream);
+                                             status, ue, um, ctx, stream);
 }
 
 }  // namespace dflash2

@@ -252,16 +252,34 @@ __global__ __launch_bounds__(256) void selector_tf_kernel(
 
 // ------------------------------------------------------------------ host side
 
+// The selector's context rows: the caller's g_in as given (then only the
+// status word is cleared, by a one-thread kernel rather than a memset node),
+// or g = h W_Hᵀ formed into the workspace after its status word.
+__global__ void clear_status_kernel(uint32_t *status) { *status = 0u; }
+
+static hipError_t context_rows(int dtype, int64_t N, int H, int r, const void *h, const void *w_h, const float *g_in,
+                               void *workspace, const float **g, hipStream_t stream) {
+    uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
+    if (g_in) {
+        *g = g_in;
+        hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(1), 0, stream, status);
+        return hipGetLastError();
+    }
+    float *gw = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
+    *g = gw;
+    return launch_context_proj(dtype, N, H, r, h, w_h, gw, status, stream);
+}
+
 hipError_t launch_selector_walk(int dtype, int n_blocks, int bs, int H, int V, int r, int K,
-                                const void *h, const void *w_h, const void *A, const void *B,
+                                const void *h, const void *w_h, const float *g_in, const void *A, const void *B,
                                 const int32_t *cand_ids, const float *cand_vals,
                                 const int32_t *anchors, int32_t *path, float *path_score,
                                 void *workspace, hipStream_t stream, const SampleParams *sample) {
     uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
-    float *g = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
     const int64_t N = (int64_t)n_blocks * bs;
     const size_t lds = walk_lds_bytes(bs, K);
-    hipError_t e = launch_context_proj(dtype, N, H, r, h, w_h, g, status, stream);
+    const float *g = nullptr;
+    hipError_t e = context_rows(dtype, N, H, r, h, w_h, g_in, workspace, &g, stream);
     if (e != hipSuccess) return e;
     const int n_it = (K + 15) / 16;
     const int items = bs >= 2 ? 1 + (bs - 2) * n_it : 1;
@@ -331,15 +349,16 @@ hipError_t noalloc_scratch(void **ptr) {
 }
 
 hipError_t launch_selector_tf(int dtype, int64_t N, int H, int V, int r, int K, const void *h,
-                              const void *w_h, const void *A, const void *B, const int32_t *cand_ids,
+                              const void *w_h, const float *g_in, const void *A, const void *B,
+                              const int32_t *cand_ids,
                               const float *cand_vals, const int32_t *pred_ids,
                               const int32_t *gold_ids, const uint8_t *force,
                               const float *gold_logit, float *out_scores, int32_t *out_best,
                               float *out_ce, uint8_t *out_valid, void *workspace,
                               hipStream_t stream) {
     uint32_t *status = reinterpret_cast<uint32_t *>(workspace);
-    float *g = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + kStatusBytes);
-    hipError_t e = launch_context_proj(dtype, N, H, r, h, w_h, g, status, stream);
+    const float *g = nullptr;
+    hipError_t e = context_rows(dtype, N, H, r, h, w_h, g_in, workspace, &g, stream);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((N + 3) / 4);
     if (dtype == 0)

@@ -50,13 +50,13 @@ def _load() -> ctypes.CDLL:
         "dflash2_conv_prepare": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P],
         "dflash2_conv_finish": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P],
         "dflash2_unary_topk": [ctypes.c_int, I64, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
-        "dflash2_unary_topk_ex": [ctypes.c_int, I64, I32, I32, I32, P, P, P, ctypes.c_float, ctypes.c_float,
-                                  P, P, P, P, P, P, P, SZ, P],
-        "dflash2_selector_walk": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, SZ, P],
-        "dflash2_selector_walk_noalloc": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P],
-        "dflash2_selector_sample": [ctypes.c_int, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P,
-                                    ctypes.c_float, ctypes.c_uint64, P, P, P, SZ, P],
-        "dflash2_selector_score_tf": [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "dflash2_unary_topk_ex": [ctypes.c_int, I64, I32, I32, I32, P, P, P, ctypes.c_float, ctypes.c_float, P, I32,
+                                  P, P, P, P, P, P, P, P, SZ, P],
+        "dflash2_selector_walk": [ctypes.c_int, I32, I32, I32, I32, I32, I32] + [P] * 11 + [SZ, P],
+        "dflash2_selector_walk_noalloc": [ctypes.c_int, I32, I32, I32, I32, I32, I32] + [P] * 11,
+        "dflash2_selector_sample": [ctypes.c_int, I32, I32, I32, I32, I32, I32] + [P] * 8 +
+                                   [ctypes.c_float, ctypes.c_uint64, P, P, P, SZ, P],
+        "dflash2_selector_score_tf": [ctypes.c_int, I64, I32, I32, I32, I32] + [P] * 16 + [SZ, P],
         "dflash2_selector_ce_backward": [ctypes.c_int, I64, I32, I32, I32, I32] + [P] * 16 + [P, SZ, P],
         "dflash2_decode_head": [ctypes.c_int, I32, I32, I32, I32, I32, I32] + [P] * 10 + [P, SZ, P],
         "dflash2_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
@@ -201,10 +201,20 @@ def unary_topk(h: torch.Tensor, w_lm: torch.Tensor, top_k: int, gold_ids: Option
 
 def unary_topk_ex(h: torch.Tensor, w_lm: torch.Tensor, top_k: int, gold_ids: Optional[torch.Tensor] = None,
                   output_multiplier: float = 1.0, softcap: float = 0.0, want_lse: bool = False,
-                  want_metrics: bool = False, workspace: Optional[torch.Tensor] = None):
+                  want_metrics: bool = False, workspace: Optional[torch.Tensor] = None,
+                  w_h: Optional[torch.Tensor] = None, g: Optional[torch.Tensor] = None):
     """unary_topk over softcap(output_multiplier * U).  -> (ids, vals, gold_logit or None, lse [N] or None,
-    gold_prob [N] or None, gold_hit [N] uint8 or None); the gold metrics need gold_ids and want_metrics."""
+    gold_prob [N] or None, gold_hit [N] uint8 or None); the gold metrics need gold_ids and want_metrics.
+    With w_h [r, H] and g [N, r] float32, g also receives the context projection h w_hᵀ."""
     _same_dtype(h, w_lm)
+    if (w_h is None) != (g is None):
+        raise ValueError("w_h and g come together")
+    r = 0
+    if w_h is not None:
+        _same_dtype(h, w_h)
+        r = w_h.shape[0]
+        if g.dtype != torch.float32 or tuple(g.shape) != (h.shape[0], r):
+            raise TypeError("g must be float32 [N, r]")
     N, H = h.shape
     V = w_lm.shape[0]
     dev = h.device
@@ -221,29 +231,53 @@ def unary_topk_ex(h: torch.Tensor, w_lm: torch.Tensor, top_k: int, gold_ids: Opt
     if workspace is None:
         workspace = make_workspace(OP_UNARY_TOPK, N, H, V, 0, top_k, dev)
     st = _lib.dflash2_unary_topk_ex(_dtype_code(h), N, H, V, top_k, _ptr(h), _ptr(w_lm), _ptr(gold_ids),
-                                    float(output_multiplier), float(softcap), _ptr(ids), _ptr(vals), _ptr(gl),
-                                    _ptr(lse), _ptr(prob), _ptr(hit), _ptr(workspace), workspace.numel(),
-                                    _stream(dev))
+                                    float(output_multiplier), float(softcap), _ptr(w_h), r, _ptr(ids), _ptr(vals),
+                                    _ptr(gl), _ptr(lse), _ptr(prob), _ptr(hit), _ptr(g), _ptr(workspace),
+                                    workspace.numel(), _stream(dev))
     _check(st, "dflash2_unary_topk_ex")
     return ids, vals, gl, lse, prob, hit
 
 
+def unary_topk_ctx(h: torch.Tensor, w_lm: torch.Tensor, top_k: int, w_h: torch.Tensor,
+                   gold_ids: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   g: Optional[torch.Tensor] = None):
+    """The unary top-K and the selector's context rows in one call (dflash2_unary_topk_ex with w_h).
+    -> (ids, vals, gold_logit or None, g [N, r] float32)."""
+    if g is None:
+        g = torch.empty((h.shape[0], w_h.shape[0]), dtype=torch.float32, device=h.device)
+    ids, vals, gl, _, _, _ = unary_topk_ex(h, w_lm, top_k, gold_ids=gold_ids, workspace=workspace, w_h=w_h, g=g)
+    return ids, vals, gl, g
+
+
+def _selector_shapes(h, w_h, g, cb_pred, cb_succ):
+    """(N, H) of the selector's rows; h and w_h may be None when the context rows g are given."""
+    _same_dtype(cb_pred, *[t for t in (h, w_h, cb_succ) if t is not None])
+    if g is not None:
+        if g.dtype != torch.float32 or g.dim() != 2 or g.shape[1] != cb_pred.shape[1]:
+            raise TypeError("g must be float32 [N, r]")
+        return g.shape[0], (h.shape[1] if h is not None else 64)
+    if h is None or w_h is None:
+        raise ValueError("h and w_h are needed without g")
+    return h.shape
+
+
 def selector_walk(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, block_size: int,
-                  workspace: Optional[torch.Tensor] = None, want_scores: bool = True):
-    """-> (path [n_blocks, bs] int32, path_score [n_blocks, bs] float32 or None)."""
-    _same_dtype(h, w_h, cb_pred, cb_succ)
+                  workspace: Optional[torch.Tensor] = None, want_scores: bool = True, g=None):
+    """-> (path [n_blocks, bs] int32, path_score [n_blocks, bs] float32 or None).  g: the context
+    rows formed beforehand (unary_topk_ctx), or None to form them from h and w_h."""
     _ids(cand_ids, "cand_ids")
     _ids(anchor_ids, "anchor_ids")
-    N, H = h.shape
+    N, H = _selector_shapes(h, w_h, g, cb_pred, cb_succ)
     V, r = cb_pred.shape
     K = cand_ids.shape[1]
     nb = anchor_ids.shape[0]
-    dev = h.device
+    dev = cb_pred.device
     path = torch.empty((nb, block_size), dtype=torch.int32, device=dev)
     ps = torch.empty((nb, block_size), dtype=torch.float32, device=dev) if want_scores else None
     if workspace is None:
         workspace = make_workspace(OP_SELECTOR_WALK, nb * block_size, H, V, r, K, dev)
-    st = _lib.dflash2_selector_walk(_dtype_code(h), nb, block_size, H, V, r, K, _ptr(h), _ptr(w_h), _ptr(cb_pred),
+    st = _lib.dflash2_selector_walk(_dtype_code(cb_pred), nb, block_size, H, V, r, K, _ptr(h), _ptr(w_h), _ptr(g),
+                                    _ptr(cb_pred),
                                     _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals), _ptr(anchor_ids), _ptr(path),
                                     _ptr(ps), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "dflash2_selector_walk")
@@ -252,25 +286,24 @@ def selector_walk(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, blo
 
 def selector_walk_noalloc(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, block_size: int,
                           path: Optional[torch.Tensor] = None, path_score: Optional[torch.Tensor] = None,
-                          want_scores: bool = True):
+                          want_scores: bool = True, g=None):
     """selector_walk without a workspace (the library's own device array; see
     dflash2_selector_walk_noalloc).  Outputs may be passed in, so that a
     caller that cannot allocate allocates nothing here either.
     -> (path [n_blocks, bs] int32, path_score [n_blocks, bs] float32 or None)."""
-    _same_dtype(h, w_h, cb_pred, cb_succ)
     _ids(cand_ids, "cand_ids")
     _ids(anchor_ids, "anchor_ids")
-    N, H = h.shape
+    N, H = _selector_shapes(h, w_h, g, cb_pred, cb_succ)
     V, r = cb_pred.shape
     K = cand_ids.shape[1]
     nb = anchor_ids.shape[0]
-    dev = h.device
+    dev = cb_pred.device
     if path is None:
         path = torch.empty((nb, block_size), dtype=torch.int32, device=dev)
     if path_score is None and want_scores:
         path_score = torch.empty((nb, block_size), dtype=torch.float32, device=dev)
-    st = _lib.dflash2_selector_walk_noalloc(_dtype_code(h), nb, block_size, H, V, r, K, _ptr(h), _ptr(w_h),
-                                            _ptr(cb_pred), _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals),
+    st = _lib.dflash2_selector_walk_noalloc(_dtype_code(cb_pred), nb, block_size, H, V, r, K, _ptr(h), _ptr(w_h),
+                                            _ptr(g), _ptr(cb_pred), _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals),
                                             _ptr(anchor_ids), _ptr(path), _ptr(path_score), _stream(dev))
     _check(st, "dflash2_selector_walk_noalloc")
     return path, path_score
@@ -278,22 +311,22 @@ def selector_walk_noalloc(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_
 
 def selector_sample(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, anchor_ids, block_size: int,
                     temperature: float = 1.0, seed: int = 0, workspace: Optional[torch.Tensor] = None,
-                    want_scores: bool = True):
+                    want_scores: bool = True, g=None):
     """-> (path [n_blocks, bs] int32, path_score [n_blocks, bs] float32 or None), the
     path drawn from softmax(S / temperature) with the counter-based generator keyed by seed."""
-    _same_dtype(h, w_h, cb_pred, cb_succ)
     _ids(cand_ids, "cand_ids")
     _ids(anchor_ids, "anchor_ids")
-    N, H = h.shape
+    N, H = _selector_shapes(h, w_h, g, cb_pred, cb_succ)
     V, r = cb_pred.shape
     K = cand_ids.shape[1]
     nb = anchor_ids.shape[0]
-    dev = h.device
+    dev = cb_pred.device
     path = torch.empty((nb, block_size), dtype=torch.int32, device=dev)
     ps = torch.empty((nb, block_size), dtype=torch.float32, device=dev) if want_scores else None
     if workspace is None:
         workspace = make_workspace(OP_SELECTOR_WALK, nb * block_size, H, V, r, K, dev)
-    st = _lib.dflash2_selector_sample(_dtype_code(h), nb, block_size, H, V, r, K, _ptr(h), _ptr(w_h), _ptr(cb_pred),
+    st = _lib.dflash2_selector_sample(_dtype_code(cb_pred), nb, block_size, H, V, r, K, _ptr(h), _ptr(w_h), _ptr(g),
+                                      _ptr(cb_pred),
                                       _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals), _ptr(anchor_ids),
                                       float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(path), _ptr(ps),
                                       _ptr(workspace), workspace.numel(), _stream(dev))
@@ -338,15 +371,14 @@ def decode_head(h, w_lm, top_k: int, w_h=None, cb_pred=None, cb_succ=None, ancho
 
 
 def selector_score_tf(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, pred_ids, gold_ids=None, force=None,
-                      gold_logit=None, workspace: Optional[torch.Tensor] = None):
+                      gold_logit=None, workspace: Optional[torch.Tensor] = None, g=None):
     """-> (scores [N, K] float32, best_ids [N] int32, ce [N] float32 or None, valid [N] uint8 or None)."""
-    _same_dtype(h, w_h, cb_pred, cb_succ)
     _ids(cand_ids, "cand_ids")
     _ids(pred_ids, "pred_ids")
-    N, H = h.shape
+    N, H = _selector_shapes(h, w_h, g, cb_pred, cb_succ)
     V, r = cb_pred.shape
     K = cand_ids.shape[1]
-    dev = h.device
+    dev = cb_pred.device
     scores = torch.empty((N, K), dtype=torch.float32, device=dev)
     best = torch.empty(N, dtype=torch.int32, device=dev)
     ce = valid = None
@@ -358,7 +390,8 @@ def selector_score_tf(h, w_h, cb_pred, cb_succ, cand_ids, cand_vals, pred_ids, g
         raise TypeError("force must be uint8")
     if workspace is None:
         workspace = make_workspace(OP_SELECTOR_TF, N, H, V, r, K, dev)
-    st = _lib.dflash2_selector_score_tf(_dtype_code(h), N, H, V, r, K, _ptr(h), _ptr(w_h), _ptr(cb_pred),
+    st = _lib.dflash2_selector_score_tf(_dtype_code(cb_pred), N, H, V, r, K, _ptr(h), _ptr(w_h), _ptr(g),
+                                        _ptr(cb_pred),
                                         _ptr(cb_succ), _ptr(cand_ids), _ptr(cand_vals), _ptr(pred_ids),
                                         _ptr(gold_ids), _ptr(force), _ptr(gold_logit), _ptr(scores), _ptr(best),
                                         _ptr(ce), _ptr(valid), _ptr(workspace), workspace.numel(), _stream(dev))

@@ -169,16 +169,27 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
  *   (DFLASH2_ERR_SHAPE otherwise).  Asking for out_lse or out_gold_prob
  *   adds a sum of exponentials to every logit tile (about a fifth more time
  *   on many bf16 rows, a few percent at decode sizes); without them the
- *   kernels are those of dflash2_unary_topk.  Outputs must not overlap each
- *   other or the workspace.  Workspace: that of DFLASH2_OP_UNARY_TOPK.  Other
- *   rules as dflash2_unary_topk.
+ *   kernels are those of dflash2_unary_topk.
+ *   w_h [rank, H] dtype and out_g [N, rank] float32, both or neither: the
+ *   selector's context projection g = h w_hᵀ of the same rows ([verl PR]
+ *   "What DFlash2 adds", H(h)), for dflash2_selector_walk, _sample and
+ *   _score_tf to take as their g.  On the many-row bf16 path its weight rows
+ *   stream through the LM-head kernel after the vocabulary's, as extra
+ *   tiles, so the selector adds no pass over h of its own; elsewhere it is
+ *   one more launch (the sums may round in another order than the selector
+ *   calls' own projection: float32 over H products either way).
+ *   rank >= 1 (DFLASH2_ERR_SHAPE), a multiple of 8 and at
+ *   most DFLASH2_MAX_RANK (DFLASH2_ERR_UNSUPPORTED) when out_g is given.
+ *   Outputs must not overlap each other, the workspace or any input.
+ *   Workspace: that of DFLASH2_OP_UNARY_TOPK.  Other rules as
+ *   dflash2_unary_topk.
  */
 dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, int32_t vocab, int32_t top_k,
                                      const void *h, const void *w_lm, const int32_t *gold_ids,
-                                     float output_multiplier, float final_logit_softcapping, int32_t *out_ids,
-                                     float *out_vals, float *out_gold_logit, float *out_lse, float *out_gold_prob,
-                                     uint8_t *out_gold_hit, void *workspace, size_t workspace_bytes,
-                                     void *stream);
+                                     float output_multiplier, float final_logit_softcapping, const void *w_h,
+                                     int32_t rank, int32_t *out_ids, float *out_vals, float *out_gold_logit,
+                                     float *out_lse, float *out_gold_prob, uint8_t *out_gold_hit, float *out_g,
+                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Greedy selector walk per anchor block ([verl PR] "What DFlash2 adds",
@@ -199,6 +210,9 @@ dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, 
  *   n_blocks, block_size (<= 64), hidden H, vocab V, rank r (multiple of 8, <= 4096),
  *   top_k K (<= 64)
  *   h [N, H] dtype (N = n_blocks*bs); w_h [r, H] dtype
+ *   g [N, r] float32 or NULL: the context rows formed beforehand (the out_g of
+ *   dflash2_unary_topk_ex); then h and w_h are not read and may be NULL, and
+ *   no projection runs.  Without g, h and w_h are required (DFLASH2_ERR_NULL).
  *   cb_pred, cb_succ [V, r] dtype; cand_ids [N, K] int32; cand_vals [N, K] float32
  *   anchor_ids [n_blocks] int32
  *   out_path [n_blocks, bs] int32; out_path_score [n_blocks, bs] float32 or NULL
@@ -206,7 +220,7 @@ dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, 
  */
 dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_size,
                                      int32_t hidden, int32_t vocab, int32_t rank, int32_t top_k,
-                                     const void *h, const void *w_h, const void *cb_pred,
+                                     const void *h, const void *w_h, const float *g, const void *cb_pred,
                                      const void *cb_succ, const int32_t *cand_ids,
                                      const float *cand_vals, const int32_t *anchor_ids,
                                      int32_t *out_path, float *out_path_score, void *workspace,
@@ -229,7 +243,8 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
 #define DFLASH2_NOALLOC_SCRATCH_BYTES (8u * 1024u * 1024u + 256u)
 dflash2_status dflash2_selector_walk_noalloc(int dtype, int32_t n_blocks, int32_t block_size,
                                              int32_t hidden, int32_t vocab, int32_t rank, int32_t top_k,
-                                             const void *h, const void *w_h, const void *cb_pred,
+                                             const void *h, const void *w_h, const float *g,
+                                             const void *cb_pred,
                                              const void *cb_succ, const int32_t *cand_ids,
                                              const float *cand_vals, const int32_t *anchor_ids,
                                              int32_t *out_path, float *out_path_score, void *stream);
@@ -252,7 +267,7 @@ dflash2_status dflash2_selector_walk_noalloc(int dtype, int32_t n_blocks, int32_
  */
 dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t block_size,
                                        int32_t hidden, int32_t vocab, int32_t rank, int32_t top_k,
-                                       const void *h, const void *w_h, const void *cb_pred,
+                                       const void *h, const void *w_h, const float *g, const void *cb_pred,
                                        const void *cb_succ, const int32_t *cand_ids,
                                        const float *cand_vals, const int32_t *anchor_ids,
                                        float temperature, uint64_t seed, int32_t *out_path,
@@ -303,6 +318,8 @@ dflash2_status dflash2_decode_head(int dtype, int32_t n_blocks, int32_t block_si
  * S'[n, gold] for valid rows, 0 otherwise; out_valid[n] in {0, 1}.
  *
  *   h [N, H], w_h [r, H], cb_pred/cb_succ [V, r]: dtype
+ *   g [N, r] float32 or NULL: precomputed context rows, as in
+ *   dflash2_selector_walk (then h and w_h may be NULL)
  *   cand_ids [N, K] int32, cand_vals [N, K] float32, pred_ids [N] int32
  *   gold_ids [N] int32 or NULL; force [N] uint8 or NULL (needs gold_ids);
  *   gold_logit [N] float32, required when force is given
@@ -311,7 +328,8 @@ dflash2_status dflash2_decode_head(int dtype, int32_t n_blocks, int32_t block_si
  */
 dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidden,
                                          int32_t vocab, int32_t rank, int32_t top_k,
-                                         const void *h, const void *w_h, const void *cb_pred,
+                                         const void *h, const void *w_h, const float *g,
+                                         const void *cb_pred,
                                          const void *cb_succ, const int32_t *cand_ids,
                                          const float *cand_vals, const int32_t *pred_ids,
                                          const int32_t *gold_ids, const uint8_t *force,

@@ -124,6 +124,23 @@ def close(gpu, ref, rtol=RTOL, atol=ATOL) -> np.ndarray:
     return np.abs(gpu - ref) <= atol + rtol * np.abs(ref)
 
 
+def scale_codebooks(inp, r, dtype):
+    """Larger codebooks, so that the pair term overrides the unary pick on
+    20-50 % of the steps against the N(0, 1) candidate logits (x6 at rank <= 64
+    and in float32, x3 above): both terms then decide picks."""
+    s = 6 if dtype == "f32" or r <= 64 else 3
+    for k in ("cb_pred", "cb_succ"):
+        inp[k] = inp[k] * np.float32(s) if dtype == "f32" else O.round_bf16(O.widen(inp[k], "bf16") * s)
+
+
+def context_ok(gpu_g, h, w_h, dtype: str) -> np.ndarray:
+    """The float32 context rows g = h W_Hᵀ (a sum of H products each) within
+    CORR_ULPS ulps of the sum of their magnitudes, as the conv corrections."""
+    exact = O.context_projection(h, w_h, dtype)
+    absum = np.abs(O.widen(h, dtype)) @ np.abs(O.widen(w_h, dtype)).T
+    return np.abs(np.asarray(gpu_g, np.float64) - exact) <= CORR_ULPS * 2.0 ** -24 * absum
+
+
 def oracle_logits_rows(h: np.ndarray, w_lm: np.ndarray, dtype: str, chunk: int = 16384) -> np.ndarray:
     """The oracle's exact logits for a few rows, vocabulary chunk by chunk
     (keeps the float64 copy of a large LM head out of memory)."""

@@ -116,11 +116,11 @@ def test_unary_topk_rules():
 
 
 def topk_ex(dtype=1, n=8, h=256, v=4096, k=16, hp=fake(0), w=fake(1), gold=None, mult=1.0, cap=0.0, ids=fake(2),
-            vals=fake(3), gl=None, lse=None, prob=None, hit=None, ws=fake(4), wsb=None):
+            vals=fake(3), gl=None, lse=None, prob=None, hit=None, ws=fake(4), wsb=None, wh=None, r=0, g=None):
     if wsb is None:
         wsb = D.workspace_bytes(D.OP_UNARY_TOPK, n, h, v, 0, k) if n > 0 else 1 << 20
-    return L.dflash2_unary_topk_ex(dtype, n, h, v, k, hp, w, gold, mult, cap, ids, vals, gl, lse, prob, hit, ws, wsb,
-                                   None)
+    return L.dflash2_unary_topk_ex(dtype, n, h, v, k, hp, w, gold, mult, cap, wh, r, ids, vals, gl, lse, prob, hit, g,
+                                   ws, wsb, None)
 
 
 @no_gpu
@@ -140,12 +140,25 @@ def test_unary_topk_ex_rules():
     assert topk_ex(lse=fake(3)) == ALIAS and topk_ex(gold=fake(5), gl=fake(6), hit=fake(6)) == ALIAS
     assert topk_ex(lse=fake(4)) == ALIAS
     assert topk_ex(lse=fake(0)) == ALIAS and topk_ex(gold=fake(5), gl=fake(6), prob=fake(5)) == ALIAS
+    # the context rows: W_H and g together, a rank the selector supports
+    assert topk_ex(wh=fake(8), r=32) == NULL and topk_ex(g=fake(9), r=32) == NULL
+    ctx = dict(wh=fake(8), r=32, g=fake(9))
+    assert topk_ex(**{**ctx, "r": 0}) == SHAPE
+    assert topk_ex(**{**ctx, "r": 12}) == UNSUP and topk_ex(**{**ctx, "r": 4104}) == UNSUP
+    assert topk_ex(**ctx, mult=0.0) == SHAPE             # the other rules still hold
+    assert topk_ex(**{**ctx, "g": fake(3)}) == ALIAS      # g over the values
+    assert topk_ex(**{**ctx, "g": fake(4)}) == ALIAS      # over the workspace
+    assert topk_ex(**{**ctx, "g": fake(8)}) == ALIAS      # over W_H
+    assert topk_ex(**{**ctx, "g": fake(0)}) == ALIAS      # over h
+    assert topk_ex(**{**ctx, "ids": fake(8)}) == ALIAS    # an output over W_H
+    # without g the rank is not read
+    assert topk_ex(r=12) == topk_ex(r=-5) == topk_ex()
 
-
-def walk(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, ws=fake(9), wsb=None, path=fake(7), anchors=fake(6), ps=None):
+def walk(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, ws=fake(9), wsb=None, path=fake(7), anchors=fake(6), ps=None,
+         hp=fake(0), wh=fake(1), g=None):
     if wsb is None:
         wsb = D.workspace_bytes(D.OP_SELECTOR_WALK, nb * bs, h, v, r, k) if nb * bs > 0 else 1 << 20
-    return L.dflash2_selector_walk(dtype, nb, bs, h, v, r, k, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+    return L.dflash2_selector_walk(dtype, nb, bs, h, v, r, k, hp, wh, g, fake(2), fake(3), fake(4), fake(5),
                                    anchors, path, ps, ws, wsb, None)
 
 
@@ -162,10 +175,17 @@ def test_selector_walk_rules():
     # outputs and workspace overlap no input: candidate ids, values, anchors, codebooks
     assert walk(path=fake(4)) == ALIAS and walk(ps=fake(5)) == ALIAS
     assert walk(path=fake(6)) == ALIAS and walk(ws=fake(2)) == ALIAS and walk(ps=fake(0)) == ALIAS
+    # precomputed context rows stand in for h and W_H; without them both are needed
+    assert walk(hp=None) == NULL and walk(wh=None) == NULL and walk(hp=None, wh=None) == NULL
+    rows = walk(hp=None, wh=None, g=fake(11))
+    assert rows not in (NULL, ALIAS, SHAPE, UNSUP) and walk(g=fake(11)) == rows
+    assert walk(hp=None, wh=None, g=fake(11), path=fake(11)) == ALIAS  # an output over g
+    assert walk(hp=None, wh=None, g=fake(11), ws=fake(11)) == ALIAS    # the workspace over g
+    assert walk(hp=None, wh=None, g=fake(7)) == ALIAS                  # g under the path
 
-
-def walk_na(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, path=fake(10), ps=None, anchors=fake(6)):
-    return L.dflash2_selector_walk_noalloc(dtype, nb, bs, h, v, r, k, fake(0), fake(1), fake(2), fake(3), fake(4),
+def walk_na(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, path=fake(10), ps=None, anchors=fake(6), hp=fake(0),
+            wh=fake(1), g=None):
+    return L.dflash2_selector_walk_noalloc(dtype, nb, bs, h, v, r, k, hp, wh, g, fake(2), fake(3), fake(4),
                                            fake(5), anchors, path, ps, None)
 
 
@@ -182,7 +202,7 @@ def test_selector_walk_noalloc_rules():
     assert walk_na(path=None) == NULL and walk_na(anchors=None) == NULL
     assert walk_na(ps=fake(10)) == ALIAS
     assert walk_na(path=fake(4)) == ALIAS and walk_na(ps=fake(6)) == ALIAS and walk_na(path=fake(3)) == ALIAS
-
+    assert walk_na(hp=None) == NULL and walk_na(hp=None, wh=None, g=fake(11), path=fake(11)) == ALIAS
 
 def dhead(dtype=1, nb=1, bs=8, h=512, v=1000, r=32, k=16, wh=fake(2), A=fake(3), B=fake(4), anchors=fake(5),
           ids=fake(10), vals=fake(11), path=fake(12), ps=None, ws=fake(20), wsb=None):
@@ -215,10 +235,10 @@ def test_decode_head_rules():
 
 
 def sample(dtype=1, nb=2, bs=8, h=256, v=1000, r=32, k=16, temp=1.0, path=fake(10), ps=None, anchors=fake(6),
-           ws=fake(12), wsb=None):
+           ws=fake(12), wsb=None, hp=fake(0), wh=fake(1), g=None):
     if wsb is None:
         wsb = D.workspace_bytes(D.OP_SELECTOR_WALK, max(nb * bs, 1), h, v, r, k) if nb > 0 else 1 << 20
-    return L.dflash2_selector_sample(dtype, nb, bs, h, v, r, k, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+    return L.dflash2_selector_sample(dtype, nb, bs, h, v, r, k, hp, wh, g, fake(2), fake(3), fake(4), fake(5),
                                      anchors, temp, 0x1234, path, ps, ws, wsb, None)
 
 
@@ -233,13 +253,13 @@ def test_selector_sample_rules():
     assert sample(wsb=100) == WS
     assert sample(ps=fake(10)) == ALIAS
     assert sample(path=fake(5)) == ALIAS and sample(ps=fake(4)) == ALIAS and sample(ws=fake(6)) == ALIAS
-
+    assert sample(wh=None) == NULL and sample(hp=None, wh=None, g=fake(11), ws=fake(11)) == ALIAS
 
 def tf(dtype=1, n=16, h=256, v=1000, r=32, k=16, gold=None, force=None, gl=None, ce=None, valid=None, ws=fake(12),
-       wsb=None, scores=fake(13), best=fake(14)):
+       wsb=None, scores=fake(13), best=fake(14), hp=fake(0), wh=fake(1), g=None):
     if wsb is None:
         wsb = D.workspace_bytes(D.OP_SELECTOR_TF, n, h, v, r, k) if n > 0 else 1 << 20
-    return L.dflash2_selector_score_tf(dtype, n, h, v, r, k, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+    return L.dflash2_selector_score_tf(dtype, n, h, v, r, k, hp, wh, g, fake(2), fake(3), fake(4), fake(5),
                                        fake(6), gold, force, gl, scores, best, ce, valid, ws, wsb, None)
 
 
@@ -258,7 +278,9 @@ def test_selector_tf_rules():
     assert tf(**{**full, "valid": fake(8)}) == ALIAS   # valid over force
     assert tf(**{**full, "ce": fake(9)}) == ALIAS      # ce over the gold logits
     assert tf(**{**full, "ce": fake(7)}) == ALIAS      # ce over the gold ids
-
+    assert tf(hp=None) == NULL and tf(hp=None, wh=None, g=fake(15)) not in (NULL, ALIAS)
+    assert tf(hp=None, wh=None, g=fake(15), scores=fake(15)) == ALIAS  # scores over g
+    assert tf(g=fake(15), best=fake(15)) == ALIAS                      # with h and W_H given too
 
 def bwd(dtype=1, n=16, h=256, v=1000, r=32, k=16, gold=fake(7), force=None, gl=None, gce=fake(9), gp=fake(20),
         gs=fake(40), gw=fake(60), ce=None, valid=None, ws=fake(12), wsb=None, hp=fake(0)):

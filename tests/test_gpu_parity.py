@@ -9,7 +9,7 @@ import torch
 from block_draft_head_amd.inputs import Workload, make_inputs, to_storage
 from oracle import dflash2_oracle as O
 from tests.helpers import (act_ok, close, compare_grads, compare_sample, compare_tf, compare_topk, compare_walk, conv_delta,
-                           corr_abs, corr_ok, to_dev, to_np)
+                           corr_abs, corr_ok, scale_codebooks, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -326,15 +326,6 @@ WALK_CASES = [
     (128, 8, 256, 3000, 512, 20, "bf16"), (130, 4, 256, 2000, 40, 64, "bf16"), (200, 2, 256, 500, 256, 1, "bf16"),
     (129, 16, 256, 4000, 1024, 33, "bf16"),
 ]
-
-
-def scale_codebooks(inp, r, dtype):
-    """Larger codebooks, so that the pair term overrides the unary pick on
-    20-50 % of the steps against the N(0, 1) candidate logits (x6 at rank <= 64
-    and in float32, x3 above): both terms then decide picks."""
-    s = 6 if dtype == "f32" or r <= 64 else 3
-    for k in ("cb_pred", "cb_succ"):
-        inp[k] = inp[k] * np.float32(s) if dtype == "f32" else O.round_bf16(O.widen(inp[k], "bf16") * s)
 
 
 @pytest.mark.parametrize("nb,bs,H,V,r,K,dtype", WALK_CASES)

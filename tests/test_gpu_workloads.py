@@ -14,9 +14,12 @@ checked on what it can compute one by one:
   and one random row of every 256-row tile (the many-row kernel's row tile).
   Every checked row's list is merged from every vocabulary slab's partial
   list, so each slab takes part in every checked row;
-* the selector on every block / row, the oracle fed the GPU's candidate ids
-  with its own exact logits for them (stage-wise, so a top-K near-tie cannot
-  cascade); the walks must override the unary pick somewhere.
+* outside the decode head, the context rows that the LM head's call forms
+  (every element, within the float32 bound of tests/helpers.py);
+* the selector on every block / row, fed those rows, the oracle fed the
+  GPU's candidate ids with its own exact logits for them and its own exact
+  context rows (stage-wise, so a top-K near-tie cannot cascade); the walks
+  must override the unary pick somewhere.
 """
 import numpy as np
 import pytest
@@ -24,8 +27,8 @@ import torch
 
 from block_draft_head_amd.inputs import WORKLOAD_ORDER, WORKLOADS, make_inputs
 from oracle import dflash2_oracle as O
-from tests.helpers import (act_ok, close, compare_grads, compare_tf, compare_topk, compare_walk, conv_delta, corr_abs,
-                           corr_ok, oracle_logits_rows, to_dev, to_np)
+from tests.helpers import (act_ok, close, compare_grads, compare_tf, compare_topk, compare_walk, context_ok, conv_delta,
+                           corr_abs, corr_ok, oracle_logits_rows, to_dev, to_np)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -113,8 +116,9 @@ def test_full_size_workload(D, name):
                                             dev["anchors"], bs, workspace=ws)
         gl = None
     else:
+        # the context rows formed in the LM head's call, as bench.py does
         ws = D.make_workspace(D.OP_UNARY_TOPK, N, H, V, 0, K, "cuda")
-        ids, vals, gl = D.unary_topk(dev["h"], dev["w_lm"], K, gold_ids=gold, workspace=ws)
+        ids, vals, gl, g = D.unary_topk_ctx(dev["h"], dev["w_lm"], K, dev["w_h"], gold_ids=gold, workspace=ws)
     assert D.read_device_status(ws) == 0
     gids, gvals = to_np(ids), to_np(vals)
     srows = tile_rows(N, rng)
@@ -130,12 +134,15 @@ def test_full_size_workload(D, name):
     log(f"[{name}] selector")
     u_at = O.logits_at(inp["h"], inp["w_lm"], gids, dt)
     g64 = O.context_projection(inp["h"], inp["w_h"], dt)
+    if not fused:
+        ok = context_ok(to_np(g), inp["h"], inp["w_h"], dt)
+        assert ok.all(), f"context rows: {(~ok).sum()} outside the bound, first at {np.argwhere(~ok)[:3]}"
     if tf_mode:
         gold_exact = O.logits_at(inp["h"], inp["w_lm"], inp["gold"][:, None], dt)[:, 0]
         assert close(to_np(gl), gold_exact).all(), "gold logit differs"
         ws_sel = D.make_workspace(D.OP_SELECTOR_TF, N, H, V, r, K, "cuda")
-        res = D.selector_score_tf(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"],
-                                  gold_ids=gold, force=dev["force"], gold_logit=gl, workspace=ws_sel)
+        res = D.selector_score_tf(None, None, dev["cb_pred"], dev["cb_succ"], ids, vals, dev["pred"], gold_ids=gold,
+                                  force=dev["force"], gold_logit=gl, workspace=ws_sel, g=g)
         gpu = tuple(to_np(t) for t in res)
         ref = O.selector_score_tf(g64, inp["cb_pred"], inp["cb_succ"], gids, u_at, inp["pred"], dt,
                                   gold_ids=inp["gold"], force=inp["force"], gold_logit=gold_exact)
@@ -164,8 +171,8 @@ def test_full_size_workload(D, name):
     else:
         if not fused:
             ws_sel = D.make_workspace(D.OP_SELECTOR_WALK, N, H, V, r, K, "cuda")
-            path, ps = D.selector_walk(dev["h"], dev["w_h"], dev["cb_pred"], dev["cb_succ"], ids, vals,
-                                       dev["anchors"], bs, workspace=ws_sel)
+            path, ps = D.selector_walk(None, None, dev["cb_pred"], dev["cb_succ"], ids, vals, dev["anchors"], bs,
+                                       workspace=ws_sel, g=g)
             assert D.read_device_status(ws_sel) == 0
         fails, flags, teeth, msgs = compare_walk(to_np(path), to_np(ps), g64, inp["cb_pred"], inp["cb_succ"], gids,
                                                  u_at, inp["anchors"], bs, dt)

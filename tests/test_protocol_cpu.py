@@ -3,7 +3,7 @@ import numpy as np
 
 from oracle import dflash2_oracle as O
 from block_draft_head_amd.inputs import WORKLOADS, make_inputs
-from tests.helpers import CORR_ULPS, act_ok, bf16_bracketed, compare_topk, conv_delta, corr_abs
+from tests.helpers import CORR_ULPS, act_ok, bf16_bracketed, compare_topk, context_ok, conv_delta, corr_abs
 
 
 def test_bf16_bracket_accepts_both_neighbours_and_nothing_else():
@@ -105,3 +105,20 @@ def test_conv_rule_fails_a_shifted_tap():
     ok = act_ok(O.round_bf16(bad), ex, "bf16", delta)
     tapped = np.array([n % bs >= 1 for n in range(2 * bs)])
     assert (~ok[tapped]).mean() > 0.9 and ok[~tapped].all()
+
+
+def test_context_rule_accepts_a_float32_product_and_fails_a_dropped_term():
+    """The float32 product h W_Hᵀ passes the context-row bound at H 5120; the
+    same product with one of its H terms dropped (one column of W_H zeroed)
+    fails it on nearly every element, and so does the product through a W_H
+    whose rows are off by one."""
+    rng = np.random.default_rng(3)
+    N, H, r = 64, 5120, 48
+    h = O.round_bf16(rng.standard_normal((N, H)))
+    w_h = O.round_bf16(rng.standard_normal((r, H)) * 0.02)
+    x32, w32 = O.widen(h, "bf16").astype(np.float32), O.widen(w_h, "bf16").astype(np.float32)
+    assert context_ok(x32 @ w32.T, h, w_h, "bf16").all()
+    dropped = w32.copy()
+    dropped[:, 1234] = 0.0
+    assert (~context_ok(x32 @ dropped.T, h, w_h, "bf16")).mean() > 0.9
+    assert not context_ok(x32 @ np.roll(w32, 1, axis=0).T, h, w_h, "bf16").any()
