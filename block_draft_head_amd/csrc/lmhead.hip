@@ -784,11 +784,14 @@ __global__ __launch_bounds__(256) void lmhead_tiled_kernel(
 // After a tile, every lane compares its accumulators with their rows'
 // thresholds and appends each logit at or above one to that row's LDS slots;
 // the owners then insert their slots into their lists and raise their
-// thresholds.  A slab's first tile (no thresholds yet), and a tile in which
-// some row's hits overflow its slots, take the exact path instead: the tile's
-// logits go to a per-workgroup buffer in the workspace and each owner scans
-// its whole row there.  Insertion keeps the exact top-KL under the key order,
-// so the result does not depend on the tiling or on which path a tile took.
+// thresholds.  A slab's first tile has no thresholds yet: for KL <= 16 each
+// row takes as its threshold the KL-th largest of its 64 lane maxima (see
+// lane_max_bound), else the tile takes the exact path.  On the exact path the
+// tile's logits go to a per-workgroup buffer in the workspace and an owner
+// scans its whole row there; when the tile was also scanned, only the rows
+// whose hits overflowed their slots do (the others take their slots).
+// Insertion keeps the exact top-KL under the key order, so the result does
+// not depend on the tiling or on which path a tile took.
 constexpr int kRowCand = 32;        // candidate slots per tile row (over the second stage buffer)
 constexpr int kCandPerThread = 16;  // exact path: buffers merged once one holds more (16 more land per step)
 constexpr int kCandStride = kCandPerThread + 16;
@@ -796,6 +799,7 @@ constexpr size_t kBigTileFloats = (size_t)big::BM * big::BN;  // exact path buff
 static_assert(big::BM * kRowCand * 8 <= big::STAGE, "candidate slots over one stage buffer");
 static_assert(big::NT * 64 * 4 <= big::STAGE, "register-scan scratch over one stage buffer");
 static_assert(big::NT * kCandStride * 8 <= big::STAGE, "exact-path buffers over one stage buffer");
+static_assert(64 * big::BM * 4 <= big::STAGE, "lane maxima over one stage buffer");
 
 // (row tile, slab) of workgroup `bid`: the workgroups of one XCD (bid % 8)
 // take a block of up to 4 row tiles x consecutive slabs, so they share the
@@ -905,6 +909,57 @@ __device__ __forceinline__ void register_lse(const big::f32x16 (&acc)[4][4], con
         __builtin_amdgcn_sched_barrier(0);
     }
     if (far) *ovf = 1u;
+}
+
+// Thresholds from the tile itself, for a slab's first tiles.  A tile row's
+// 256 logits sit in 64 lanes (32 columns in each of two waves) holding 4 each;
+// the KL-th largest of the row's 64 lane maxima is reached by at least KL
+// distinct logits of the row (the lanes' own maxima), so it is at most the
+// KL-th largest logit of the row's list and this tile together, and the
+// larger of it and the row's threshold is still a threshold.  For KL <= 16
+// about KL + 4 logits of the tile reach it on average and almost never more
+// than the row's kRowCand slots: the register scan can take the first tile
+// (no list yet), and with it the second, where the row's threshold alone
+// lets about KL logits through and some row of 256 overflows its slots in
+// most slabs.  The maxima meet in LDS (lm, 64 slots x 256 rows, a row's
+// group of 4 at a slot moved by 4 (slot mod 16) rows so that the owners'
+// reads hit distinct banks); the owner of row t forms its bound with a max /
+// min network.  Rows past M keep +inf.  Ends with a barrier: thr is set and
+// lm is free again.
+template <int KL>
+__device__ __forceinline__ void lane_max_bound(const big::f32x16 (&acc)[4][4], float *lm, float *thr, bool my_ok) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+    const int slot = wn * 32 + (lane & 31), sw = 4 * (slot & 15);
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float m[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * g + e;
+                m[e] = fmaxf(fmaxf(agpr_read(acc[tm][0][i]), agpr_read(acc[tm][1][i])),
+                             fmaxf(agpr_read(acc[tm][2][i]), agpr_read(acc[tm][3][i])));
+            }
+            const int rb = big::acc_row(wm, tm, 4 * g, lane);  // rows rb .. rb + 3 (rb % 4 == 0)
+            *reinterpret_cast<float4 *>(lm + slot * big::BM + (rb ^ sw)) = make_float4(m[0], m[1], m[2], m[3]);
+        }
+    __syncthreads();
+    float top[KL];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) top[j] = -__builtin_inff();
+#pragma unroll 8
+    for (int s = 0; s < 64; ++s) {
+        float m = lm[s * big::BM + (t ^ (4 * (s & 15)))];
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+            const float hi = fmaxf(top[j], m);
+            m = fminf(top[j], m);
+            top[j] = hi;
+        }
+    }
+    if (my_ok) thr[t] = fmaxf(thr[t], top[KL - 1]);
+    __syncthreads();
 }
 
 __device__ __forceinline__ void register_scan(const big::f32x16 (&acc)[4][4], const float *thr, uint32_t *cnt,
@@ -1107,7 +1162,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // first or follows a tile that overflowed; an overflow in a tile that was
     // not stored drops its slots and forms the tile again, stored.  So no
     // accumulator is live past the register scan.
-    bool store = true;
+    // the register scan takes a slab's first tile (and with KL = 16 its
+    // second) with thresholds raised by lane_max_bound; else the first tiles
+    // are stored for the exact path
+    constexpr bool kBoundFirst = !LSE && KL <= 16;
+    bool store = !kBoundFirst;
     int pass = 0;  // parity of the overflow flag: per pass, a tile formed twice takes two
     // short lists live in their owner's registers between tiles (written to
     // the workspace around exact-path tiles and at the end)
@@ -1152,7 +1211,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // next, and a tile in which any of its 256 rows overflows the 32
         // slots would be formed twice, so the register scan starts once
         // that expectation is down to 16.
-        const bool scan = !fresh && v0 + BN <= V && (vt - vt0) * 16 >= KL;
+        const bool bound = kBoundFirst && !store && v0 + BN <= V && (fresh || (KL == 16 && vt - vt0 == 1));
+        const bool scan = bound || (!fresh && v0 + BN <= V && (vt - vt0) * 16 >= KL);
         store = store || !scan;
         f32x16 acc[4][4];
         mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H, prefilled);
@@ -1178,7 +1238,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
         }
         bool over = true;
+        uint32_t n_hits = 0;  // this row's hits in the scan (slots hold them all up to kRowCand)
         if (scan) {
+            if (bound) lane_max_bound<KL>(acc, reinterpret_cast<float *>(st0), thr, my_ok);
             // the idle stage buffers hold the scan's scratch
             register_scan(acc, thr, cnt, slots, &ovf[par], reinterpret_cast<float *>(st0), v0);
             if constexpr (LSE) register_lse(acc, lse_m, lse_t, &ovf[par], ue.mult, ue.cap);
@@ -1186,6 +1248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             over = ovf[par] != 0u;
             if (t == 0) ovf[par ^ 1] = 0u;  // last read a pass ago; next written a pass from now
             const uint32_t n = cnt[t];
+            n_hits = n;
             cnt[t] = 0u;
             if constexpr (LSE) {
                 // the tile's share, relative to the same shift; dropped if the
@@ -1222,8 +1285,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             continue;
         }
         if (store) {
-            // exact path over the stored tile (the slots, if any, are dropped)
-            if (my_ok) {
+            // exact path over the stored tile: every row when the tile was not
+            // scanned (or with the log-sum-exp, whose tile share was dropped),
+            // else only the rows whose hits overflowed their slots, the others
+            // inserting their slots as above
+            if (kBoundFirst && scan && n_hits <= (uint32_t)kRowCand) {
+                if (my_ok && n_hits) {
+                    if constexpr (kRegList) {
+                        for (uint32_t i = 0; i < n_hits; ++i) list_insert<KL>(RL, slots[t * kRowCand + i]);
+                        thr[t] = RL[KL - 1] ? key_val(RL[KL - 1]) : -__builtin_inff();
+                    } else {
+                        uint64_t L[KL];
+                        load_list<KL>(L, my_list);
+                        for (uint32_t i = 0; i < n_hits; ++i) list_insert<KL>(L, slots[t * kRowCand + i]);
+                        store_list<KL>(L, my_list);
+                        thr[t] = L[KL - 1] ? key_val(L[KL - 1]) : -__builtin_inff();
+                    }
+                }
+            } else if (my_ok) {
                 if constexpr (kRegList) {
                     if (!fresh) store_list<KL>(RL, my_list);
                 }
