@@ -5,10 +5,14 @@ input, inputs resident in HBM:
   walk workloads:  conv prepare + conv finish (one wrapped sublayer), the unary
                    LM-head top-K and the greedy walk (at most 8 rows, bf16:
                    dflash2_decode_head, whose LM-head kernel also streams the
-                   context projection's rows; else unary top-K, then context
-                   projection + walk);
-  packed TF:       the same conv, unary top-K with gold logits, context
-                   projection + teacher-forced scores and K-way CE.
+                   context projection's rows; else the unary top-K whose
+                   call also forms the context rows, W_H tiles on the
+                   many-row kernel's stream (`--context-rows selector`: the
+                   selector call forms them), then the walk);
+  packed TF:       the same conv, unary top-K with gold logits and the
+                   context rows, teacher-forced scores and K-way CE.
+The context rows' share of the LM-head op is reported beside it
+(`context_rows_ms`: the op with W_H minus the same op without).
 
 Timing.  Every timed step is preceded, outside its events, by a 512 MiB write
 that evicts the 256 MiB MALL, so small weights (the conv projection, the
@@ -425,6 +429,13 @@ def measure(D, torch, timer, w, dev, args, steps, warmup, attr_steps):
     lm = med["full"] - conv - sel
     # the LM-head op back to back (the weight stream exceeds the MALL, so no flush is needed)
     lm_b2b = timer.back_to_back(p.lmhead, 50 if w.n_rows <= 64 else 10)
+    ctx_ms = None
+    if p.ctx:
+        # the context rows' share of the LM-head op: the same op without W_H
+        d = p.dev
+        plain = timer.back_to_back(lambda: D.unary_topk(d["h"], d["w_lm"], w.top_k, gold_ids=p.gold,
+                                                        workspace=p.ws_topk), 50 if w.n_rows <= 64 else 10)
+        ctx_ms = lm_b2b - plain
     kern = ("lmhead_dma_kernel + decode_tail_kernel" if p.fused else
             "lmhead_dma_kernel + top-K merge" if w.n_rows <= 8 and w.dtype == "bf16" else
             "lmhead_stream_kernel + top-K merge" if w.n_rows <= 8 else
@@ -442,6 +453,7 @@ def measure(D, torch, timer, w, dev, args, steps, warmup, attr_steps):
         "attribution_ms": {k: v for k, v in med.items()}, "attribution_steps_per_variant": n_attr,
         "roofline": roof, "teeth": teeth, "path": "decode_head" if p.fused else "unary_topk + selector",
         "context_rows": "decode head" if p.fused else "lm head" if p.ctx else "selector",
+        "context_rows_ms": ctx_ms,
     }
     if w.name in TARGETS:
         out["roofline_target_frac"] = TARGETS[w.name]
@@ -543,6 +555,8 @@ def main():
                                   "interleaved in 5 rounds",
                    "attribution_ms": head["attribution_ms"]},
         "path": head["path"],
+        "context_rows": head["context_rows"],
+        "context_rows_ms": head["context_rows_ms"],
         "ops_ms": ops,
         "selector_plus_conv_over_lmhead": head["selector_plus_conv_over_lmhead"],
         "conv_10_wrappers_ms": 10 * ops["conv"],
@@ -574,7 +588,8 @@ def main():
             steps, warm, at = budget[name]
             r = measure(D, torch, timer, wk, d2, sub, steps, warm, at)
             wl[name] = {k: r[k] for k in ("ms_per_step", "blocks_per_s", "ops_ms", "selector_plus_conv_over_lmhead",
-                                          "roofline", "teeth", "path", "attribution_steps_per_variant")}
+                                          "roofline", "teeth", "path", "attribution_steps_per_variant",
+                                          "context_rows", "context_rows_ms")}
             for k in ("roofline_target_frac", "tf_coverage"):
                 if k in r:
                     wl[name][k] = r[k]
