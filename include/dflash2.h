@@ -212,7 +212,8 @@ dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, 
  *   h [N, H] dtype (N = n_blocks*bs); w_h [r, H] dtype
  *   g [N, r] float32 or NULL: the context rows formed beforehand (the out_g of
  *   dflash2_unary_topk_ex); then h and w_h are not read and may be NULL, and
- *   no projection runs.  Without g, h and w_h are required (DFLASH2_ERR_NULL).
+ *   no projection runs (hidden is still checked; the workspace is the same).
+ *   Without g, h and w_h are required (DFLASH2_ERR_NULL).
  *   cb_pred, cb_succ [V, r] dtype; cand_ids [N, K] int32; cand_vals [N, K] float32
  *   anchor_ids [n_blocks] int32
  *   out_path [n_blocks, bs] int32; out_path_score [n_blocks, bs] float32 or NULL
