@@ -431,11 +431,13 @@ def measure(D, torch, timer, w, dev, args, steps, warmup, attr_steps):
     lm_b2b = timer.back_to_back(p.lmhead, 50 if w.n_rows <= 64 else 10)
     ctx_ms = None
     if p.ctx:
-        # the context rows' share of the LM-head op: the same op without W_H
+        # the context rows' share of the LM-head op: the op minus the same op
+        # without W_H, both back to back in 5 interleaved rounds (median)
         d = p.dev
-        plain = timer.back_to_back(lambda: D.unary_topk(d["h"], d["w_lm"], w.top_k, gold_ids=p.gold,
-                                                        workspace=p.ws_topk), 50 if w.n_rows <= 64 else 10)
-        ctx_ms = lm_b2b - plain
+        plain = lambda: D.unary_topk(d["h"], d["w_lm"], w.top_k, gold_ids=p.gold, workspace=p.ws_topk)
+        reps = 50 if w.n_rows <= 64 else 10
+        diffs = [timer.back_to_back(p.lmhead, reps) - timer.back_to_back(plain, reps) for _ in range(5)]
+        ctx_ms = statistics.median(diffs)
     kern = ("lmhead_dma_kernel + decode_tail_kernel" if p.fused else
             "lmhead_dma_kernel + top-K merge" if w.n_rows <= 8 and w.dtype == "bf16" else
             "lmhead_stream_kernel + top-K merge" if w.n_rows <= 8 else
