@@ -161,30 +161,40 @@ def test_walk_from_context_rows_clears_the_status(D):
     assert D.read_device_status(ws) == 0 and (path >= 0).all()
 
 
-def test_context_only_slabs_leave_the_log_sum_exp_and_metrics_alone(D):
+LSE_CASES = [
+    # (N, H, V, r, K, dtype, forced slabs): 256 x 256 tiles with two slabs of
+    # context tiles only; the LDS-streamed and the float32 register-streamed
+    # decode regimes, where g is its own launch beside the log-sum-exp kernels
+    (260, 256, 2000, 520, 16, "bf16", 8), (8, 4096, 30011, 256, 16, "bf16", 0), (5, 256, 7001, 32, 16, "f32", 0),
+]
+
+
+@pytest.mark.parametrize("N,H,V,r,K,dtype,slabs", LSE_CASES)
+def test_context_rows_leave_the_log_sum_exp_and_metrics_alone(D, N, H, V, r, K, dtype, slabs):
     # slabs holding only context tiles contribute empty lists and an empty
     # log-sum-exp partial; the transformed top-K, the log-sum-exp and the gold
     # metrics match the oracle as without W_H
-    N, H, V, r, K, mult, cap = 260, 256, 2000, 520, 16, 1.3, 6.0
-    inp = inputs(N, 1, H, V, r, K, "bf16", 43)
+    log(f"topk_ex+g+lse N={N} H={H} V={V} r={r} K={K} {dtype} slabs={slabs or 'auto'}")
+    mult, cap = 1.3, 6.0
+    inp = inputs(N, 1, H, V, r, K, dtype, 43)
     gold = inp["gold"].copy()
-    U = O.lm_logits(inp["h"], inp["w_lm"], "bf16")
+    U = O.lm_logits(inp["h"], inp["w_lm"], dtype)
     gold[::3] = np.argmax(U[::3], axis=1)
     dev = {k: to_dev(inp[k]) for k in ("h", "w_lm", "w_h")}
     g = torch.empty((N, r), dtype=torch.float32, device="cuda")
     try:
-        D.debug_force_slabs(8)
+        D.debug_force_slabs(slabs)
         ids, vals, gl, lse, prob, hit = D.unary_topk_ex(dev["h"], dev["w_lm"], K, gold_ids=to_dev(gold),
                                                         output_multiplier=mult, softcap=cap, want_lse=True,
                                                         want_metrics=True, w_h=dev["w_h"], g=g)
         torch.cuda.synchronize()
     finally:
         D.debug_force_slabs(0)
-    rids, rvals, rlse, rgl, rprob, rhit = O.unary_topk_ex(inp["h"], inp["w_lm"], K, "bf16", gold_ids=gold,
+    rids, rvals, rlse, rgl, rprob, rhit = O.unary_topk_ex(inp["h"], inp["w_lm"], K, dtype, gold_ids=gold,
                                                           output_multiplier=mult, softcap=cap)
     fails, flags, msgs = compare_topk(to_np(ids), to_np(vals), O.transform_logits(U, mult, cap), K)
     assert fails == 0, msgs[:5]
     assert close(to_np(gl), rgl).all() and close(to_np(lse), rlse).all()
     assert close(to_np(prob), rprob, atol=1e-6).all()
     assert np.array_equal(to_np(hit), (to_np(ids) == gold[:, None]).any(1).astype(np.uint8))
-    assert context_ok(to_np(g), inp["h"], inp["w_h"], "bf16").all()
+    assert context_ok(to_np(g), inp["h"], inp["w_h"], dtype).all()
