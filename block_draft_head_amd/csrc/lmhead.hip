@@ -1705,6 +1705,16 @@ static int slab_count(int automatic, int limit) {
     return n < 1 ? 1 : n > limit ? limit : n;
 }
 
+// Workgroups for a weight stream of n tiles over at most `cap`: as few as
+// keep the largest share at ceil(n / cap) tiles, so that every workgroup
+// carries that share but a few (the stream is bound by HBM, not by the
+// workgroup count, and the one-tile-longer workgroups set its end).
+static int balanced_stream_grid(int n, int cap) {
+    if (n <= cap) return n;
+    const int per = (n + cap - 1) / cap;
+    return (n + per - 1) / per;
+}
+
 static int first_stage_keys(int n_keys, int K) {
     return (n_keys + kMergeChunk - 1) / kMergeChunk * K;
 }
@@ -1725,7 +1735,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.dma = true;
         p.ksplit = ks;
         p.n_tiles = (V + 15) / 16;
-        p.grid_x = slab_count(kStreamWGs, p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs);
+        p.grid_x = slab_count(balanced_stream_grid(p.n_tiles, kStreamWGs), p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs);
         p.grid_y = 1;
         p.n_lists = p.grid_x;
         p.lds = dma_lds_bytes(H, ks);
@@ -1733,7 +1743,7 @@ LmheadPlan plan_lmhead(int dtype, int64_t M, int H, int V, int K) {
         p.streaming = true;
         p.nw = nw;
         p.n_tiles = (V + 15) / 16;
-        p.grid_x = slab_count(kStreamWGs, p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs);
+        p.grid_x = slab_count(balanced_stream_grid(p.n_tiles, kStreamWGs), p.n_tiles < kStreamWGs ? p.n_tiles : kStreamWGs);
         p.grid_y = 1;
         p.n_lists = p.grid_x;
         p.lds = stream_lds;
@@ -1875,10 +1885,14 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
 DecodeLayout decode_layout(int64_t M, int H, int V, int r, int K) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     DecodeLayout L{};
-    const int tiles = (V + 15) / 16 + (r > 0 ? (r + 15) / 16 : 0);
-    L.grid = slab_count(kStreamWGs, tiles < kStreamWGs ? tiles : kStreamWGs);
+    const int tiles_v = (V + 15) / 16, tiles = tiles_v + (r > 0 ? (r + 15) / 16 : 0);
+    auto grid_of = [](int n) { return slab_count(balanced_stream_grid(n, kStreamWGs), n < kStreamWGs ? n : kStreamWGs); };
+    L.grid = grid_of(tiles);
+    // room for the lists of either call (with W_H's tiles the grid may be the
+    // smaller one), so a workspace sized for the walk serves the lattice alone
+    const int lists = L.grid > grid_of(tiles_v) ? L.grid : grid_of(tiles_v);
     L.partial = kStatusBytes;
-    L.g = L.partial + up((size_t)M * L.grid * K * 8);
+    L.g = L.partial + up((size_t)M * lists * K * 8);
     L.total = L.g + up((size_t)M * (r > 0 ? r : 0) * 4);
     return L;
 }

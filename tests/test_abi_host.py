@@ -315,15 +315,21 @@ def test_debug_slab_knob_changes_the_lm_head_workspace():
     auto_dma = D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16)
     auto_big = D.workspace_bytes(D.OP_UNARY_TOPK, 4096, 4096, 151936, 0, 16)
     auto_dh = D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16)
+    # the decode head streams 151936 / 16 + 256 / 16 = 9512 tiles; its automatic
+    # grid is the fewest workgroups that keep the largest share at
+    # ceil(9512 / 256) = 38 tiles: ceil(9512 / 38) = 251
+    tiles = 151936 // 16 + 256 // 16
+    grid = -(-tiles // -(-tiles // 256))
+    assert grid == 251
     try:
         D.debug_force_slabs(7)
-        # 8 rows: 7 lists of 16 keys per row instead of 256 (plus the status
+        # 8 rows: 7 lists of 16 keys per row instead of 251 (plus the status
         # header, the log-sum-exp partials and the context rows)
         assert D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16) < auto_dma
-        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh - 8 * (256 - 7) * 16 * 8
+        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh - 8 * (grid - 7) * 16 * 8
         assert D.workspace_bytes(D.OP_UNARY_TOPK, 4096, 4096, 151936, 0, 16) < auto_big
-        D.debug_force_slabs(100000 // 100)  # clamped to each kernel's limit
-        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh
+        D.debug_force_slabs(100000 // 100)  # clamped to each kernel's limit (256 stream workgroups)
+        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh + 8 * (256 - grid) * 16 * 8
     finally:
         D.debug_force_slabs(0)
     assert D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16) == auto_dma
