@@ -96,7 +96,7 @@ hipError_t launch_unary_topk(int dtype, int64_t M, int H, int V, int K, const vo
 // the workgroups' partial lists, the context rows g [M, r].
 struct DecodeLayout {
     int grid;
-    size_t partial, g, total;
+    size_t partial, heads, g, total;  // byte offsets: lists, their heads (one key per list), context rows
 };
 DecodeLayout decode_layout(int64_t M, int H, int V, int r, int K);  // r = 0: no context rows
 bool decode_head_supported(int64_t M, int H, int V, int r, int K);

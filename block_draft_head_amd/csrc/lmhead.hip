@@ -383,7 +383,7 @@ template <int KS, bool LSE, bool FUSED>
 __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ w, int M, int H, int V, int K,
     const int32_t *__restrict__ gold, float *__restrict__ gold_logit, uint64_t *__restrict__ partial,
-    uint32_t *__restrict__ status, UnaryEpi ue, DecodeFuse fu) {
+    uint32_t *__restrict__ status, UnaryEpi ue, DecodeFuse fu, uint64_t *__restrict__ heads) {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int NW = kDmaWaves, NB = kDmaRing, CAP = kDmaCandCap, AH = kDmaAhead, LD = kDmaLead;
     constexpr int G = NW / KS;   // wave groups
@@ -680,6 +680,8 @@ __global__ __launch_bounds__(64 * kDmaWaves) void lmhead_dma_kernel(
         }
         const uint64_t top = wave_topk<R>(k, K, myscratch);
         if (lane < K) partial[((size_t)row * gridDim.x + blockIdx.x) * K + lane] = top;
+        // the list's head again, beside the other workgroups' heads of the row
+        if (heads && lane == 0) heads[(size_t)row * gridDim.x + blockIdx.x] = top;
     }
 }
 
@@ -1551,7 +1553,9 @@ __global__ __launch_bounds__(256) void topk_merge_rows_kernel(const uint64_t *__
 // merges row w's partial lists (n_lists <= 256 sorted lists of K keys), then
 // the workgroup walks every block on the merged lattice.
 //
-// The merge reads list heads first.  With v the largest value such that at
+// The merge reads list heads first (the stream kernel writes each list's head
+// a second time into the row's array of heads, so a wave's load of them is
+// consecutive words rather than one cache line per list).  With v the largest value such that at
 // least K heads have a high word (the order image of the logit) >= v, any key
 // whose high word is below v has K larger keys and is not among the row's K
 // best; so only lists whose head reaches v, and only their keys that do,
@@ -1581,7 +1585,8 @@ __device__ __forceinline__ uint32_t high_word_bound(const uint64_t (&k)[R], int 
 
 template <int NJ, bool WALK>
 __global__ __launch_bounds__(64 * kTailWaves) void decode_tail_kernel(
-    const uint64_t *__restrict__ partial, int M, int n_lists, int K, int V, int32_t *__restrict__ out_ids,
+    const uint64_t *__restrict__ partial, const uint64_t *__restrict__ heads, int M, int n_lists, int K, int V,
+    int32_t *__restrict__ out_ids,
     float *__restrict__ out_vals, const float *__restrict__ g, const uint16_t *__restrict__ A,
     const uint16_t *__restrict__ B, const int32_t *__restrict__ anchors, int bs, int r, int32_t *__restrict__ path,
     float *__restrict__ path_score, uint32_t *__restrict__ status) {
@@ -1600,7 +1605,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void decode_tail_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int li = lane + 64 * i;
-        hk[i] = (row < M && li < n_lists) ? rl[(size_t)li * K] : 0ull;
+        hk[i] = (row < M && li < n_lists) ? heads[(size_t)row * n_lists + li] : 0ull;
     }
     const bool g_in_lds = WALK && M * r <= kTailCtxFloats;
     if constexpr (WALK) {
@@ -1821,7 +1826,7 @@ static hipError_t run_lmhead(const LmheadPlan &p, int64_t M, int H, int V, int K
                 if (err != hipSuccess) return err;
                 hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(64 * kDmaWaves), p.lds, stream, (const uint16_t *)h,
                                    (const uint16_t *)w, (int)M, H, V, K, gold, gold_logit, partial, status, ue,
-                                   DecodeFuse{});
+                                   DecodeFuse{}, nullptr);
                 return hipGetLastError();
             };
             e = p.ksplit == 4 ? launch(lmhead_dma_kernel<4, LSE, false>)
@@ -1892,7 +1897,8 @@ DecodeLayout decode_layout(int64_t M, int H, int V, int r, int K) {
     // smaller one), so a workspace sized for the walk serves the lattice alone
     const int lists = L.grid > grid_of(tiles_v) ? L.grid : grid_of(tiles_v);
     L.partial = kStatusBytes;
-    L.g = L.partial + up((size_t)M * lists * K * 8);
+    L.heads = L.partial + up((size_t)M * lists * K * 8);
+    L.g = L.heads + up((size_t)M * lists * 8);
     L.total = L.g + up((size_t)M * (r > 0 ? r : 0) * 4);
     return L;
 }
@@ -1911,6 +1917,7 @@ hipError_t launch_decode_head(int64_t M, int H, int V, int K, const void *h, con
     uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
     uint32_t *status = reinterpret_cast<uint32_t *>(ws);
     uint64_t *partial = reinterpret_cast<uint64_t *>(ws + L.partial);
+    uint64_t *heads = reinterpret_cast<uint64_t *>(ws + L.heads);
     float *g = reinterpret_cast<float *>(ws + L.g);
     const DecodeFuse fu{(const uint16_t *)w_h, walk ? r : 0, g};
     const int ks = dma_ksplit(H);
@@ -1920,7 +1927,7 @@ hipError_t launch_decode_head(int64_t M, int H, int V, int K, const void *h, con
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(kern, dim3(L.grid), dim3(64 * kDmaWaves), lds, stream, (const uint16_t *)h,
                            (const uint16_t *)w, (int)M, H, V, K, nullptr, nullptr, partial, status,
-                           UnaryEpi{1.f, 0.f, nullptr}, fu);
+                           UnaryEpi{1.f, 0.f, nullptr}, fu, heads);
         return hipGetLastError();
     };
     hipError_t e = ks == 4 ? stream_kernel(lmhead_dma_kernel<4, false, true>)
@@ -1928,7 +1935,7 @@ hipError_t launch_decode_head(int64_t M, int H, int V, int K, const void *h, con
                              : stream_kernel(lmhead_dma_kernel<1, false, true>);
     if (e != hipSuccess) return e;
     auto tail = [&](auto kern) -> hipError_t {
-        hipLaunchKernelGGL(kern, dim3(1), dim3(64 * kTailWaves), 0, stream, partial, (int)M, L.grid, K, V, out_ids,
+        hipLaunchKernelGGL(kern, dim3(1), dim3(64 * kTailWaves), 0, stream, partial, heads, (int)M, L.grid, K, V, out_ids,
                            out_vals, g, (const uint16_t *)A, (const uint16_t *)B, anchors, bs, walk ? r : 0, path,
                            path_score, status);
         return hipGetLastError();

@@ -326,10 +326,13 @@ def test_debug_slab_knob_changes_the_lm_head_workspace():
         # 8 rows: 7 lists of 16 keys per row instead of 251 (plus the status
         # header, the log-sum-exp partials and the context rows)
         assert D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16) < auto_dma
-        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh - 8 * (grid - 7) * 16 * 8
+        # (the lists and their heads; each region rounded up to 256 bytes)
+        up = lambda x: (x + 255) // 256 * 256
+        lists = lambda n: up(8 * n * 16 * 8) + up(8 * n * 8)
+        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh - lists(grid) + lists(7)
         assert D.workspace_bytes(D.OP_UNARY_TOPK, 4096, 4096, 151936, 0, 16) < auto_big
         D.debug_force_slabs(100000 // 100)  # clamped to each kernel's limit (256 stream workgroups)
-        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh + 8 * (256 - grid) * 16 * 8
+        assert D.workspace_bytes(D.OP_DECODE_HEAD, 8, 4096, 151936, 256, 16) == auto_dh + lists(256) - lists(grid)
     finally:
         D.debug_force_slabs(0)
     assert D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16) == auto_dma
