@@ -116,13 +116,15 @@ def test_decode_head_flags_an_out_of_range_anchor(D):
     assert D.read_device_status(ws) == 0
 
 
-@pytest.mark.parametrize("kind", ["clustered", "tied", "one_list"])
-def test_decode_head_merge_fallbacks(D, kind):
+@pytest.mark.parametrize("kind,K", [("clustered", 16), ("clustered", 4), ("clustered", 6), ("tied", 16),
+                                    ("one_list", 16)])
+def test_decode_head_merge_fallbacks(D, kind, K):
     # lattices that defeat the fast merge: the top-K inside one workgroup's
-    # slice (a list whose prefix all reaches the bound), or every logit of a
-    # row tied (more survivors than the sort holds); the exact paths must give
-    # the plain top-K bit for bit
-    nb, bs, H, V, r, K = 1, 8, 512, 6000, 32, 16
+    # slice (many keys of one list reach the bound; at small K nearly every
+    # key of that list does), or every logit of a row tied (more survivors
+    # than the sort holds); the exact paths must give the plain top-K bit for
+    # bit
+    nb, bs, H, V, r = 1, 8, 512, 6000, 32
     inp = inputs(nb, bs, H, V, r, K, 21, 1)
     w = O.widen(inp["w_lm"], "bf16")
     hh = O.widen(inp["h"], "bf16")
