@@ -173,9 +173,9 @@ __device__ __forceinline__ void tiled_store_c(float *ctile, const f32x4 (&acc)[C
 // of two LDS buffers, chunk c of row r at slot c ^ ((r >> 1) & 7), so the 16
 // rows that one quarter of a wave reads for an MFMA fragment fall on 16
 // different 16-byte bank groups.  While a stage is multiplied, the next one
-// is fetched from HBM into registers and, during the stage's last k16 step,
-// written to the idle buffer; inside a stage the fragments of k16 step s + 1
-// are read from LDS between the MFMAs of step s.
+// is copied from global memory straight into the idle buffer; inside a stage
+// the fragments of k16 step s + 1 are read from LDS between the MFMAs of
+// step s.
 namespace big {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -188,6 +188,8 @@ constexpr int KS = BK / 16;                    // k16 steps per stage
 constexpr int HALF = BM * ROWB;                // 32 KB: the A (or B) part of a stage
 constexpr int STAGE = 2 * HALF;                // 64 KB: A rows, then B rows
 constexpr int LW = HALF / 1024 / (NT / 64);    // 1 KB copies per wave per operand per stage (8)
+constexpr int TOUCH_AHEAD = 2;                 // k-tiles between a B slice's touch and its copies
+constexpr int TOUCH_SINK = NT / 64 * 256;      // LDS bytes the touches land in (256 per wave)
 
 __device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ ((row >> 1) & 7)) << 4); }
 
@@ -205,16 +207,27 @@ __device__ __forceinline__ int acc_row(int wm, int tm, int i, int lane) {
 // The operands go from global memory straight into LDS (global_load_lds_dwordx4):
 // one instruction of a wave fills 1 KB of consecutive LDS, 16 bytes per lane,
 // so each lane fetches the global chunk that the swizzled layout puts at its
-// slot.  No staging registers and no LDS write instructions.  The two stage
-// buffers must be distinct __shared__ arrays: the compiler's wait tracking
-// then sees that reading one stage does not depend on the copies still
-// filling the other, and the only wait for the copies is the one before the
-// barrier that ends each k-tile.
+// slot.  No staging registers and no LDS write instructions.  The copies are
+// inline assembly, so the compiler neither knows of them nor waits for them:
+// the one wait is the count before the barrier that ends each k-tile, and
+// every reuse of a stage buffer follows such a barrier.  (Left to the
+// compiler, its waits for its own LDS copies drain every load in flight
+// before the next LDS read, so nothing could stay in flight across a k-tile.)
+//
+// Touches (TCH): the last global read of each k-tile is one 4-byte read per
+// B row of the k-slice TOUCH_AHEAD tiles ahead, into a scratch word of LDS
+// that nothing reads.  Each row's slice is one 128-byte line, so the slice
+// reaches L2 before its copies are issued, and the wait that ends the k-tile
+// leaves that read in flight (vmcnt(1)); the next k-tile's wait covers it.
+// This pays where a B tile is read by few workgroups (few row tiles: most of
+// its k-slices come from HBM, whose latency the two-stage ring alone does not
+// cover), and is left off for the long lists, whose epilogue it slows.
 struct Pipe {
     const uint8_t *A, *B;       // first row of the A tile / B tile
     uint32_t ao[LW], bo[LW];     // byte offset of this lane's chunk of copy j, k-slice 0
     int wbase;                   // wave-uniform LDS offset of this wave's copies
     int aro[4], bro[4], hk;
+    uint32_t to;                 // this lane's B row (64 * wave + lane) at k-slice 0, for the touches
 
     // Rows past a_rows (b_rows) read row a_rows - 1 (b_rows - 1); 256 * H * 2 < 2^32.
     __device__ __forceinline__ void init(const uint16_t *A_, int a_rows, const uint16_t *B_, int b_rows, int H) {
@@ -228,6 +241,7 @@ struct Pipe {
             ao[j] = (uint32_t)min(row, a_rows - 1) * (uint32_t)H * 2u + (uint32_t)c * 16u;
             bo[j] = (uint32_t)min(row, b_rows - 1) * (uint32_t)H * 2u + (uint32_t)c * 16u;
         }
+        to = (uint32_t)min(wave * 64 + lane, b_rows - 1) * (uint32_t)H * 2u;
         const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31;
         hk = lane >> 5;
 #pragma unroll
@@ -236,13 +250,37 @@ struct Pipe {
             bro[i] = wn * 128 + i * 32 + r32;
         }
     }
+    // (wave-uniform; read from the first lane so that the copies can take it
+    // as their scalar base whatever the compiler proves about it)
+    static __device__ __forceinline__ const uint8_t *uniform(const uint8_t *p) {
+        const uint64_t v = (uint64_t)p;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+        return (const uint8_t *)(((uint64_t)hi << 32) | lo);
+    }
+    static __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+        return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t *)p;
+    }
+    // 16 bytes per lane from base + off into LDS at dst + 16 lane.  s_nop 4:
+    // the wait states that a scalar base or M0 written just before needs (the
+    // compiler adds none to inline assembly).
+    static __device__ __forceinline__ void copy16(const uint8_t *base, uint32_t off, const uint8_t *dst) {
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform(base)),
+                     "{m0}"(lds_addr(dst))
+                     : "memory");
+    }
+    // 4 bytes of this lane's B row in k-slice k0b into the wave's sink word
+    __device__ __forceinline__ void touch(uint32_t k0b, const uint8_t *sink) const {
+        asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(to + k0b), "s"(uniform(B)),
+                     "{m0}"(lds_addr(sink))
+                     : "memory");
+    }
     // k-slice at byte offset k0b into stage st
     __device__ __forceinline__ void fill(uint8_t *st, uint32_t k0b) {
 #pragma unroll
         for (int j = 0; j < LW; ++j) {
-            __builtin_amdgcn_global_load_lds(A + (ao[j] + k0b), (lds_void *)(st + wbase + j * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(B + (bo[j] + k0b), (lds_void *)(st + HALF + wbase + j * 1024), 16, 0,
-                                             0);
+            copy16(A, ao[j] + k0b, st + wbase + j * 1024);
+            copy16(B, bo[j] + k0b, st + HALF + wbase + j * 1024);
         }
     }
     __device__ __forceinline__ void frags(const uint8_t *st, int s, u32x4 (&fa)[4], u32x4 (&fb)[4]) const {
@@ -253,28 +291,31 @@ struct Pipe {
             fb[i] = *reinterpret_cast<const u32x4 *>(st + HALF + swz(bro[i], c));
         }
     }
-    // copies j0 .. j1 of k-slice k0b into stage st
-    __device__ __forceinline__ void fill_part(uint8_t *st, uint32_t k0b, int j0, int j1) {
-#pragma unroll
-        for (int j = j0; j < j1; ++j) {
-            __builtin_amdgcn_global_load_lds(A + (ao[j] + k0b), (lds_void *)(st + wbase + j * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(B + (bo[j] + k0b), (lds_void *)(st + HALF + wbase + j * 1024), 16, 0,
-                                             0);
-        }
-    }
-    // One k-tile from `cur` while k-slice nk fills `nxt`; the fragments of the
-    // first k16 step of `nxt` are read after the closing barrier.  The copies
-    // go out during the first two k16 steps, one between each MFMA and the
-    // next (all 16 at the start of the tile measured 6% slower: they queue
-    // ahead of the fragment reads).
+    // One k-tile from `cur` while k-slice nk fills `nxt` (and, with TCH, B's
+    // k-slice tk is touched); the fragments of the first k16 step of `nxt`
+    // are read after the closing barrier.  The copies go out during the
+    // first two k16 steps, each after one fragment read, between one MFMA
+    // and the next (all 16 at the start of the tile measured 6% slower: they
+    // queue ahead of the fragment reads).
+    static_assert(LW == 8 && KS == 4, "the copies go out four per operand in each of the first two k16 steps");
+    template <bool TCH>
     __device__ __forceinline__ void tile(f32x16 (&acc)[4][4], const uint8_t *cur, uint8_t *nxt, uint32_t nk,
-                                         u32x4 (&fa)[2][4], u32x4 (&fb)[2][4]) {
+                                         u32x4 (&fa)[2][4], u32x4 (&fb)[2][4], uint32_t tk, const uint8_t *sink) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int c0 = s & 1;
-            if (s + 1 < KS) frags(cur, s + 1, fa[c0 ^ 1], fb[c0 ^ 1]);
-            if (s < 2) fill_part(nxt, nk, s * LW / 2, (s + 1) * LW / 2);
+            if (s + 1 < KS) {
+                const int c = 2 * (s + 1) + hk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    fa[c0 ^ 1][i] = *reinterpret_cast<const u32x4 *>(cur + swz(aro[i], c));
+                    if (s < 2) copy16(A, ao[s * 4 + i] + nk, nxt + wbase + (s * 4 + i) * 1024);
+                    fb[c0 ^ 1][i] = *reinterpret_cast<const u32x4 *>(cur + HALF + swz(bro[i], c));
+                    if (s < 2) copy16(B, bo[s * 4 + i] + nk, nxt + HALF + wbase + (s * 4 + i) * 1024);
+                }
+            }
+            if (TCH && s == 2) touch(tk, sink);  // after every copy of the tile
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
@@ -284,13 +325,15 @@ struct Pipe {
                 for (int i = 0; i < 8; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                    if (s < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies into nxt have landed
+        // this wave's copies into nxt have landed (its touch may still be in
+        // flight), and its fragment reads of cur are done
+        if constexpr (TCH) asm volatile("s_waitcnt vmcnt(1)\n\ts_waitcnt lgkmcnt(0)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)" ::: "memory");
         __syncthreads();
         frags(nxt, 0, fa[0], fb[0]);
     }
@@ -298,10 +341,11 @@ struct Pipe {
 
 // acc = A[0 .. 256) . B[0 .. 256)^T over all of H (H % 64 == 0), A and B
 // pointing at the tiles' first rows (row r at r * H elements).  st0 and st1
-// are two distinct __shared__ arrays of at least STAGE bytes.  On return every
-// copy has landed and all waves have passed a barrier after their last
-// fragment read that matters; the caller may reuse st0 and st1 after one more
-// barrier (the last fragment reads are of a spare slice and unused).
+// are two __shared__ buffers of at least STAGE bytes, sink (TCH) one of
+// TOUCH_SINK bytes.  On return every copy and touch has landed and all waves
+// have passed a barrier after their last fragment read that matters; the
+// caller may reuse st0 and st1 after one more barrier (the last fragment
+// reads are of a spare slice and unused).
 //
 // prefilled: the caller has already issued this wave's copies of k-slice 0
 // into st0 (prefill below, same operands), so the first stage only waits.
@@ -311,8 +355,10 @@ __device__ __forceinline__ void prefill(uint8_t *st0, const uint16_t *A, int a_r
     P.init(A, a_rows, B, b_rows, H);
     P.fill(st0, 0);
 }
-__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *st0, uint8_t *st1, const uint16_t *A,
-                                         int a_rows, const uint16_t *B, int b_rows, int H, bool prefilled = false) {
+template <bool TCH>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *st0, uint8_t *st1, const uint8_t *sink,
+                                         const uint16_t *A, int a_rows, const uint16_t *B, int b_rows, int H,
+                                         bool prefilled = false) {
     Pipe P;
     P.init(A, a_rows, B, b_rows, H);
 #pragma unroll
@@ -328,13 +374,17 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *st0, uint
     P.frags(st0, 0, fa[0], fb[0]);
     const int KT = H / BK;
     // stage buffers alternate by name, two k-tiles per trip; a tile with no
-    // next slice re-fills its idle buffer with the last slice (in bounds, unused)
+    // next slice re-fills its idle buffer with the last slice, and one with no
+    // slice TOUCH_AHEAD ahead touches the last (in bounds, unused)
+    const uint8_t *wsink = sink + (threadIdx.x >> 6) * 256;
+    auto ahead = [&](int k) { return (uint32_t)min(k, KT - 1) * BK * 2; };
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
-        P.tile(acc, st0, st1, (uint32_t)(kt + 1) * BK * 2, fa, fb);
-        P.tile(acc, st1, st0, (uint32_t)min(kt + 2, KT - 1) * BK * 2, fa, fb);
+        P.tile<TCH>(acc, st0, st1, ahead(kt + 1), fa, fb, ahead(kt + TOUCH_AHEAD), wsink);
+        P.tile<TCH>(acc, st1, st0, ahead(kt + 2), fa, fb, ahead(kt + 1 + TOUCH_AHEAD), wsink);
     }
-    if (kt < KT) P.tile(acc, st0, st1, (uint32_t)(KT - 1) * BK * 2, fa, fb);
+    if (kt < KT) P.tile<TCH>(acc, st0, st1, ahead(KT - 1), fa, fb, ahead(KT - 1), wsink);
+    if constexpr (TCH) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last touch
 }
 
 }  // namespace big

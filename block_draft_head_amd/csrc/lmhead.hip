@@ -1130,6 +1130,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     using namespace big;
     __shared__ __align__(16) uint8_t st0[STAGE];
     __shared__ __align__(16) uint8_t st1[STAGE];
+    // B-slice touches for the short lists (off for the long ones, whose
+    // epilogue they slow)
+    constexpr bool kTouch = KL <= 16;
+    __shared__ __align__(16) uint8_t touch_sink[kTouch ? TOUCH_SINK : 16];
     uint64_t *slots = reinterpret_cast<uint64_t *>(st1);  // register-scan hits, [BM][kRowCand]
     __shared__ __align__(16) float thr[BM];  // per tile row: value of its KL-th key (+inf: not a row)
     __shared__ uint32_t cnt[BM];             // per tile row: register-scan hits this tile
@@ -1190,7 +1194,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             // the accumulators stored as they are (rows past M or r dropped)
             const int c0 = (vt - n_vt) * BN;
             f32x16 acc[4][4];
-            mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, ctx.wh + (size_t)c0 * H, ctx.r - c0, H, false);
+            mainloop<kTouch>(acc, st0, st1, touch_sink, h + (size_t)m0 * H, M - m0, ctx.wh + (size_t)c0 * H,
+                             ctx.r - c0, H, false);
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
@@ -1217,7 +1222,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool scan = bound || (!fresh && v0 + BN <= V && (vt - vt0) * 16 >= KL);
         store = store || !scan;
         f32x16 acc[4][4];
-        mainloop(acc, st0, st1, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H, prefilled);
+        mainloop<kTouch>(acc, st0, st1, touch_sink, h + (size_t)m0 * H, M - m0, w + (size_t)v0 * H, V - v0, H,
+                         prefilled);
         prefilled = false;
         if (store) {
             // straight from the accumulators, one base address per 4-row group
