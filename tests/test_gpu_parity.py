@@ -118,6 +118,9 @@ TOPK_CASES = [
     (8, 4096, 30011, 16, "bf16"), (1, 4096, 5003, 64, "bf16"), (3, 2048, 70001, 5, "bf16"),
     # many rows whose 32 lists of 32 keys (1024) one wave merges in two chunks
     (1800, 256, 9000, 20, "bf16"),
+    # many rows, lists of 32 and 64 keys over slabs of several tiles (the
+    # scan's hits inserted into the lists between tiles)
+    (300, 256, 70000, 64, "bf16"), (300, 256, 70000, 24, "bf16"),
 ]
 
 
@@ -251,6 +254,7 @@ def test_unary_topk_is_deterministic(D):
     (300, 256, 7000, 16, "f32"),    # many rows, float32 tiles
     (8, 512, 20011, 16, "bf16"),    # at most 8 rows, weights through LDS
     (5, 256, 5000, 64, "f32"),      # at most 8 rows, float32 register stream
+    (300, 256, 70000, 64, "bf16"),  # many rows, 64-key lists: one slab of 274 tiles down to one tile per slab
 ])
 def test_slab_count_does_not_change_the_lists(D, N, H, V, K, dtype):
     """The vocabulary split (the number of partial lists per row, forced by the
