@@ -121,6 +121,9 @@ TOPK_CASES = [
     # many rows, lists of 32 and 64 keys over slabs of several tiles (the
     # scan's hits inserted into the lists between tiles)
     (300, 256, 70000, 64, "bf16"), (300, 256, 70000, 24, "bf16"),
+    # many rows, an odd number of 64-deep k-tiles (5, 1, 3): the k loop's
+    # last tile alone, with and without the weight-row touches
+    (40, 320, 5003, 16, "bf16"), (300, 64, 4000, 16, "bf16"), (64, 192, 3001, 64, "bf16"),
 ]
 
 
