@@ -7,6 +7,7 @@
 
 #include <array>
 #include <climits>
+#include <initializer_list>
 #include <iterator>
 #include <cstdint>
 
@@ -49,6 +50,16 @@ bool aliased(const O &outs, const I &ins) {
 
 // The bytes of an optional argument: 0 when it is NULL.
 size_t opt(const void *p, size_t b) { return p ? b : 0; }
+
+// true when a floating-point array or the workspace (vec16) is off a 16-byte
+// boundary or an int32 array (word4) off a 4-byte one; NULL passes
+bool misaligned(std::initializer_list<const void *> vec16, std::initializer_list<const void *> word4 = {}) {
+    for (const void *p : vec16)
+        if (reinterpret_cast<uintptr_t>(p) % 16) return true;
+    for (const void *p : word4)
+        if (reinterpret_cast<uintptr_t>(p) % 4) return true;
+    return false;
+}
 
 dflash2_status launched(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : DFLASH2_ERR_LAUNCH; }
 
@@ -156,6 +167,7 @@ dflash2_status dflash2_conv_prepare(int dtype, int64_t n_tokens, int32_t block_s
     const size_t act = (size_t)n_tokens * hidden * es;
     const size_t kp = (size_t)n_tokens * taps * (hidden / group_size) * 4;
     const size_t G = (size_t)(hidden / group_size);
+    if (misaligned({x, w_proj, base, x_out, k_post})) return DFLASH2_ERR_UNSUPPORTED;
     const Span outs[] = {{x_out, act}, {k_post, kp}};
     const Span ins[] = {{x, act}, {w_proj, 2 * (size_t)taps * G * hidden * es}, {base, 2 * (size_t)taps * hidden * es}};
     if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
@@ -173,6 +185,7 @@ dflash2_status dflash2_conv_finish(int dtype, int64_t n_tokens, int32_t block_si
     const size_t es = elem_size(dtype);
     const size_t act = (size_t)n_tokens * hidden * es;
     const size_t kp = (size_t)n_tokens * taps * (hidden / group_size) * 4;
+    if (misaligned({y, k_post, base, y_out})) return DFLASH2_ERR_UNSUPPORTED;
     const Span outs[] = {{y_out, act}};
     const Span ins[] = {{y, act}, {k_post, kp}, {base, 2 * (size_t)taps * hidden * es}};
     if (aliased(outs, ins)) return DFLASH2_ERR_ALIAS;
@@ -194,6 +207,8 @@ dflash2_status dflash2_unary_topk(int dtype, int64_t n_rows, int32_t hidden, int
     if (gold_ids && !out_gold_logit) return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_UNARY_TOPK, n_rows, hidden, vocab, 0, top_k))
         return DFLASH2_ERR_WORKSPACE;
+    if (misaligned({h, w_lm, out_vals, out_gold_logit, workspace}, {gold_ids, out_ids}))
+        return DFLASH2_ERR_UNSUPPORTED;
     const size_t nk = (size_t)n_rows * top_k, n = (size_t)n_rows, es = elem_size(dtype);
     const Span outs[] = {{out_ids, nk * 4}, {out_vals, nk * 4}, {out_gold_logit, opt(out_gold_logit, n * 4)},
                          {workspace, workspace_bytes}};
@@ -226,6 +241,9 @@ dflash2_status dflash2_unary_topk_ex(int dtype, int64_t n_rows, int32_t hidden, 
     }
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_UNARY_TOPK, n_rows, hidden, vocab, 0, top_k))
         return DFLASH2_ERR_WORKSPACE;
+    if (misaligned({h, w_lm, w_h, out_vals, out_gold_logit, out_lse, out_gold_prob, out_g, workspace},
+                   {gold_ids, out_ids}))
+        return DFLASH2_ERR_UNSUPPORTED;
     const size_t nk = (size_t)n_rows * top_k, n = (size_t)n_rows, es = elem_size(dtype);
     const size_t r = out_g ? (size_t)rank : 0;
     const Span outs[] = {{out_ids, nk * 4}, {out_vals, nk * 4}, {out_gold_logit, opt(out_gold_logit, n * 4)},
@@ -256,6 +274,9 @@ dflash2_status dflash2_selector_walk(int dtype, int32_t n_blocks, int32_t block_
         return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
+    if (misaligned({h, w_h, g, cb_pred, cb_succ, cand_vals, out_path_score, workspace},
+                   {cand_ids, anchor_ids, out_path}))
+        return DFLASH2_ERR_UNSUPPORTED;
     if (aliased(walk_outputs(N, out_path, out_path_score, workspace, workspace_bytes),
                 walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, g, cb_pred, cb_succ, cand_ids,
                             cand_vals, anchor_ids)))
@@ -281,6 +302,8 @@ dflash2_status dflash2_selector_walk_noalloc(int dtype, int32_t n_blocks, int32_
         return DFLASH2_ERR_UNSUPPORTED;
     if (!(g || (h && w_h)) || !cb_pred || !cb_succ || !cand_ids || !cand_vals || !anchor_ids || !out_path)
         return DFLASH2_ERR_NULL;
+    if (misaligned({h, w_h, g, cb_pred, cb_succ, cand_vals, out_path_score}, {cand_ids, anchor_ids, out_path}))
+        return DFLASH2_ERR_UNSUPPORTED;
     if (aliased(walk_outputs(N, out_path, out_path_score, nullptr, 0),
                 walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, g, cb_pred, cb_succ, cand_ids,
                             cand_vals, anchor_ids)))
@@ -310,6 +333,9 @@ dflash2_status dflash2_selector_sample(int dtype, int32_t n_blocks, int32_t bloc
         return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_WALK, N, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
+    if (misaligned({h, w_h, g, cb_pred, cb_succ, cand_vals, out_path_score, workspace},
+                   {cand_ids, anchor_ids, out_path}))
+        return DFLASH2_ERR_UNSUPPORTED;
     if (aliased(walk_outputs(N, out_path, out_path_score, workspace, workspace_bytes),
                 walk_inputs(dtype, n_blocks, N, hidden, vocab, rank, top_k, h, w_h, g, cb_pred, cb_succ, cand_ids,
                             cand_vals, anchor_ids)))
@@ -342,6 +368,9 @@ dflash2_status dflash2_decode_head(int dtype, int32_t n_blocks, int32_t block_si
     if (sel && (!w_h || !cb_pred || !cb_succ || !anchor_ids || !out_path)) return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_DECODE_HEAD, N, hidden, vocab, r, top_k))
         return DFLASH2_ERR_WORKSPACE;
+    if (misaligned({h, w_lm, w_h, cb_pred, cb_succ, out_vals, out_path_score, workspace},
+                   {anchor_ids, out_ids, out_path}))
+        return DFLASH2_ERR_UNSUPPORTED;
     const size_t nk = (size_t)N * top_k * 4, np = (size_t)N * 4, cb = (size_t)vocab * r * 2;
     const Span outs[] = {{out_ids, nk}, {out_vals, nk}, {out_path, opt(out_path, np)},
                          {out_path_score, opt(out_path_score, np)}, {workspace, workspace_bytes}};
@@ -373,6 +402,9 @@ dflash2_status dflash2_selector_score_tf(int dtype, int64_t n_rows, int32_t hidd
     if (gold_ids && (!out_ce || !out_valid)) return DFLASH2_ERR_NULL;
     if (workspace_bytes < dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_TF, n_rows, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
+    if (misaligned({h, w_h, g, cb_pred, cb_succ, cand_vals, gold_logit, out_scores, out_ce, workspace},
+                   {cand_ids, pred_ids, gold_ids, out_best_ids}))
+        return DFLASH2_ERR_UNSUPPORTED;
     const size_t nk = (size_t)n_rows * top_k * 4, n = (size_t)n_rows, es = elem_size(dtype);
     const size_t cb = (size_t)vocab * rank * es;
     const Span outs[] = {{out_scores, nk}, {out_best_ids, n * 4}, {out_ce, opt(out_ce, n * 4)},
@@ -408,6 +440,10 @@ dflash2_status dflash2_selector_ce_backward(int dtype, int64_t n_rows, int32_t h
     if (workspace_bytes <
         dflash2_workspace_bytes(DFLASH2_OP_SELECTOR_CE_BACKWARD, n_rows, hidden, vocab, rank, top_k))
         return DFLASH2_ERR_WORKSPACE;
+    if (misaligned({h, w_h, cb_pred, cb_succ, cand_vals, gold_logit, grad_ce, grad_pred, grad_succ, grad_wh, out_ce,
+                    workspace},
+                   {cand_ids, pred_ids, gold_ids}))
+        return DFLASH2_ERR_UNSUPPORTED;
     const size_t es = elem_size(dtype);
     const size_t cb = (size_t)vocab * rank * 4, wh = (size_t)rank * hidden * 4;
     const size_t n = (size_t)n_rows, nk = n * top_k;

@@ -48,6 +48,12 @@
  * - Workspaces: caller-owned device memory of at least
  *   dflash2_workspace_bytes() bytes, any contents.  Calls that share a
  *   workspace must not run concurrently.
+ * - Alignment: every floating-point array (dtype, float32) and the
+ *   workspace start on a multiple of 16 bytes, every int32 array on a
+ *   multiple of 4 (uint8 arrays: any address); the kernels read and write
+ *   them 16 bytes at a time.  A pointer that is not returns
+ *   DFLASH2_ERR_UNSUPPORTED.  (Allocations are; a view stays aligned when its
+ *   offset is a multiple of 8 bf16 or 4 float32 elements.)
  */
 #ifndef DFLASH2_H_
 #define DFLASH2_H_

@@ -310,6 +310,33 @@ def test_selector_ce_backward_rules():
     assert bwd(ce=fake(9)) == ALIAS              # ce on grad_ce
 
 
+def off(i, b):
+    """fake(i) moved by b bytes"""
+    return P(0x4000000 * (i + 1) + b)
+
+
+@no_gpu
+def test_alignment_rules():
+    """Floating-point arrays and the workspace off a 16-byte boundary, or
+    int32 arrays off a 4-byte one, are refused before anything is enqueued."""
+    assert prep(x=off(0, 8)) == UNSUP and prep(kp=off(4, 4)) == UNSUP and prep(b=off(2, 2)) == UNSUP
+    assert fin(y=off(0, 2)) == UNSUP and fin(yo=off(3, 8)) == UNSUP and fin(kp=off(1, 4)) == UNSUP
+    assert topk(hp=off(0, 2)) == UNSUP and topk(w=off(1, 8)) == UNSUP and topk(vals=off(3, 4)) == UNSUP
+    assert topk(ws=off(4, 8)) == UNSUP and topk(ids=off(2, 2)) == UNSUP
+    assert topk(gold=off(5, 2), gl=fake(6)) == UNSUP and topk(gold=fake(5), gl=off(6, 4)) == UNSUP
+    assert topk_ex(wh=fake(8), r=32, g=off(9, 4)) == UNSUP and topk_ex(lse=off(7, 4)) == UNSUP
+    assert walk(ps=off(8, 4)) == UNSUP and walk(path=off(7, 2)) == UNSUP and walk(anchors=off(6, 1)) == UNSUP
+    assert walk(hp=None, wh=None, g=off(11, 8)) == UNSUP and walk(ws=off(9, 8)) == UNSUP
+    assert walk_na(anchors=off(6, 2)) == UNSUP and walk_na(hp=off(0, 2)) == UNSUP
+    assert sample(ps=off(11, 4)) == UNSUP and sample(ws=off(12, 4)) == UNSUP
+    assert dhead(vals=off(11, 4)) == UNSUP and dhead(ws=off(20, 8)) == UNSUP and dhead(ids=off(10, 2)) == UNSUP
+    assert dhead(A=off(3, 2)) == UNSUP and dhead(ps=off(13, 4)) == UNSUP
+    assert tf(scores=off(13, 4)) == UNSUP and tf(best=off(14, 2)) == UNSUP and tf(hp=off(0, 8)) == UNSUP
+    assert bwd(gp=off(20, 4)) == UNSUP and bwd(gce=off(9, 8)) == UNSUP and bwd(gold=off(7, 2)) == UNSUP
+    # uint8 arrays may sit anywhere: a misplaced one is still caught by another rule
+    assert tf(gold=fake(7), force=off(8, 1), gl=None) == NULL
+
+
 def test_debug_slab_knob_changes_the_lm_head_workspace():
     assert L.dflash2_debug_force_slabs(-1) == SHAPE and L.dflash2_debug_force_slabs(4097) == SHAPE
     auto_dma = D.workspace_bytes(D.OP_UNARY_TOPK, 8, 4096, 151936, 0, 16)
